@@ -1,0 +1,215 @@
+/*
+ * specattn.h -- C ABI of the speculative-decoding attention hot path for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * One speculative iteration of a video LLM has four data-parallel steps:
+ *   draft:   u = FC([e_t ; h_{t-1}])                    spec_hsr_fuse
+ *            text-anchored attention over text rows     spec_vata_attn
+ *            (or top-K sparse attention over all rows)  spec_topk_attn
+ *   verify:  gamma+1 rows against the full KV cache     spec_verify_attn
+ *   accept:  argmax + longest matching prefix           spec_accept
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers are DEVICE pointers unless marked (host).  The caller owns every
+ *   buffer; the library never allocates, frees or retains caller memory.
+ * - Every call is asynchronous on `stream`.  SPEC_OK means the work was
+ *   enqueued; faults surface at the caller's next synchronisation.  Every
+ *   argument error the host can detect returns a non-zero status before
+ *   anything is enqueued, so nothing is partially written.
+ * - Workspace: scratch memory comes from the caller (`ws`, `ws_bytes`), sized
+ *   by the matching spec_*_workspace() query (which depends only on shapes;
+ *   a size of 0 means the call needs none and `ws` may be NULL).  It needs no
+ *   initialisation: a call clears the counters it uses, in stream order,
+ *   before relying on them.  Calls that share a workspace must not run
+ *   concurrently (same stream, or ordered by events); calls with distinct
+ *   workspaces may run concurrently on different streams.
+ * - Query heads: q and out are [B, n_max, Hq, d] row-major; query head h
+ *   reads KV head h / (Hq / Hkv) (consecutive query heads share a KV head).
+ * - Positions: sequence b holds kv_len[b] KV positions, which include the
+ *   query rows' own K/V (the caller writes them before the call).  Query row
+ *   i < q_len[b] sits at absolute position P = kv_len[b] - q_len[b] + i and
+ *   sees key position j iff j <= P (bottom-right causal mask).  Rows
+ *   i >= q_len[b] are padding and are written as O = 0, LSE = -inf.
+ * - LSE is the natural-log log-sum-exp of the scaled scores, fp32
+ *   [B, n_max, Hq]; pass NULL to skip it.
+ * - Scores use the caller's `scale` (normally 1/sqrt(d)); Q and K are
+ *   post-rotary.  Accumulation is fp32 for every input dtype.
+ * - Contents of device index arrays (kv_len, q_len, text_idx, text_len,
+ *   page_table, draft, gamma) are preconditions: values outside the stated
+ *   ranges are undefined behaviour.
+ *
+ * Sources (the pages this library implements; titles as published):
+ * - "Sparrow: Text-Anchored Window Attention with Visual-Semantic Glimpsing
+ *   for Speculative Decoding in Video LLMs" (arXiv 2602.15318), as explained
+ *   on gist.science (zh and pt, technical summary section 3 / 3.A) and
+ *   summarised on shd-paper.top (method details).
+ * - "Sparse-to-Dense: A Free Lunch for Lossless Acceleration of Video
+ *   Understanding in LLMs", as explained on gist.science (pt), technical
+ *   summary "Metodologia" (decoding procedure, KV-cache selection).
+ */
+#ifndef SPECATTN_H
+#define SPECATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPEC_ABI_VERSION 1
+
+typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype_t;
+
+typedef enum {
+  SPEC_OK = 0,
+  SPEC_ERR_NULL = 1,        /* a required pointer is NULL                     */
+  SPEC_ERR_SHAPE = 2,       /* a size is out of range or inconsistent         */
+  SPEC_ERR_DTYPE = 3,       /* unsupported dtype or dtype combination         */
+  SPEC_ERR_WORKSPACE = 4,   /* ws_bytes below the spec_*_workspace() size     */
+  SPEC_ERR_UNSUPPORTED = 5, /* valid request outside what this build supports */
+  SPEC_ERR_HIP = 6          /* the HIP runtime refused a launch or query      */
+} spec_status_t;
+
+/*
+ * KV-cache descriptor.  Two layouts:
+ *  contiguous (page_size == 0): k, v are [B, num_kv_heads, max_len, head_dim];
+ *      position p of sequence b, head g is row (b*Hkv + g)*max_len + p.
+ *  paged (page_size a power of two, 1..256): k, v are a pool
+ *      [num_pages, num_kv_heads, page_size, head_dim]; position p of sequence
+ *      b lives in physical page page_table[b*max_pages + p/page_size] at slot
+ *      p % page_size.  max_len is then a host-side upper bound on kv_len[b]
+ *      (used only to size the launch).
+ * dtype is SPEC_F32 or SPEC_BF16 (both K and V); head_dim is 64 or 128.
+ * kv_len (device, [B]) gives 1 <= kv_len[b] <= max_len.
+ */
+typedef struct spec_kv {
+  const void* k;
+  const void* v;
+  int32_t dtype;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t max_len;
+  const int32_t* kv_len;
+  int32_t page_size;
+  int32_t max_pages;
+  const int32_t* page_table;
+} spec_kv_t;
+
+/*
+ * spec_verify_attn -- dense verification attention (Sparse-to-Dense,
+ * "Metodologia", decoding procedure: the dense model checks all gamma
+ * speculative tokens in parallel with one I/O pass over the full KV cache,
+ * using standard attention).
+ *
+ * q:      [B, n_max, Hq, head_dim] in q_dtype (must equal kv->dtype).
+ * q_len:  device [B], 1 <= q_len[b] <= min(n_max, kv_len[b]); NULL = n_max.
+ * out:    [B, n_max, Hq, head_dim] in out_dtype (SPEC_F32 or SPEC_BF16,
+ *         rounded to nearest even).
+ * lse:    fp32 [B, n_max, Hq] or NULL.
+ * Limits: n_max * (Hq / Hkv) <= 64; Hq % Hkv == 0.
+ * For every valid row: O = softmax(scale * q K^T + causal mask) V over key
+ * positions 0..P.
+ */
+size_t spec_verify_attn_workspace(const spec_kv_t* kv, int32_t batch, int32_t n_max,
+                                  int32_t num_q_heads);
+spec_status_t spec_verify_attn(const spec_kv_t* kv, int32_t batch, const void* q,
+                               int32_t q_dtype, int32_t n_max, const int32_t* q_len,
+                               int32_t num_q_heads, float scale, void* out, int32_t out_dtype,
+                               float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * spec_vata_attn -- text-anchored draft attention (Sparrow, technical summary
+ * 3.1 / 3.A: the draft drops the visual KV cache and attends only to
+ * text-anchored positions, so its cost scales with the text length).
+ *
+ * text_idx: device [B, t_max] int32 logical positions, 0 <= idx < kv_len[b];
+ * text_len: device [B], 0 <= text_len[b] <= t_max.  Only the K/V rows named
+ * by text_idx[b, 0..text_len[b]) are read.  Row i sees list entry t iff
+ * text_idx[b, t] <= P (its own absolute position); a repeated position counts
+ * twice; a row that sees no entry gets O = 0, LSE = -inf.
+ * Other arguments as spec_verify_attn.
+ */
+size_t spec_vata_attn_workspace(const spec_kv_t* kv, int32_t batch, int32_t n_max,
+                                int32_t num_q_heads, int32_t t_max);
+spec_status_t spec_vata_attn(const spec_kv_t* kv, int32_t batch, const void* q,
+                             int32_t q_dtype, int32_t n_max, const int32_t* q_len,
+                             int32_t num_q_heads, const int32_t* text_idx,
+                             const int32_t* text_len, int32_t t_max, float scale, void* out,
+                             int32_t out_dtype, float* lse, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
+
+/*
+ * spec_topk_attn -- top-K sparse draft attention (Sparse-to-Dense,
+ * "Metodologia": the sparse draft attends only to the most relevant KV
+ * entries; "Selecao de Cache KV": relevance is the group-mean attention
+ * score).  One query row per sequence at position kv_len[b]-1.
+ *
+ * Per (b, KV head g): qbar = sum of the group's query vectors (fp64, heads in
+ * increasing order); score_j = sum_c qbar[c]*K[b,g,j,c] (fp64, c increasing,
+ * every product and sum rounded, no fused multiply-add) for j < kv_len[b].
+ * Keys are ranked by (score descending, index ascending) and the first
+ * min(top_k, kv_len[b]) are kept.
+ * sel_idx: device [B, Hkv, top_k] int32, the kept positions in ascending
+ *          order, then -1 in unused slots.
+ * q:       [B, 1, Hq, head_dim]; out [B, 1, Hq, head_dim]; lse [B, 1, Hq].
+ * Every head of group g attends with plain softmax over the kept keys only.
+ */
+size_t spec_topk_attn_workspace(const spec_kv_t* kv, int32_t batch, int32_t num_q_heads,
+                                int32_t top_k);
+spec_status_t spec_topk_attn(const spec_kv_t* kv, int32_t batch, const void* q,
+                             int32_t q_dtype, int32_t num_q_heads, int32_t top_k, float scale,
+                             int32_t* sel_idx, void* out, int32_t out_dtype, float* lse,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * spec_hsr_fuse -- hidden-state-reuse fusion FC (Sparrow, technical summary
+ * 3.1 HSR: the current text embedding is concatenated with the target's
+ * reused text hidden state and projected by one fully connected layer).
+ *
+ * Y[r, o] = sum_{k < 2D} X[r, k] * W[o, k],  X[r] = concat(E[r], H[r]).
+ * e, h:  [m, d_model] bf16 row-major.   w: [d_model, 2*d_model] bf16
+ *        (output-major, the PyTorch Linear layout).  No bias.
+ * y:     [m, d_model] in out_dtype (SPEC_F32 or SPEC_BF16).
+ * fp32 accumulation on the matrix cores.  Limits: d_model % 64 == 0,
+ * 1 <= m <= 65536.
+ */
+size_t spec_hsr_fuse_workspace(int32_t m, int32_t d_model);
+spec_status_t spec_hsr_fuse(const void* e, const void* h, const void* w, int32_t dtype,
+                            int32_t m, int32_t d_model, void* y, int32_t out_dtype, void* ws,
+                            size_t ws_bytes, hipStream_t stream);
+
+/*
+ * spec_accept -- greedy acceptance (Sparse-to-Dense, "Metodologia", decoding
+ * procedure: keep the longest prefix of draft tokens that match the dense
+ * model's predictions, plus one bonus token from the dense model).
+ *
+ * logits:     [B, n_max, vocab] in dtype (SPEC_F32 or SPEC_BF16), finite.
+ * draft:      device [B, n_max-1] int32 draft tokens.
+ * gamma:      device [B] with 0 <= gamma[b] <= n_max-1; NULL = n_max-1.
+ * target_tok: device [B, n_max]: t[b,i] = lowest index of the maximum of row
+ *             i for i <= gamma[b] (IEEE compare, so -0 == +0), else -1.
+ * accept_len: device [B]: n_b = the largest n <= gamma[b] with
+ *             draft[b,j] == t[b,j] for all j < n.
+ * next_tok:   device [B]: t[b, n_b], the bonus token.
+ * The sequence grows by draft[b, 0..n_b) followed by next_tok[b].
+ */
+size_t spec_accept_workspace(int32_t batch, int32_t n_max, int32_t vocab);
+spec_status_t spec_accept(const void* logits, int32_t dtype, int32_t batch, int32_t n_max,
+                          int32_t vocab, const int32_t* draft, const int32_t* gamma,
+                          int32_t* target_tok, int32_t* accept_len, int32_t* next_tok,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* spec_status_str(spec_status_t status);
+
+/* SPEC_ABI_VERSION of the loaded library. */
+int32_t spec_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECATTN_H */

@@ -1,0 +1,342 @@
+"""ctypes binding of libspecattn (the C ABI declared in include/specattn.h).
+
+Argument marshalling only: every step of the hot path runs in the HIP
+library.  PyTorch provides device memory and the current stream.  Loading
+fails loudly when the library has not been built; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libspecattn.so")
+
+SPEC_F32 = 0
+SPEC_BF16 = 1
+SPEC_ABI_VERSION = 1
+
+STATUS = {
+    0: "SPEC_OK", 1: "SPEC_ERR_NULL", 2: "SPEC_ERR_SHAPE", 3: "SPEC_ERR_DTYPE",
+    4: "SPEC_ERR_WORKSPACE", 5: "SPEC_ERR_UNSUPPORTED", 6: "SPEC_ERR_HIP",
+}
+
+# Every function the header declares, with its ctypes signature.
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_F = ctypes.c_float
+_S = ctypes.c_size_t
+
+
+class SpecKV(ctypes.Structure):
+    """Mirror of ``spec_kv_t``."""
+
+    _fields_ = [("k", _P), ("v", _P), ("dtype", _I), ("num_kv_heads", _I), ("head_dim", _I),
+                ("max_len", _I), ("kv_len", _P), ("page_size", _I), ("max_pages", _I),
+                ("page_table", _P)]
+
+
+_KVP = ctypes.POINTER(SpecKV)
+
+SIGNATURES = {
+    "spec_verify_attn_workspace": (_S, [_KVP, _I, _I, _I]),
+    "spec_verify_attn": (_I, [_KVP, _I, _P, _I, _I, _P, _I, _F, _P, _I, _P, _P, _S, _P]),
+    "spec_vata_attn_workspace": (_S, [_KVP, _I, _I, _I, _I]),
+    "spec_vata_attn": (_I, [_KVP, _I, _P, _I, _I, _P, _I, _P, _P, _I, _F, _P, _I, _P, _P, _S, _P]),
+    "spec_topk_attn_workspace": (_S, [_KVP, _I, _I, _I]),
+    "spec_topk_attn": (_I, [_KVP, _I, _P, _I, _I, _I, _F, _P, _P, _I, _P, _P, _S, _P]),
+    "spec_hsr_fuse_workspace": (_S, [_I, _I]),
+    "spec_hsr_fuse": (_I, [_P, _P, _P, _I, _I, _I, _P, _I, _P, _S, _P]),
+    "spec_accept_workspace": (_S, [_I, _I, _I]),
+    "spec_accept": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _S, _P]),
+    "spec_status_str": (ctypes.c_char_p, [_I]),
+    "spec_abi_version": (_I, []),
+}
+
+
+class SpecError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} returned {STATUS.get(status, status)}")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"libspecattn is not built ({path} missing); run "
+                          "`python -m speculative_decoding_attention_amd.build` first")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if lib.spec_abi_version() != SPEC_ABI_VERSION:
+        raise ImportError("libspecattn ABI version mismatch")
+    return lib
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        _lib = load_library()
+    return _lib
+
+
+# ---------------------------------------------------------------- helpers --
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return SPEC_F32
+    if t == torch.bfloat16:
+        return SPEC_BF16
+    raise TypeError(f"unsupported dtype {t}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> torch.Tensor:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(fn: str, st: int):
+    if st != 0:
+        raise SpecError(fn, st)
+
+
+class Workspace:
+    """A device scratch buffer, grown on demand.
+
+    The library clears whatever counters it uses at the start of each call,
+    so one workspace can serve consecutive calls of any entry point on one
+    stream (never two overlapping calls).
+    """
+
+    def __init__(self, device=None):
+        self.device = torch.device(device) if device is not None else None
+        self.buf: Optional[torch.Tensor] = None
+
+    def get(self, nbytes: int, device: torch.device):
+        if nbytes == 0:
+            return None, 0
+        if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
+            self.buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        return ctypes.c_void_p(self.buf.data_ptr()), self.buf.numel()
+
+
+_default_ws = {}
+
+
+def _workspace(ws: Optional[Workspace], device: torch.device) -> Workspace:
+    if ws is not None:
+        return ws
+    key = (device.type, device.index)
+    if key not in _default_ws:
+        _default_ws[key] = Workspace(device)
+    return _default_ws[key]
+
+
+class KVCache:
+    """Descriptor of a KV cache held in torch device tensors.
+
+    Contiguous: k, v ``[B, Hkv, max_len, d]``.  Paged: k, v
+    ``[num_pages, Hkv, page_size, d]`` with ``page_table [B, max_pages]``
+    int32 and a host-side bound ``max_len`` on the lengths.
+    """
+
+    def __init__(self, k: torch.Tensor, v: torch.Tensor, kv_len: torch.Tensor,
+                 page_table: Optional[torch.Tensor] = None, page_size: int = 0,
+                 max_len: Optional[int] = None):
+        _dev(k, "k")
+        _dev(v, "v", k.dtype)
+        _dev(kv_len, "kv_len", torch.int32)
+        if k.shape != v.shape or k.dim() != 4:
+            raise ValueError("k and v must have the same 4-d shape")
+        self.k, self.v, self.kv_len = k, v, kv_len
+        self.page_size = int(page_size)
+        self.page_table = page_table
+        if self.page_size:
+            _dev(page_table, "page_table", torch.int32)
+            if k.shape[2] != self.page_size:
+                raise ValueError("paged k/v must be [num_pages, Hkv, page_size, d]")
+            if max_len is None:
+                raise ValueError("paged caches need a host-side max_len bound")
+            self.max_len = int(max_len)
+        else:
+            self.max_len = int(k.shape[2]) if max_len is None else int(max_len)
+            if self.max_len != k.shape[2]:
+                raise ValueError("contiguous max_len must equal k.shape[2]")
+        self.struct = SpecKV(
+            k.data_ptr(), v.data_ptr(), _dtype_code(k.dtype), int(k.shape[1]), int(k.shape[3]),
+            self.max_len, kv_len.data_ptr(), self.page_size,
+            int(page_table.shape[1]) if self.page_size else 0,
+            page_table.data_ptr() if self.page_size else None)
+
+    @property
+    def num_kv_heads(self) -> int:
+        return int(self.k.shape[1])
+
+    @property
+    def head_dim(self) -> int:
+        return int(self.k.shape[3])
+
+    @property
+    def device(self) -> torch.device:
+        return self.k.device
+
+
+# -------------------------------------------------------- entry points ----
+
+def spec_verify_attn(kv: KVCache, q: torch.Tensor, q_len: Optional[torch.Tensor] = None,
+                     scale: Optional[float] = None, out_dtype: Optional[torch.dtype] = None,
+                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                     want_lse: bool = True, workspace: Optional[Workspace] = None):
+    """Dense verification attention; returns (out, lse)."""
+    L = lib()
+    _dev(q, "q", kv.k.dtype)
+    B, n_max, Hq, d = q.shape
+    if q_len is not None:
+        _dev(q_len, "q_len", torch.int32)
+    out_dtype = out_dtype or q.dtype
+    if out is None:
+        out = torch.empty((B, n_max, Hq, d), dtype=out_dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, n_max, Hq), dtype=torch.float32, device=q.device)
+    scale = float(d ** -0.5) if scale is None else float(scale)
+    need = L.spec_verify_attn_workspace(ctypes.byref(kv.struct), B, n_max, Hq)
+    wsp, wsn = _workspace(workspace, q.device).get(need, q.device)
+    st = L.spec_verify_attn(ctypes.byref(kv.struct), B, _ptr(q), _dtype_code(q.dtype), n_max,
+                            _ptr(q_len), Hq, scale, _ptr(out), _dtype_code(out.dtype), _ptr(lse),
+                            wsp, wsn, _stream(q.device))
+    _check("spec_verify_attn", st)
+    return out, lse
+
+
+def spec_vata_attn(kv: KVCache, q: torch.Tensor, text_idx: torch.Tensor, text_len: torch.Tensor,
+                   q_len: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                   out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+                   workspace: Optional[Workspace] = None):
+    """Text-anchored draft attention over text_idx; returns (out, lse)."""
+    L = lib()
+    _dev(q, "q", kv.k.dtype)
+    _dev(text_idx, "text_idx", torch.int32)
+    _dev(text_len, "text_len", torch.int32)
+    B, n_max, Hq, d = q.shape
+    t_max = int(text_idx.shape[1])
+    if q_len is not None:
+        _dev(q_len, "q_len", torch.int32)
+    out_dtype = out_dtype or q.dtype
+    if out is None:
+        out = torch.empty((B, n_max, Hq, d), dtype=out_dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, n_max, Hq), dtype=torch.float32, device=q.device)
+    scale = float(d ** -0.5) if scale is None else float(scale)
+    need = L.spec_vata_attn_workspace(ctypes.byref(kv.struct), B, n_max, Hq, t_max)
+    wsp, wsn = _workspace(workspace, q.device).get(need, q.device)
+    st = L.spec_vata_attn(ctypes.byref(kv.struct), B, _ptr(q), _dtype_code(q.dtype), n_max,
+                          _ptr(q_len), Hq, _ptr(text_idx), _ptr(text_len), t_max, scale,
+                          _ptr(out), _dtype_code(out.dtype), _ptr(lse), wsp, wsn,
+                          _stream(q.device))
+    _check("spec_vata_attn", st)
+    return out, lse
+
+
+def spec_topk_attn(kv: KVCache, q: torch.Tensor, top_k: int, scale: Optional[float] = None,
+                   out_dtype: Optional[torch.dtype] = None, sel_idx: Optional[torch.Tensor] = None,
+                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                   want_lse: bool = True, workspace: Optional[Workspace] = None):
+    """Top-K sparse draft attention for one query row; returns (sel_idx, out, lse)."""
+    L = lib()
+    _dev(q, "q", kv.k.dtype)
+    B, one, Hq, d = q.shape
+    if one != 1:
+        raise ValueError("q must be [B, 1, Hq, d]")
+    out_dtype = out_dtype or q.dtype
+    if sel_idx is None:
+        sel_idx = torch.empty((B, kv.num_kv_heads, top_k), dtype=torch.int32, device=q.device)
+    if out is None:
+        out = torch.empty((B, 1, Hq, d), dtype=out_dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, 1, Hq), dtype=torch.float32, device=q.device)
+    scale = float(d ** -0.5) if scale is None else float(scale)
+    need = L.spec_topk_attn_workspace(ctypes.byref(kv.struct), B, Hq, top_k)
+    wsp, wsn = _workspace(workspace, q.device).get(need, q.device)
+    st = L.spec_topk_attn(ctypes.byref(kv.struct), B, _ptr(q), _dtype_code(q.dtype), Hq, int(top_k),
+                          scale, _ptr(sel_idx), _ptr(out), _dtype_code(out.dtype), _ptr(lse),
+                          wsp, wsn, _stream(q.device))
+    _check("spec_topk_attn", st)
+    return sel_idx, out, lse
+
+
+def spec_hsr_fuse(e: torch.Tensor, h: torch.Tensor, w: torch.Tensor,
+                  out_dtype: torch.dtype = torch.bfloat16, y: Optional[torch.Tensor] = None,
+                  workspace: Optional[Workspace] = None):
+    """HSR fusion FC: Y = concat(E, H) @ W^T; returns y."""
+    L = lib()
+    _dev(e, "e", torch.bfloat16)
+    _dev(h, "h", torch.bfloat16)
+    _dev(w, "w", torch.bfloat16)
+    m, d = e.shape
+    if h.shape != e.shape or tuple(w.shape) != (d, 2 * d):
+        raise ValueError("expected e, h [m, d] and w [d, 2d]")
+    if y is None:
+        y = torch.empty((m, d), dtype=out_dtype, device=e.device)
+    need = L.spec_hsr_fuse_workspace(m, d)
+    wsp, wsn = _workspace(workspace, e.device).get(need, e.device)
+    st = L.spec_hsr_fuse(_ptr(e), _ptr(h), _ptr(w), SPEC_BF16, m, d, _ptr(y), _dtype_code(y.dtype),
+                         wsp, wsn, _stream(e.device))
+    _check("spec_hsr_fuse", st)
+    return y
+
+
+def spec_accept(logits: torch.Tensor, draft: torch.Tensor, gamma: Optional[torch.Tensor] = None,
+                target_tok: Optional[torch.Tensor] = None,
+                accept_len: Optional[torch.Tensor] = None,
+                next_tok: Optional[torch.Tensor] = None,
+                workspace: Optional[Workspace] = None):
+    """Greedy acceptance; returns (target_tok, accept_len, next_tok)."""
+    L = lib()
+    _dev(logits, "logits")
+    B, n_max, V = logits.shape
+    _dev(draft, "draft", torch.int32)
+    if gamma is not None:
+        _dev(gamma, "gamma", torch.int32)
+    dev = logits.device
+    if target_tok is None:
+        target_tok = torch.empty((B, n_max), dtype=torch.int32, device=dev)
+    if accept_len is None:
+        accept_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    if next_tok is None:
+        next_tok = torch.empty((B,), dtype=torch.int32, device=dev)
+    need = L.spec_accept_workspace(B, n_max, V)
+    wsp, wsn = _workspace(workspace, dev).get(need, dev)
+    st = L.spec_accept(_ptr(logits), _dtype_code(logits.dtype), B, n_max, V, _ptr(draft),
+                       _ptr(gamma), _ptr(target_tok), _ptr(accept_len), _ptr(next_tok), wsp, wsn,
+                       _stream(dev))
+    _check("spec_accept", st)
+    return target_tok, accept_len, next_tok
+
+
+def spec_status_str(status: int) -> str:
+    return lib().spec_status_str(status).decode()
+
+
+def spec_abi_version() -> int:
+    return int(lib().spec_abi_version())

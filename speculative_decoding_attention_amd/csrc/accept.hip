@@ -1,0 +1,183 @@
+// Greedy acceptance on gfx950: per-row argmax over the vocabulary, then the
+// longest prefix of draft tokens that match, plus the bonus token.
+//
+// The vocabulary scan is split into chunks so every CU streams the logits.
+// A workgroup reduces its chunk to one packed 64-bit key
+//   (order-preserving bits of the value) << 32 | (0xFFFFFFFF - index)
+// whose maximum is "largest value, then lowest index" in any reduction order,
+// and merges it into its row with a 64-bit atomic max.  The last workgroup of
+// each sequence (arrival counter) turns the row maxima into target tokens,
+// counts the matching prefix and writes the outputs.  The maxima and counters
+// are cleared by a fill kernel at the start of every call.
+#include "common.h"
+#include "internal.h"
+
+namespace spec {
+
+namespace {
+
+constexpr int kAcceptThreads = 256;
+
+struct AcceptArgs {
+  const void* logits;
+  const int32_t* draft;
+  const int32_t* gamma;
+  int32_t* target_tok;
+  int32_t* accept_len;
+  int32_t* next_tok;
+  unsigned long long* best;   // [B, n_max] packed maxima (cleared per call)
+  uint32_t* tick;             // [B] arrival counters (cleared per call)
+  int32_t B, n_max, V, chunk, chunks, vec;
+};
+
+__device__ __forceinline__ unsigned long long pack_key(float x, uint32_t idx) {
+  if (x == 0.f) x = 0.f;                       // IEEE: -0 == +0
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t k = (u >> 31) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)k << 32) | (0xFFFFFFFFu - idx);
+}
+
+__device__ __forceinline__ unsigned long long umax64(unsigned long long a, unsigned long long b) {
+  return a > b ? a : b;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kAcceptThreads) void accept_kernel(AcceptArgs a) {
+  __shared__ unsigned long long red[kAcceptThreads / 64];
+  __shared__ uint32_t s_tick;
+  const int row = blockIdx.x / a.chunks;              // b * n_max + i
+  const int ch = blockIdx.x - row * a.chunks;
+  const int b = row / a.n_max, i = row - b * a.n_max;
+  const int gam = a.gamma ? min(max(a.gamma[b], 0), a.n_max - 1) : a.n_max - 1;
+  const int v0 = ch * a.chunk, v1 = min(a.V, v0 + a.chunk);
+  unsigned long long best = 0;
+  if (i <= gam) {
+    if (BF16) {
+      const uint16_t* p = reinterpret_cast<const uint16_t*>(a.logits) + (size_t)row * a.V;
+      if (a.vec) {
+        for (int v = v0 + 8 * threadIdx.x; v < v1; v += 8 * kAcceptThreads) {
+          const u32x4_t w = ld16(p + v);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            best = umax64(best, pack_key(__uint_as_float(w[j] << 16), v + 2 * j));
+            best = umax64(best, pack_key(__uint_as_float(w[j] & 0xFFFF0000u), v + 2 * j + 1));
+          }
+        }
+      } else {
+        for (int v = v0 + threadIdx.x; v < v1; v += kAcceptThreads)
+          best = umax64(best, pack_key(bf16_bits_to_f32(p[v]), v));
+      }
+    } else {
+      const float* p = reinterpret_cast<const float*>(a.logits) + (size_t)row * a.V;
+      if (a.vec) {
+        for (int v = v0 + 4 * threadIdx.x; v < v1; v += 4 * kAcceptThreads) {
+          const u32x4_t w = ld16(p + v);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) best = umax64(best, pack_key(__uint_as_float(w[j]), v + j));
+        }
+      } else {
+        for (int v = v0 + threadIdx.x; v < v1; v += kAcceptThreads)
+          best = umax64(best, pack_key(p[v], v));
+      }
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+      const unsigned long long other =
+          ((unsigned long long)(uint32_t)__shfl_xor((int)(best >> 32), o) << 32) |
+          (uint32_t)__shfl_xor((int)(uint32_t)best, o);
+      best = umax64(best, other);
+    }
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = best;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      unsigned long long m = red[0];
+      for (int w = 1; w < kAcceptThreads / 64; ++w) m = umax64(m, red[w]);
+      atomicMax(&a.best[row], m);
+    }
+  }
+  // every workgroup of the sequence arrives, including rows past gamma
+  if (threadIdx.x == 0) {
+    __threadfence();
+    s_tick = atomicAdd(&a.tick[b], 1u);
+  }
+  __syncthreads();
+  if (s_tick != (uint32_t)(a.n_max * a.chunks - 1)) return;
+  if (threadIdx.x == 0) {
+    __threadfence();
+    int n = -1, nxt = 0;
+    for (int r = 0; r < a.n_max; ++r) {
+      unsigned long long* slot = &a.best[(size_t)b * a.n_max + r];
+      const unsigned long long k = atomicExch(slot, 0ull);
+      const int t = (r <= gam) ? (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull)) : -1;
+      a.target_tok[(size_t)b * a.n_max + r] = t;
+      if (r <= gam && n < 0) {
+        if (r == gam || a.draft[(size_t)b * (a.n_max - 1) + r] != t) {
+          n = r;
+          nxt = t;
+        }
+      }
+    }
+    a.accept_len[b] = n;
+    a.next_tok[b] = nxt;
+    a.tick[b] = 0u;
+  }
+}
+
+struct AcceptPlan {
+  int chunk, chunks, vec;
+  size_t off_tick, ws_bytes;
+};
+
+AcceptPlan plan_accept(int batch, int n_max, int vocab, bool bf16) {
+  AcceptPlan p;
+  const int elems_per_thread = bf16 ? 128 : 64;     // 256 B of logits per thread
+  p.chunk = kAcceptThreads * elems_per_thread;
+  const int vw = bf16 ? 8 : 4;
+  p.vec = (vocab % vw == 0) ? 1 : 0;
+  if (p.chunk > vocab) p.chunk = ((vocab + vw - 1) / vw) * vw;
+  p.chunks = (vocab + p.chunk - 1) / p.chunk;
+  p.off_tick = align_up((size_t)batch * n_max * sizeof(unsigned long long), 256);
+  p.ws_bytes = p.off_tick + align_up((size_t)batch * sizeof(uint32_t), 256);
+  return p;
+}
+
+}  // namespace
+
+size_t accept_workspace(int batch, int n_max, int vocab) {
+  const AcceptPlan a = plan_accept(batch, n_max, vocab, true);
+  const AcceptPlan b = plan_accept(batch, n_max, vocab, false);
+  return a.ws_bytes > b.ws_bytes ? a.ws_bytes : b.ws_bytes;
+}
+
+spec_status_t launch_accept(const void* logits, int dtype, int batch, int n_max, int vocab,
+                            const int32_t* draft, const int32_t* gamma, int32_t* target_tok,
+                            int32_t* accept_len, int32_t* next_tok, void* ws,
+                            hipStream_t stream) {
+  const bool bf16 = (dtype == SPEC_BF16);
+  const AcceptPlan p = plan_accept(batch, n_max, vocab, bf16);
+  AcceptArgs a;
+  a.logits = logits;
+  a.draft = draft;
+  a.gamma = gamma;
+  a.target_tok = target_tok;
+  a.accept_len = accept_len;
+  a.next_tok = next_tok;
+  a.best = reinterpret_cast<unsigned long long*>(ws);
+  a.tick = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws) + p.off_tick);
+  a.B = batch;
+  a.n_max = n_max;
+  a.V = vocab;
+  a.chunk = p.chunk;
+  a.chunks = p.chunks;
+  a.vec = p.vec;
+  // row maxima and arrival counters start at zero
+  const spec_status_t st = launch_zero(ws, p.off_tick + (size_t)batch * sizeof(uint32_t), stream);
+  if (st != SPEC_OK) return st;
+  const dim3 grid((unsigned)batch * n_max * p.chunks), block(kAcceptThreads);
+  if (bf16)
+    hipLaunchKernelGGL(accept_kernel<true>, grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL(accept_kernel<false>, grid, block, 0, stream, a);
+  return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+}  // namespace spec

@@ -1,0 +1,238 @@
+// C ABI of libspecattn: argument validation, workspace sizing and launch.
+// Every argument error the host can detect is reported before anything is
+// enqueued on the caller's stream.
+#include <math.h>
+#include <string.h>
+
+#include "internal.h"
+
+using namespace spec;
+
+namespace {
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int log2_int(int x) {
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
+}
+
+spec_status_t check_kv(const spec_kv_t* kv) {
+  if (!kv || !kv->k || !kv->v || !kv->kv_len) return SPEC_ERR_NULL;
+  if (kv->dtype != SPEC_F32 && kv->dtype != SPEC_BF16) return SPEC_ERR_DTYPE;
+  if (kv->head_dim != 64 && kv->head_dim != 128) return SPEC_ERR_UNSUPPORTED;
+  if (kv->num_kv_heads < 1 || kv->max_len < 1) return SPEC_ERR_SHAPE;
+  if (kv->page_size != 0) {
+    if (!is_pow2(kv->page_size) || kv->page_size > 256) return SPEC_ERR_SHAPE;
+    if (!kv->page_table) return SPEC_ERR_NULL;
+    if (kv->max_pages < 1) return SPEC_ERR_SHAPE;
+    if ((long long)kv->max_pages * kv->page_size < kv->max_len) return SPEC_ERR_SHAPE;
+  }
+  return SPEC_OK;
+}
+
+spec_status_t check_common(const spec_kv_t* kv, int32_t batch, const void* q, int32_t q_dtype,
+                           int32_t n_max, int32_t num_q_heads, float scale, const void* out,
+                           int32_t out_dtype) {
+  const spec_status_t st = check_kv(kv);
+  if (st != SPEC_OK) return st;
+  if (!q || !out) return SPEC_ERR_NULL;
+  if (batch < 1 || n_max < 1 || num_q_heads < 1) return SPEC_ERR_SHAPE;
+  if (num_q_heads % kv->num_kv_heads != 0) return SPEC_ERR_SHAPE;
+  if (q_dtype != kv->dtype) return SPEC_ERR_DTYPE;
+  if (out_dtype != SPEC_F32 && out_dtype != SPEC_BF16) return SPEC_ERR_DTYPE;
+  if (!isfinite(scale)) return SPEC_ERR_SHAPE;
+  if ((long long)n_max * (num_q_heads / kv->num_kv_heads) > 64) return SPEC_ERR_UNSUPPORTED;
+  if ((long long)batch * kv->num_kv_heads > (1 << 24)) return SPEC_ERR_SHAPE;
+  return SPEC_OK;
+}
+
+AttnArgs make_args(const spec_kv_t* kv, int32_t batch, const void* q, int32_t n_max,
+                   const int32_t* q_len, int32_t num_q_heads, float scale, void* out,
+                   int32_t out_dtype, float* lse) {
+  AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = kv->k;
+  a.v = kv->v;
+  a.kv_len = kv->kv_len;
+  a.q_len = q_len;
+  a.page_table = kv->page_size ? kv->page_table : nullptr;
+  a.max_pages = kv->max_pages;
+  a.page_shift = kv->page_size ? log2_int(kv->page_size) : -1;
+  a.B = batch;
+  a.Hq = num_q_heads;
+  a.Hkv = kv->num_kv_heads;
+  a.G = num_q_heads / kv->num_kv_heads;
+  a.n_max = n_max;
+  a.R = n_max * a.G;
+  a.max_len = kv->max_len;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.out = out;
+  a.out_bf16 = (out_dtype == SPEC_BF16);
+  a.lse = lse;
+  return a;
+}
+
+spec_status_t check_ws(size_t need, const void* ws, size_t ws_bytes) {
+  if (need == 0) return SPEC_OK;
+  if (!ws) return SPEC_ERR_NULL;
+  if (ws_bytes < need) return SPEC_ERR_WORKSPACE;
+  return SPEC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t spec_abi_version(void) { return SPEC_ABI_VERSION; }
+
+const char* spec_status_str(spec_status_t status) {
+  switch (status) {
+    case SPEC_OK: return "SPEC_OK";
+    case SPEC_ERR_NULL: return "SPEC_ERR_NULL: a required pointer is NULL";
+    case SPEC_ERR_SHAPE: return "SPEC_ERR_SHAPE: a size is out of range or inconsistent";
+    case SPEC_ERR_DTYPE: return "SPEC_ERR_DTYPE: unsupported dtype or dtype combination";
+    case SPEC_ERR_WORKSPACE: return "SPEC_ERR_WORKSPACE: workspace smaller than required";
+    case SPEC_ERR_UNSUPPORTED: return "SPEC_ERR_UNSUPPORTED: outside what this build supports";
+    case SPEC_ERR_HIP: return "SPEC_ERR_HIP: the HIP runtime refused a launch or query";
+  }
+  return "unknown spec_status_t";
+}
+
+// ------------------------------------------------------------- verify ----
+
+size_t spec_verify_attn_workspace(const spec_kv_t* kv, int32_t batch, int32_t n_max,
+                                  int32_t num_q_heads) {
+  if (check_kv(kv) != SPEC_OK || batch < 1 || n_max < 1 || num_q_heads < 1 ||
+      num_q_heads % kv->num_kv_heads)
+    return 0;
+  const int R = n_max * (num_q_heads / kv->num_kv_heads);
+  return plan_attention(batch * kv->num_kv_heads, kv->max_len, R, kv->head_dim).ws_bytes;
+}
+
+spec_status_t spec_verify_attn(const spec_kv_t* kv, int32_t batch, const void* q,
+                               int32_t q_dtype, int32_t n_max, const int32_t* q_len,
+                               int32_t num_q_heads, float scale, void* out, int32_t out_dtype,
+                               float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  spec_status_t st =
+      check_common(kv, batch, q, q_dtype, n_max, num_q_heads, scale, out, out_dtype);
+  if (st != SPEC_OK) return st;
+  AttnArgs a = make_args(kv, batch, q, n_max, q_len, num_q_heads, scale, out, out_dtype, lse);
+  a.mode = 0;
+  const AttnPlan plan = plan_attention(batch * kv->num_kv_heads, kv->max_len, a.R, kv->head_dim);
+  st = check_ws(plan.ws_bytes, ws, ws_bytes);
+  if (st != SPEC_OK) return st;
+  return launch_attention(a, kv->head_dim, kv->dtype, plan, ws, stream);
+}
+
+// --------------------------------------------------------------- VATA ----
+
+size_t spec_vata_attn_workspace(const spec_kv_t* kv, int32_t batch, int32_t n_max,
+                                int32_t num_q_heads, int32_t t_max) {
+  if (check_kv(kv) != SPEC_OK || batch < 1 || n_max < 1 || num_q_heads < 1 || t_max < 1 ||
+      num_q_heads % kv->num_kv_heads)
+    return 0;
+  const int R = n_max * (num_q_heads / kv->num_kv_heads);
+  return plan_attention(batch * kv->num_kv_heads, t_max, R, kv->head_dim).ws_bytes;
+}
+
+spec_status_t spec_vata_attn(const spec_kv_t* kv, int32_t batch, const void* q,
+                             int32_t q_dtype, int32_t n_max, const int32_t* q_len,
+                             int32_t num_q_heads, const int32_t* text_idx,
+                             const int32_t* text_len, int32_t t_max, float scale, void* out,
+                             int32_t out_dtype, float* lse, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+  spec_status_t st =
+      check_common(kv, batch, q, q_dtype, n_max, num_q_heads, scale, out, out_dtype);
+  if (st != SPEC_OK) return st;
+  if (!text_idx || !text_len) return SPEC_ERR_NULL;
+  if (t_max < 1) return SPEC_ERR_SHAPE;
+  AttnArgs a = make_args(kv, batch, q, n_max, q_len, num_q_heads, scale, out, out_dtype, lse);
+  a.mode = 1;
+  a.slots = text_idx;
+  a.slot_len = text_len;
+  a.slot_stride = t_max;
+  const AttnPlan plan = plan_attention(batch * kv->num_kv_heads, t_max, a.R, kv->head_dim);
+  st = check_ws(plan.ws_bytes, ws, ws_bytes);
+  if (st != SPEC_OK) return st;
+  return launch_attention(a, kv->head_dim, kv->dtype, plan, ws, stream);
+}
+
+// -------------------------------------------------------------- top-K ----
+
+size_t spec_topk_attn_workspace(const spec_kv_t* kv, int32_t batch, int32_t num_q_heads,
+                                int32_t top_k) {
+  if (check_kv(kv) != SPEC_OK || batch < 1 || num_q_heads < 1 || top_k < 1 ||
+      num_q_heads % kv->num_kv_heads)
+    return 0;
+  const int G = num_q_heads / kv->num_kv_heads;
+  return plan_topk(batch * kv->num_kv_heads, kv->max_len, top_k, G, kv->head_dim).ws_bytes;
+}
+
+spec_status_t spec_topk_attn(const spec_kv_t* kv, int32_t batch, const void* q,
+                             int32_t q_dtype, int32_t num_q_heads, int32_t top_k, float scale,
+                             int32_t* sel_idx, void* out, int32_t out_dtype, float* lse,
+                             void* ws, size_t ws_bytes, hipStream_t stream) {
+  spec_status_t st = check_common(kv, batch, q, q_dtype, 1, num_q_heads, scale, out, out_dtype);
+  if (st != SPEC_OK) return st;
+  if (!sel_idx) return SPEC_ERR_NULL;
+  if (top_k < 1) return SPEC_ERR_SHAPE;
+  if ((long long)batch * kv->num_kv_heads * kv->max_len > (1LL << 31)) return SPEC_ERR_SHAPE;
+  AttnArgs a = make_args(kv, batch, q, 1, nullptr, num_q_heads, scale, out, out_dtype, lse);
+  const TopkPlan plan = plan_topk(batch * kv->num_kv_heads, kv->max_len, top_k, a.R, kv->head_dim);
+  st = check_ws(plan.ws_bytes, ws, ws_bytes);
+  if (st != SPEC_OK) return st;
+  st = launch_topk_select(a, kv->head_dim, kv->dtype, top_k, sel_idx, plan, ws, stream);
+  if (st != SPEC_OK) return st;
+  a.mode = 2;
+  a.slots = sel_idx;
+  a.slot_stride = top_k;
+  return launch_attention(a, kv->head_dim, kv->dtype, plan.attn,
+                          reinterpret_cast<char*>(ws) + plan.off_attn, stream);
+}
+
+// ---------------------------------------------------------------- HSR ----
+
+size_t spec_hsr_fuse_workspace(int32_t m, int32_t d_model) {
+  if (m < 1 || m > 65536 || d_model < 64 || d_model % 64) return 0;
+  return hsr_workspace(m, d_model);
+}
+
+spec_status_t spec_hsr_fuse(const void* e, const void* h, const void* w, int32_t dtype,
+                            int32_t m, int32_t d_model, void* y, int32_t out_dtype, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
+  if (!e || !h || !w || !y) return SPEC_ERR_NULL;
+  if (dtype != SPEC_BF16) return SPEC_ERR_DTYPE;
+  if (out_dtype != SPEC_F32 && out_dtype != SPEC_BF16) return SPEC_ERR_DTYPE;
+  if (m < 1 || m > 65536 || d_model < 64 || d_model % 64 || d_model > (1 << 16))
+    return SPEC_ERR_SHAPE;
+  const spec_status_t st = check_ws(hsr_workspace(m, d_model), ws, ws_bytes);
+  if (st != SPEC_OK) return st;
+  return launch_hsr(e, h, w, m, d_model, y, out_dtype == SPEC_BF16, ws, stream);
+}
+
+// ------------------------------------------------------------- accept ----
+
+size_t spec_accept_workspace(int32_t batch, int32_t n_max, int32_t vocab) {
+  if (batch < 1 || n_max < 1 || vocab < 1) return 0;
+  return accept_workspace(batch, n_max, vocab);
+}
+
+spec_status_t spec_accept(const void* logits, int32_t dtype, int32_t batch, int32_t n_max,
+                          int32_t vocab, const int32_t* draft, const int32_t* gamma,
+                          int32_t* target_tok, int32_t* accept_len, int32_t* next_tok,
+                          void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!logits || !target_tok || !accept_len || !next_tok) return SPEC_ERR_NULL;
+  if (n_max > 1 && !draft) return SPEC_ERR_NULL;
+  if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ERR_DTYPE;
+  if (batch < 1 || n_max < 1 || vocab < 1 || vocab >= 0x7fffffff) return SPEC_ERR_SHAPE;
+  if ((long long)batch * n_max > (1 << 24)) return SPEC_ERR_SHAPE;
+  const spec_status_t st = check_ws(accept_workspace(batch, n_max, vocab), ws, ws_bytes);
+  if (st != SPEC_OK) return st;
+  return launch_accept(logits, dtype, batch, n_max, vocab, draft, gamma, target_tok, accept_len,
+                       next_tok, ws, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Shared device helpers for the gfx950 kernels (wave64, MFMA, LDS).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace spec {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kXcds = 8;  // MI355X: 256 CUs in 8 XCDs, one L2 each
+
+// Workgroups are dealt round-robin to the XCDs (WG i runs on XCD i % 8).
+// Remap so that each XCD gets a contiguous range of work items: neighbouring
+// work (the splits of one (sequence, KV head) unit, the tiles of one GEMM
+// row band) then shares that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int i, int n) {
+  const int per = n / kXcds, rem = n % kXcds;
+  const int x = i % kXcds, j = i / kXcds;
+  return (x < rem) ? x * (per + 1) + j : rem * (per + 1) + (x - rem) * per + j;
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Round to nearest even (inputs are finite on every path that calls this).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// 16-byte global load / store helpers.
+__device__ __forceinline__ u32x4_t ld16(const void* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) {
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// Butterfly reductions across lanes l ^ 16 and l ^ 32 (the four 16-lane
+// rows of a wave that hold the same MFMA output column).
+__device__ __forceinline__ float max_across_rows(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+__device__ __forceinline__ float sum_across_rows(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+}  // namespace spec

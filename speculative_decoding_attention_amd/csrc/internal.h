@@ -1,0 +1,89 @@
+// Host-side interfaces between the C-ABI layer (api.hip) and the kernel
+// translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/specattn.h"
+
+namespace spec {
+
+// Arguments of the split-K attention kernel.  One "unit" is a (sequence b,
+// KV head g) pair; its key slots t in [0, T_b) map to positions through
+// `mode`:
+//   0  dense:        position = t,                         T_b = kv_len[b]
+//   1  text list:    position = slots[b*stride + t],       T_b = slot_len[b]
+//   2  top-K list:   position = slots[(b*Hkv+g)*stride+t], T_b = min(stride, kv_len[b])
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* kv_len;
+  const int32_t* q_len;       // may be null (= n_max)
+  const int32_t* page_table;  // paged layout when page_shift >= 0
+  int32_t max_pages;
+  int32_t page_shift;
+  const int32_t* slots;
+  const int32_t* slot_len;
+  int32_t slot_stride;
+  int32_t mode;
+  int32_t B, Hq, Hkv, G, n_max, R, max_len;
+  int32_t S, chunk;           // splits per unit and slots per split
+  float scale_log2;           // softmax scale * log2(e)
+  float* part_acc;            // [U*S, R, D] unnormalised partial outputs
+  float* part_ml;             // [U*S, 3, R] partial (max, sum, rounded-weight sum), log2 domain
+  void* out;
+  int32_t out_bf16;
+  float* lse;
+};
+
+struct AttnPlan {
+  int S = 1;
+  int chunk = 0;
+  int grid = 0;
+  size_t ws_bytes = 0;
+  size_t off_ml = 0;
+};
+
+int device_cu_count();
+
+// Split plan for U units of at most t_max slots and R rows of width d.
+AttnPlan plan_attention(int units, int t_max, int rows, int d);
+
+spec_status_t launch_attention(AttnArgs a, int d, int dtype, const AttnPlan& plan, void* ws,
+                               hipStream_t stream);
+
+// Top-K: scores + selection into sel_idx, then attention via launch_attention.
+struct TopkPlan {
+  size_t off_scores = 0;    // fp64 [U, max_len]
+  size_t off_hist = 0;      // uint32 [U, 4096]
+  size_t off_attn = 0;      // attention workspace
+  AttnPlan attn;
+  size_t ws_bytes = 0;
+};
+TopkPlan plan_topk(int units, int max_len, int top_k, int rows, int d);
+spec_status_t launch_topk_select(const AttnArgs& a, int d, int dtype, int top_k,
+                                 int32_t* sel_idx, const TopkPlan& plan, void* ws,
+                                 hipStream_t stream);
+
+// HSR fusion GEMM.
+size_t hsr_workspace(int m, int d_model);
+spec_status_t launch_hsr(const void* e, const void* h, const void* w, int m, int d_model,
+                         void* y, int out_bf16, void* ws, hipStream_t stream);
+
+// Greedy acceptance.
+size_t accept_workspace(int batch, int n_max, int vocab);
+spec_status_t launch_accept(const void* logits, int dtype, int batch, int n_max, int vocab,
+                            const int32_t* draft, const int32_t* gamma, int32_t* target_tok,
+                            int32_t* accept_len, int32_t* next_tok, void* ws,
+                            hipStream_t stream);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Clears `bytes` (a multiple of 4) at `p` with a fill kernel, so it is safe
+// inside captured graphs.
+spec_status_t launch_zero(void* p, size_t bytes, hipStream_t stream);
+
+}  // namespace spec

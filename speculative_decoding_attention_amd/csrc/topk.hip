@@ -1,0 +1,390 @@
+// Top-K key selection for sparse draft attention (gfx950).
+//
+// Score (per sequence b, KV head g, key j < kv_len[b]):
+//   qbar[c]  = q[h0][c] + q[h0+1][c] + ...   (fp64, heads of the group in order)
+//   score_j  = (((0 + qbar[0]*k_j[0]) + qbar[1]*k_j[1]) + ...)   (fp64, c in
+//              order, each product and each sum rounded separately)
+// The evaluation order is fixed so the result is reproducible bit for bit by
+// any implementation.  Keys are ranked by (score desc, index asc).
+//
+// topk_score_kernel: 256 keys per workgroup are staged through LDS with
+//   coalesced 16-byte loads; each thread then runs one key's fp64 chain.  It
+//   writes the score and adds the key to a per-unit 4096-bin histogram of a
+//   coarse monotone key (the top 12 bits of the order-preserving bit pattern
+//   of float(score): sign, exponent, 3 mantissa bits).
+// topk_select_kernel: one 1024-thread workgroup per unit.  From the
+//   histogram it finds the bin holding the K-th key, gathers that bin's keys
+//   into LDS, sorts them by (score desc, index asc), which fixes the exact
+//   threshold (score*, index*), then writes the selected indices in ascending
+//   order with a block-wide ordered compaction.  If the boundary bin holds
+//   more keys than LDS can sort, an exact radix select over the 64-bit keys
+//   (8-bit digits) takes over.
+#include <math.h>
+
+#include "common.h"
+#include "internal.h"
+
+namespace spec {
+
+namespace {
+
+constexpr int kHistBins = 4096;
+constexpr int kScoreKeys = 256;   // keys per score workgroup
+constexpr int kCandMax = 4096;    // candidates sortable in LDS
+
+struct TopkArgs {
+  const void* q;
+  const void* k;
+  const int32_t* kv_len;
+  const int32_t* page_table;
+  int32_t max_pages, page_shift;
+  int32_t B, Hq, Hkv, G, max_len, top_k;
+  double* scores;       // [U, max_len]
+  uint32_t* hist;       // [U, kHistBins]
+  int32_t* sel_idx;     // [U, top_k]
+};
+
+__device__ __forceinline__ size_t topk_row(const TopkArgs& a, int b, int g, int pos) {
+  if (a.page_shift >= 0) {
+    const int page = a.page_table[(size_t)b * a.max_pages + (pos >> a.page_shift)];
+    const int slot = pos & ((1 << a.page_shift) - 1);
+    return (((size_t)page * a.Hkv + g) << a.page_shift) + slot;
+  }
+  return ((size_t)b * a.Hkv + g) * (size_t)a.max_len + pos;
+}
+
+// Order-preserving 64-bit key of a double; -0 is folded onto +0.
+__device__ __forceinline__ uint64_t order_key64(double x) {
+  if (x == 0.0) x = 0.0;
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+__device__ __forceinline__ uint32_t coarse_bin(double x) {
+  float f = (float)x;                   // round to nearest: monotone non-decreasing
+  if (f == 0.f) f = 0.f;
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t k = (u >> 31) ? ~u : (u | 0x80000000u);
+  return k >> 20;
+}
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void topk_score_kernel(TopkArgs a) {
+  constexpr int ROW_B = BF16 ? D * 2 : D * 4;       // bytes per key row
+  constexpr int PITCH = ROW_B + 8;                  // padded LDS pitch
+  __shared__ __align__(16) unsigned char krows[kScoreKeys * PITCH];
+  __shared__ double qbar[D];
+  __shared__ uint32_t hist[kHistBins];
+
+  const int tiles = (a.max_len + kScoreKeys - 1) / kScoreKeys;
+  const int u = blockIdx.x / tiles, tile = blockIdx.x - (blockIdx.x / tiles) * tiles;
+  const int b = u / a.Hkv, g = u - b * a.Hkv;
+  const int L = a.kv_len[b];
+  const int j0 = tile * kScoreKeys;
+  if (j0 >= L) return;
+  const int nk = min(kScoreKeys, L - j0);
+
+  for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) hist[i] = 0;
+  if (threadIdx.x < D) {
+    double s = 0.0;
+    for (int h = g * a.G; h < (g + 1) * a.G; ++h) {
+      const size_t qi = ((size_t)b * a.Hq + h) * D + threadIdx.x;   // q is [B, 1, Hq, D]
+      const double qv = BF16 ? (double)bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(a.q)[qi])
+                             : (double)reinterpret_cast<const float*>(a.q)[qi];
+      s = __dadd_rn(s, qv);
+    }
+    qbar[threadIdx.x] = s;
+  }
+  // stage the K rows: ROW_B/16 chunks of 16 bytes per key
+  constexpr int CH = ROW_B / 16;
+  const unsigned char* kb = reinterpret_cast<const unsigned char*>(a.k);
+  for (int e = threadIdx.x; e < nk * CH; e += blockDim.x) {
+    const int key = e / CH, ch = e - (e / CH) * CH;
+    const u32x4_t v = ld16(kb + topk_row(a, b, g, j0 + key) * ROW_B + ch * 16);
+    uint2* dst = reinterpret_cast<uint2*>(krows + key * PITCH + ch * 16);   // 8-byte aligned
+    dst[0] = make_uint2(v[0], v[1]);
+    dst[1] = make_uint2(v[2], v[3]);
+  }
+  __syncthreads();
+
+  const int key = threadIdx.x;
+  if (key < nk) {
+    double acc = 0.0;
+    const unsigned char* row = krows + key * PITCH;
+    if (BF16) {
+      for (int c = 0; c < D; c += 4) {
+        const uint2 w = *reinterpret_cast<const uint2*>(row + c * 2);
+        const double k0 = (double)__uint_as_float(w.x << 16);
+        const double k1 = (double)__uint_as_float(w.x & 0xFFFF0000u);
+        const double k2 = (double)__uint_as_float(w.y << 16);
+        const double k3 = (double)__uint_as_float(w.y & 0xFFFF0000u);
+        acc = __dadd_rn(acc, __dmul_rn(qbar[c], k0));
+        acc = __dadd_rn(acc, __dmul_rn(qbar[c + 1], k1));
+        acc = __dadd_rn(acc, __dmul_rn(qbar[c + 2], k2));
+        acc = __dadd_rn(acc, __dmul_rn(qbar[c + 3], k3));
+      }
+    } else {
+      for (int c = 0; c < D; c += 2) {
+        const float2 w = *reinterpret_cast<const float2*>(row + c * 4);
+        acc = __dadd_rn(acc, __dmul_rn(qbar[c], (double)w.x));
+        acc = __dadd_rn(acc, __dmul_rn(qbar[c + 1], (double)w.y));
+      }
+    }
+    a.scores[(size_t)u * a.max_len + j0 + key] = acc;
+    atomicAdd(&hist[coarse_bin(acc)], 1u);
+  }
+  __syncthreads();
+  uint32_t* gh = a.hist + (size_t)u * kHistBins;
+  for (int i = threadIdx.x; i < kHistBins; i += blockDim.x)
+    if (hist[i]) atomicAdd(&gh[i], hist[i]);
+}
+
+// Block-wide exclusive prefix sum of one value per thread (1024 threads).
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum,
+                                                         uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t run = 0;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+      const uint32_t t = wsum[w];
+      wsum[w] = run;
+      run += t;
+    }
+    *total = run;
+  }
+  __syncthreads();
+  const uint32_t r = wsum[wave] + x - v;
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ bool cand_before(uint64_t ka, int ia, uint64_t kb, int ib) {
+  return ka > kb || (ka == kb && ia < ib);   // (score desc, index asc)
+}
+
+__global__ __launch_bounds__(1024) void topk_select_kernel(TopkArgs a) {
+  __shared__ uint64_t ckey[kCandMax];
+  __shared__ int32_t cidx[kCandMax];
+  __shared__ uint32_t wsum[16];
+  __shared__ uint32_t s_total, s_ncand, s_bin, s_above;
+  __shared__ uint64_t s_thr_key;
+  __shared__ int32_t s_thr_idx;
+  __shared__ uint32_t dh[256];
+
+  const int u = blockIdx.x;
+  const int b = u / a.Hkv;
+  const int L = a.kv_len[b];
+  const int K = a.top_k;
+  const double* sc = a.scores + (size_t)u * a.max_len;
+  int32_t* out = a.sel_idx + (size_t)u * K;
+  uint32_t* gh = a.hist + (size_t)u * kHistBins;
+  const int tid = threadIdx.x, nt = blockDim.x;
+
+  if (K >= L) {
+    for (int j = tid; j < K; j += nt) out[j] = (j < L) ? j : -1;
+    for (int i = tid; i < kHistBins; i += nt) gh[i] = 0;
+    return;
+  }
+
+  // (a) boundary bin of the coarse histogram: highest bin whose suffix count
+  //     reaches K.  Thread t owns bins [4t, 4t+4); counts scanned from the top.
+  if (tid == 0) {
+    s_bin = 0;
+    s_above = 0;
+  }
+  uint32_t c4[4];
+  uint32_t mine = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    c4[i] = gh[kHistBins - 1 - (tid * 4 + i)];   // descending bin order
+    mine += c4[i];
+  }
+  const uint32_t before = block_exclusive_scan(mine, wsum, &s_total);
+  {
+    uint32_t run = before;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (run < (uint32_t)K && run + c4[i] >= (uint32_t)K) {
+        s_bin = kHistBins - 1 - (tid * 4 + i);
+        s_above = run;
+      }
+      run += c4[i];
+    }
+  }
+  if (tid == 0) s_ncand = 0;
+  __syncthreads();
+  for (int i = tid; i < kHistBins; i += nt) gh[i] = 0;   // leave the histogram clean
+  const uint32_t bstar = s_bin;
+  int need = K - (int)s_above;                           // 1..count(bstar)
+
+  // (b) gather the boundary bin's keys
+  for (int j = tid; j < L; j += nt) {
+    const double s = sc[j];
+    if (coarse_bin(s) == bstar) {
+      const uint32_t p = atomicAdd(&s_ncand, 1u);
+      if (p < (uint32_t)kCandMax) {
+        ckey[p] = order_key64(s);
+        cidx[p] = j;
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t ncand = s_ncand;
+
+  if (ncand <= (uint32_t)kCandMax) {
+    // (c) bitonic sort of the candidates, padded to a power of two
+    uint32_t n2 = 1;
+    while (n2 < ncand) n2 <<= 1;
+    for (uint32_t i = ncand + tid; i < n2; i += nt) {
+      ckey[i] = 0;          // below every real key
+      cidx[i] = 0x7fffffff;
+    }
+    __syncthreads();
+    for (uint32_t size = 2; size <= n2; size <<= 1) {
+      for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+        for (uint32_t t = tid; t < n2 / 2; t += nt) {
+          const uint32_t lo = 2 * t - (t & (stride - 1));
+          const uint32_t hi = lo + stride;
+          const bool up = ((lo & size) == 0);   // "up" = (score desc, index asc) order
+          const uint64_t kl = ckey[lo], kh = ckey[hi];
+          const int il = cidx[lo], ih = cidx[hi];
+          const bool swap = up ? cand_before(kh, ih, kl, il) : cand_before(kl, il, kh, ih);
+          if (swap) {
+            ckey[lo] = kh; ckey[hi] = kl;
+            cidx[lo] = ih; cidx[hi] = il;
+          }
+        }
+        __syncthreads();
+      }
+    }
+    need = max(1, min(need, (int)max(ncand, 1u)));        // guards a corrupted histogram
+    if (tid == 0) {
+      s_thr_key = ckey[need - 1];
+      s_thr_idx = cidx[need - 1];
+    }
+    __syncthreads();
+  } else {
+    // Exact radix select on the 64-bit keys of the boundary bin, 8-bit digits
+    // from the top; `rem` keys of the current prefix group are still needed.
+    uint64_t prefix = 0, pmask = 0;
+    int rem = need;
+    for (int shift = 56; shift >= 0; shift -= 8) {
+      for (int i = tid; i < 256; i += nt) dh[i] = 0;
+      __syncthreads();
+      for (int j = tid; j < L; j += nt) {
+        const double s = sc[j];
+        if (coarse_bin(s) != bstar) continue;
+        const uint64_t kk = order_key64(s);
+        if ((kk & pmask) == prefix) atomicAdd(&dh[(kk >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        uint32_t run = 0;
+        int dsel = 0;
+        for (int dgt = 255; dgt >= 0; --dgt) {
+          if (run + dh[dgt] >= (uint32_t)rem) { dsel = dgt; break; }
+          run += dh[dgt];
+        }
+        s_bin = (uint32_t)dsel;
+        s_above = run;
+      }
+      __syncthreads();
+      prefix |= (uint64_t)s_bin << shift;
+      pmask |= 255ull << shift;
+      rem -= (int)s_above;
+      __syncthreads();
+    }
+    // every key equal to `prefix` ties; the lowest `rem` indices among them win
+    uint32_t cnt_before = 0;
+    int thr = -1;
+    for (int j0 = 0; j0 < L && thr < 0; j0 += nt) {
+      const int j = j0 + tid;
+      const uint32_t f = (j < L && order_key64(sc[j]) == prefix) ? 1u : 0u;
+      const uint32_t ex = block_exclusive_scan(f, wsum, &s_total);
+      if (f && cnt_before + ex + 1 == (uint32_t)rem) s_thr_idx = j;
+      __syncthreads();
+      if (cnt_before + s_total >= (uint32_t)rem) thr = s_thr_idx;
+      cnt_before += s_total;
+      __syncthreads();
+    }
+    if (tid == 0) s_thr_key = prefix;
+    __syncthreads();
+  }
+
+  // (d) ordered compaction of the selected keys
+  const uint64_t tk = s_thr_key;
+  const int ti = s_thr_idx;
+  uint32_t base = 0;
+  for (int j0 = 0; j0 < L; j0 += nt) {
+    const int j = j0 + tid;
+    uint32_t f = 0;
+    if (j < L) {
+      const uint64_t kk = order_key64(sc[j]);
+      f = (kk > tk || (kk == tk && j <= ti)) ? 1u : 0u;
+    }
+    const uint32_t ex = block_exclusive_scan(f, wsum, &s_total);
+    if (f && base + ex < (uint32_t)K) out[base + ex] = j;
+    base += s_total;
+  }
+  for (int j = K - 1 - tid; j >= (int)base; j -= nt) out[j] = -1;   // base == K here
+}
+
+}  // namespace
+
+TopkPlan plan_topk(int units, int max_len, int top_k, int rows, int d) {
+  TopkPlan p;
+  p.off_scores = 0;
+  p.off_hist = align_up((size_t)units * max_len * sizeof(double), 256);
+  p.off_attn = align_up(p.off_hist + (size_t)units * kHistBins * sizeof(uint32_t), 256);
+  p.attn = plan_attention(units, top_k, rows, d);
+  p.ws_bytes = p.off_attn + p.attn.ws_bytes;
+  return p;
+}
+
+spec_status_t launch_topk_select(const AttnArgs& aa, int d, int dtype, int top_k,
+                                 int32_t* sel_idx, const TopkPlan& plan, void* ws,
+                                 hipStream_t stream) {
+  TopkArgs a;
+  a.q = aa.q;
+  a.k = aa.k;
+  a.kv_len = aa.kv_len;
+  a.page_table = aa.page_table;
+  a.max_pages = aa.max_pages;
+  a.page_shift = aa.page_shift;
+  a.B = aa.B;
+  a.Hq = aa.Hq;
+  a.Hkv = aa.Hkv;
+  a.G = aa.G;
+  a.max_len = aa.max_len;
+  a.top_k = top_k;
+  char* w = reinterpret_cast<char*>(ws);
+  a.scores = reinterpret_cast<double*>(w + plan.off_scores);
+  a.hist = reinterpret_cast<uint32_t*>(w + plan.off_hist);
+  a.sel_idx = sel_idx;
+  const int units = a.B * a.Hkv;
+  const int tiles = (a.max_len + kScoreKeys - 1) / kScoreKeys;
+  spec_status_t st = launch_zero(a.hist, (size_t)units * kHistBins * sizeof(uint32_t), stream);
+  if (st != SPEC_OK) return st;
+  const dim3 grid(units * tiles), block(256);
+  if (dtype == SPEC_BF16) {
+    if (d == 64) hipLaunchKernelGGL((topk_score_kernel<64, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((topk_score_kernel<128, true>), grid, block, 0, stream, a);
+  } else {
+    if (d == 64) hipLaunchKernelGGL((topk_score_kernel<64, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((topk_score_kernel<128, false>), grid, block, 0, stream, a);
+  }
+  if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
+  hipLaunchKernelGGL(topk_select_kernel, dim3(units), dim3(1024), 0, stream, a);
+  if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
+  return SPEC_OK;
+}
+
+}  // namespace spec

@@ -1,0 +1,123 @@
+"""The C-ABI library builds, loads, exports every function include/specattn.h
+declares, and rejects every host-detectable argument error before anything is
+enqueued (these calls never reach a launch, so they run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specattn.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from speculative_decoding_attention_amd import _binding, build
+    if not os.path.exists(_binding.LIB_PATH):
+        build.build_library()
+    return _binding.load_library()
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:size_t|spec_status_t|const char\*|int32_t)\s+(spec_\w+)\s*\(",
+                                 src, flags=re.M)))
+
+
+def test_header_declares_the_five_entry_points():
+    names = _declared_functions()
+    for n in ["spec_verify_attn", "spec_vata_attn", "spec_topk_attn", "spec_hsr_fuse",
+              "spec_accept"]:
+        assert n in names and n + "_workspace" in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    from speculative_decoding_attention_amd import _binding
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+        assert name in _binding.SIGNATURES, name
+
+
+def test_version_and_status_strings(L):
+    assert L.spec_abi_version() == 1
+    for code in range(7):
+        s = L.spec_status_str(code).decode()
+        assert s.startswith("SPEC_")
+    assert L.spec_status_str(99).decode() == "unknown spec_status_t"
+
+
+FAKE = 0x10000   # never dereferenced: every call below fails validation first
+
+
+def _kv(**over):
+    from speculative_decoding_attention_amd._binding import SpecKV
+    f = dict(k=FAKE, v=FAKE, dtype=1, num_kv_heads=4, head_dim=128, max_len=1024,
+             kv_len=FAKE, page_size=0, max_pages=0, page_table=None)
+    f.update(over)
+    return SpecKV(**f)
+
+
+def _verify(L, kv, B=1, q=FAKE, q_dtype=1, n_max=6, Hq=28, scale=0.088, out=FAKE, out_dtype=1,
+            ws=None, ws_bytes=0):
+    return L.spec_verify_attn(ctypes.byref(kv), B, q, q_dtype, n_max, None, Hq, scale, out,
+                              out_dtype, None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(k=None), 1), (dict(kv_len=None), 1), (dict(dtype=7), 3), (dict(head_dim=96), 5),
+    (dict(num_kv_heads=0), 2), (dict(max_len=0), 2), (dict(page_size=12), 2),
+    (dict(page_size=16, page_table=None, max_pages=4), 1),
+    (dict(page_size=16, page_table=FAKE, max_pages=4), 2),     # 4*16 < max_len
+])
+def test_verify_rejects_bad_kv(L, over, code):
+    assert _verify(L, _kv(**over)) == code
+
+
+def test_verify_rejects_bad_args(L):
+    kv = _kv()
+    assert _verify(L, kv, q=None) == 1
+    assert _verify(L, kv, out=None) == 1
+    assert _verify(L, kv, Hq=30) == 2                 # 30 % 4 != 0
+    assert _verify(L, kv, B=0) == 2
+    assert _verify(L, kv, n_max=0) == 2
+    assert _verify(L, kv, q_dtype=0) == 3             # q dtype != kv dtype
+    assert _verify(L, kv, out_dtype=5) == 3
+    assert _verify(L, kv, n_max=10) == 5              # 10 * 7 rows > 64
+    assert _verify(L, kv, scale=float("nan")) == 2
+    need = L.spec_verify_attn_workspace(ctypes.byref(kv), 1, 6, 28)
+    assert need > 0
+    assert _verify(L, kv, ws=None, ws_bytes=0) == 1
+    assert _verify(L, kv, ws=FAKE, ws_bytes=need - 1) == 4
+
+
+def test_vata_topk_rejections(L):
+    kv = _kv()
+    assert L.spec_vata_attn(ctypes.byref(kv), 1, FAKE, 1, 1, None, 28, None, FAKE, 512, 0.1, FAKE,
+                            1, None, None, 0, None) == 1
+    assert L.spec_vata_attn(ctypes.byref(kv), 1, FAKE, 1, 1, None, 28, FAKE, FAKE, 0, 0.1, FAKE,
+                            1, None, None, 0, None) == 2
+    assert L.spec_topk_attn(ctypes.byref(kv), 1, FAKE, 1, 28, 0, 0.1, FAKE, FAKE, 1, None, None,
+                            0, None) == 2
+    assert L.spec_topk_attn(ctypes.byref(kv), 1, FAKE, 1, 28, 16, 0.1, None, FAKE, 1, None, None,
+                            0, None) == 1
+    need = L.spec_topk_attn_workspace(ctypes.byref(kv), 1, 28, 16)
+    assert need >= 8 * 4 * 1024                        # fp64 scores for every key
+    assert L.spec_topk_attn(ctypes.byref(kv), 1, FAKE, 1, 28, 16, 0.1, FAKE, FAKE, 1, None,
+                            FAKE, need - 1, None) == 4
+
+
+def test_hsr_and_accept_rejections(L):
+    assert L.spec_hsr_fuse(None, FAKE, FAKE, 1, 4, 64, FAKE, 1, None, 0, None) == 1
+    assert L.spec_hsr_fuse(FAKE, FAKE, FAKE, 0, 4, 64, FAKE, 1, None, 0, None) == 3
+    assert L.spec_hsr_fuse(FAKE, FAKE, FAKE, 1, 4, 96, FAKE, 1, None, 0, None) == 2
+    assert L.spec_hsr_fuse(FAKE, FAKE, FAKE, 1, 0, 64, FAKE, 1, None, 0, None) == 2
+    assert L.spec_accept(None, 1, 1, 6, 100, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == 1
+    assert L.spec_accept(FAKE, 1, 1, 6, 100, None, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == 1
+    assert L.spec_accept(FAKE, 2, 1, 6, 100, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == 3
+    assert L.spec_accept(FAKE, 1, 1, 0, 100, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == 2
+    need = L.spec_accept_workspace(64, 6, 152064)
+    assert need >= 64 * 6 * 8
+    assert L.spec_accept(FAKE, 1, 64, 6, 152064, FAKE, None, FAKE, FAKE, FAKE, FAKE, need - 1,
+                         None) == 4

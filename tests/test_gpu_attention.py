@@ -1,0 +1,252 @@
+"""GPU parity of verification and text-anchored attention against the CPU
+oracle, at test sizes that span several tiles and splits with ragged tails,
+and at the full workload sizes the bench times."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import DEV, assert_attention_close, dev, kvcache
+
+pytestmark = pytest.mark.gpu
+
+
+def _lib():
+    import speculative_decoding_attention_amd as S
+    return S
+
+
+def _verify_pair(c, out_dtype=torch.float32):
+    S = _lib()
+    kv = kvcache(c)
+    q_len = dev(c.q_len.astype(np.int32))
+    out, lse = S.spec_verify_attn(kv, dev(c.q), q_len=q_len, scale=c.scale, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    ro, rl = oracle.verify_attention(c.q.values, c.k.values, c.v.values, c.kv_len, c.q_len,
+                                     c.num_kv_heads, c.scale, c.page_table, c.page_size)
+    return out, lse, ro, rl
+
+
+def _vata_pair(c, out_dtype=torch.float32, idx=None, tlen=None):
+    S = _lib()
+    idx = c.text_idx if idx is None else idx
+    tlen = c.text_len if tlen is None else tlen
+    kv = kvcache(c)
+    out, lse = S.spec_vata_attn(kv, dev(c.q), dev(idx.astype(np.int32)),
+                                dev(tlen.astype(np.int32)), q_len=dev(c.q_len.astype(np.int32)),
+                                scale=c.scale, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    ro, rl = oracle.vata_attention(c.q.values, c.k.values, c.v.values, c.kv_len, c.q_len, idx,
+                                   tlen, c.num_kv_heads, c.scale, c.page_table, c.page_size)
+    return out, lse, ro, rl
+
+
+# ------------------------------------------------------------ tiny (C1) ----
+
+def test_c1_verify_fp32():
+    c, _ = W.c1_tiny()
+    out, lse, ro, rl = _verify_pair(c)
+    assert_attention_close(out, lse, ro, rl, c.q_len, W.F32, "c1 verify")
+
+
+@pytest.mark.parametrize("n", [1, 5])
+def test_c1_vata_fp32(n):
+    c, _ = W.c1_tiny()
+    if n == 1:
+        c.q = W.Stored(W.F32, c.q.bits[:, -1:].copy())
+        c.q_len = np.array([1], np.int32)
+    out, lse, ro, rl = _vata_pair(c)
+    assert_attention_close(out, lse, ro, rl, c.q_len, W.F32, f"c1 vata n={n}")
+
+
+# ------------------------------------------------------- small ragged ----
+
+SMALL = [
+    # seed, B, Hq, Hkv, d, n, L, dtype, page
+    (1, 2, 8, 2, 128, 5, (700, 1333), W.BF16, 0),
+    (2, 3, 28, 4, 128, 6, (2000, 77, 1029), W.BF16, 16),
+    (3, 2, 4, 1, 64, 3, (300, 901), W.BF16, 0),
+    (4, 2, 14, 2, 128, 8, (517, 1500), W.BF16, 32),     # 56 rows per unit
+    (5, 2, 4, 2, 64, 4, (250, 999), W.F32, 0),
+    (6, 1, 6, 2, 128, 2, (1025,), W.F32, 16),
+    (7, 2, 16, 1, 128, 4, (64, 1), W.BF16, 0),          # 64 rows; a 1-key sequence
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: f"s{c[0]}")
+def test_small_verify(cfg):
+    seed, B, Hq, Hkv, d, n, L, dt, page = cfg
+    n_eff = [min(n, x) for x in np.broadcast_to(L, (B,))]
+    c = W.small_attn(seed, B, Hq, Hkv, d, n, L, dt, page_size=page, q_len=n_eff)
+    out, lse, ro, rl = _verify_pair(c)
+    assert_attention_close(out, lse, ro, rl, c.q_len, dt, f"small verify {seed}")
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: f"s{c[0]}")
+def test_small_vata(cfg):
+    seed, B, Hq, Hkv, d, n, L, dt, page = cfg
+    n_eff = [min(n, x) for x in np.broadcast_to(L, (B,))]
+    c = W.small_attn(seed, B, Hq, Hkv, d, n, L, dt, page_size=page, q_len=n_eff)
+    out, lse, ro, rl = _vata_pair(c)
+    assert_attention_close(out, lse, ro, rl, c.q_len, dt, f"small vata {seed}")
+
+
+def test_padded_query_rows_and_bf16_output():
+    c = W.small_attn(11, 3, 8, 2, 128, 6, (900, 450, 1200), W.BF16, q_len=[6, 2, 4])
+    out, lse, ro, rl = _verify_pair(c, out_dtype=torch.bfloat16)
+    assert out.dtype == torch.bfloat16
+    assert_attention_close(out, lse, ro, rl, c.q_len, W.BF16, "padded rows")
+
+
+def test_vata_empty_and_partial_lists():
+    """text_len = 0 gives O = 0, LSE = -inf; a list whose entries all lie
+    after the first rows' positions leaves those rows empty."""
+    c = W.small_attn(12, 2, 8, 2, 128, 4, (600, 600), W.BF16)
+    idx = np.zeros((2, 8), np.int32)
+    idx[1, :3] = [597, 598, 599]            # rows 0..2 of seq 1 see 0..2 entries
+    tlen = np.array([0, 3], np.int32)
+    out, lse, ro, rl = _vata_pair(c, idx=idx, tlen=tlen)
+    o = out.cpu().numpy()
+    assert np.all(o[0] == 0) and np.all(np.isneginf(lse[0].cpu().numpy()))
+    assert np.all(np.isneginf(lse[1, 0].cpu().numpy()))
+    assert_attention_close(out, lse, ro, rl, c.q_len, W.BF16, "vata partial")
+
+
+# -------------------------------------------------------- invariants ----
+
+def test_values_one_gives_one_and_lse_normalises():
+    c = W.small_attn(13, 2, 28, 4, 128, 6, (3000, 2111), W.BF16)
+    c.v = W.Stored.from_f32(np.ones(c.v.shape, np.float32), W.BF16)
+    out, lse, ro, rl = _verify_pair(c)
+    dev1 = float(np.abs(out.cpu().numpy() - 1.0).max())
+    assert dev1 < 1e-6, dev1
+    # sum_j exp(s_j - LSE) = 1 with scores from torch fp64 on the device data
+    b, i, h = 1, 3, 17
+    L, n = int(c.kv_len[b]), int(c.q_len[b])
+    k = torch.tensor(c.k.values[b, h // 7, :L - n + i + 1], dtype=torch.float64)
+    s = c.scale * (k @ torch.tensor(c.q.values[b, i, h], dtype=torch.float64))
+    assert abs(float(torch.exp(s - float(lse[b, i, h])).sum()) - 1.0) < 1e-5
+
+
+def test_vata_all_positions_equals_verify_on_device():
+    S = _lib()
+    c = W.small_attn(14, 2, 28, 4, 128, 6, (1800, 2500), W.BF16)
+    kv = kvcache(c)
+    q = dev(c.q)
+    o1, l1 = S.spec_verify_attn(kv, q, scale=c.scale, out_dtype=torch.float32)
+    idx = torch.arange(c.max_len, dtype=torch.int32, device=DEV).repeat(2, 1).contiguous()
+    o2, l2 = S.spec_vata_attn(kv, q, idx, dev(c.kv_len.astype(np.int32)), scale=c.scale,
+                              out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_first_verify_row_equals_decode_on_device():
+    S = _lib()
+    c = W.small_attn(15, 2, 28, 4, 128, 6, (2222, 1111), W.BF16)
+    kv = kvcache(c)
+    o, l = S.spec_verify_attn(kv, dev(c.q), scale=c.scale, out_dtype=torch.float32)
+    kv1 = kvcache(c)
+    kv1_len = dev((c.kv_len - 5).astype(np.int32))
+    from speculative_decoding_attention_amd import KVCache
+    kvd = KVCache(kv1.k, kv1.v, kv1_len)
+    od, ld = S.spec_verify_attn(kvd, dev(c.q)[:, :1].contiguous(), scale=c.scale,
+                                out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert (o[:, 0] - od[:, 0]).abs().max().item() < 2e-3 * o.abs().max().item()
+    assert (l[:, 0] - ld[:, 0]).abs().max().item() < 1e-4
+
+
+def test_paged_equals_contiguous_on_device():
+    S = _lib()
+    c = W.small_attn(16, 2, 28, 4, 128, 6, (1700, 2600), W.BF16, page_size=16)
+    o1, l1 = S.spec_verify_attn(kvcache(c), dev(c.q), scale=c.scale, out_dtype=torch.float32)
+    B, Hkv, d, Lm = 2, 4, 128, c.max_len
+    kc = np.zeros((B, Hkv, Lm, d), np.uint16)
+    vc = np.zeros((B, Hkv, Lm, d), np.uint16)
+    for b in range(B):
+        L = int(c.kv_len[b])
+        kc[b, :, :L] = oracle.paged_rows(c.k.bits, c.page_table, b, L, 16)
+        vc[b, :, :L] = oracle.paged_rows(c.v.bits, c.page_table, b, L, 16)
+    from speculative_decoding_attention_amd import KVCache
+    kv2 = KVCache(dev(W.Stored(W.BF16, kc)), dev(W.Stored(W.BF16, vc)),
+                  dev(c.kv_len.astype(np.int32)))
+    o2, l2 = S.spec_verify_attn(kv2, dev(c.q), scale=c.scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_repeated_calls_are_bitwise_identical():
+    S = _lib()
+    c = W.small_attn(17, 1, 28, 4, 128, 6, (25512,), W.BF16)
+    kv = kvcache(c)
+    q = dev(c.q)
+    ref = S.spec_verify_attn(kv, q, scale=c.scale, out_dtype=torch.float32)
+    for _ in range(3):
+        o, l = S.spec_verify_attn(kv, q, scale=c.scale, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref[0]) and torch.equal(l, ref[1])
+
+
+# ------------------------------------------------- full workload sizes ----
+
+@pytest.fixture(scope="module")
+def c2():
+    return W.c2_sparrow(0, with_hsr=False)[0]
+
+
+def test_c2_verify_full(c2):
+    out, lse, ro, rl = _verify_pair(c2)
+    assert_attention_close(out, lse, ro, rl, c2.q_len, W.BF16, "c2 verify")
+
+
+def test_c2_verify_bf16_output_as_benched(c2):
+    out, lse, ro, rl = _verify_pair(c2, out_dtype=torch.bfloat16)
+    assert_attention_close(out, lse, ro, rl, c2.q_len, W.BF16, "c2 verify bf16 out")
+
+
+@pytest.mark.parametrize("n", [1, 6])
+def test_c2_vata_full(c2, n):
+    c = c2
+    if n == 1:
+        c = W.AttnCase(**{**c2.__dict__})
+        c.q = W.Stored(W.BF16, c2.q.bits[:, -1:].copy())
+        c.q_len = np.array([1], np.int32)
+    out, lse, ro, rl = _vata_pair(c)
+    assert_attention_close(out, lse, ro, rl, c.q_len, W.BF16, f"c2 vata n={n}")
+
+
+@pytest.fixture(scope="module")
+def c3():
+    return W.c3_ragged_paged(0)
+
+
+def test_c3_verify_full(c3):
+    out, lse, ro, rl = _verify_pair(c3)
+    assert_attention_close(out, lse, ro, rl, c3.q_len, W.BF16, "c3 verify")
+
+
+def test_c3_vata_full(c3):
+    out, lse, ro, rl = _vata_pair(c3)
+    assert_attention_close(out, lse, ro, rl, c3.q_len, W.BF16, "c3 vata")
+
+
+def test_c4_verify_sampled():
+    """Dense verification at L = 32768, B = 4: every output of two sampled
+    (sequence, KV head) units against the oracle."""
+    S = _lib()
+    c = W.c4_topk(0)
+    out, lse = S.spec_verify_attn(kvcache(c), dev(c.q), q_len=dev(c.q_len), scale=c.scale,
+                                  out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    units = [(0, 0), (3, 2)]
+    ro, rl = oracle.verify_attention(c.q.values, c.k.values, c.v.values, c.kv_len, c.q_len, 4,
+                                     c.scale, units=units)
+    o = out.cpu().numpy()
+    l = lse.cpu().numpy()
+    for b, g in units:
+        hs = slice(g * 7, g * 7 + 7)
+        err = np.abs(o[b, :, hs] - ro[b, :, hs]).max()
+        assert err <= 1e-2 * np.abs(ro[b, :, hs]).max() and err <= 2e-2
+        assert np.abs(l[b, :, hs] - rl[b, :, hs]).max() <= 1e-3
