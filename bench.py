@@ -1,0 +1,309 @@
+"""Benchmark of the speculative-decoding hot path on one MI355X.
+
+Workload: the 25k-visual-token step -- one sequence, 28 query / 4 KV heads of
+dim 128, 25,000 visual + 512 text KV positions (64 interleaved + 448
+trailing), gamma = 5, hidden size 3584, vocabulary 152,064, bf16 inputs with
+fp32 accumulation.  Inputs are seeded synthetic normals (the pages measure on
+video benchmarks and trained models that are not used here).
+
+One step = one speculative iteration through every hot-path entry point:
+  5 x [ spec_hsr_fuse (one row, 7168 -> 3584)  ->  spec_vata_attn (n = 1) ]
+  spec_topk_attn  (one query, K = 2048 over all 25,512 keys)
+  spec_verify_attn (gamma + 1 = 6 rows over all 25,512 keys)
+  spec_accept      (argmax over [6, 152,064] bf16 logits + prefix)
+
+Timing: every timed unit is a captured HIP graph replayed on one stream, with
+HIP events around the replays; KV caches, HSR weights and logits rotate over
+enough copies that each call streams from HBM, not the 256 MiB Infinity
+Cache.  The headline value is the verification attention's algorithmic HBM
+bandwidth; draft steps/s is 1 / (HSR + text-anchored attention time).
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix peak
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_c2_traffic.json")
+KERNEL_SOURCES = ["attention.hip", "common.h", "internal.h", "api.hip"]
+
+
+def _parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--rotate", type=int, default=10, help="buffer copies cycled through")
+    ap.add_argument("--reps", type=int, default=40, help="replays of each per-entry-point graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--only", choices=["verify", "vata", "hsr", "topk", "accept", "step"],
+                    default=None, help="time one part only (for counter passes)")
+    return ap.parse_args()
+
+
+def _source_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "speculative_decoding_attention_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(sharding is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import speculative_decoding_attention_amd as S
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    R = max(1, args.rotate)
+
+    # ------------------------------------------------------------- inputs --
+    attn, hsr, acc = W.c2_sparrow(0)
+    B, n, Hq, d = attn.q.shape
+    Hkv, L, gamma, top_k = attn.num_kv_heads, attn.max_len, n - 1, attn.top_k
+    D = hsr.e.shape[1]
+    V = acc.logits.shape[2]
+
+    def to_dev(st):
+        if st.dtype == W.BF16:
+            return torch.from_numpy(st.bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(st.bits).to(dev)
+
+    k0, v0 = to_dev(attn.k), to_dev(attn.v)
+    kv_len = torch.tensor(attn.kv_len, dtype=torch.int32, device=dev)
+    kvs = [S.KVCache(k0 if r == 0 else k0.clone(), v0 if r == 0 else v0.clone(), kv_len)
+           for r in range(R)]
+    q = to_dev(attn.q)
+    q_last = q[:, -1:].contiguous()
+    text_idx = torch.tensor(attn.text_idx, dtype=torch.int32, device=dev)
+    text_len = torch.tensor(attn.text_len, dtype=torch.int32, device=dev)
+    e, h = to_dev(hsr.e), to_dev(hsr.h)
+    w0 = to_dev(hsr.w)
+    ws = [w0 if r == 0 else w0.clone() for r in range(R)]
+    lg0 = to_dev(acc.logits)
+    logits = [lg0 if r == 0 else lg0.clone() for r in range(R)]
+    draft = torch.tensor(acc.draft, dtype=torch.int32, device=dev)
+    scale = attn.scale
+
+    # outputs, preallocated so captured graphs allocate nothing
+    o_ver = torch.empty((B, n, Hq, d), dtype=torch.bfloat16, device=dev)
+    l_ver = torch.empty((B, n, Hq), dtype=torch.float32, device=dev)
+    y_hsr = torch.empty((gamma, D), dtype=torch.bfloat16, device=dev)
+    o_vata = torch.empty((gamma, 1, Hq, d), dtype=torch.bfloat16, device=dev)
+    l_vata = torch.empty((gamma, 1, Hq), dtype=torch.float32, device=dev)
+    sel = torch.empty((B, Hkv, top_k), dtype=torch.int32, device=dev)
+    o_topk = torch.empty((B, 1, Hq, d), dtype=torch.bfloat16, device=dev)
+    l_topk = torch.empty((B, 1, Hq), dtype=torch.float32, device=dev)
+    t_tok = torch.empty((B, n), dtype=torch.int32, device=dev)
+    a_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    n_tok = torch.empty((B,), dtype=torch.int32, device=dev)
+    wsp = {k: S.Workspace(dev) for k in ("verify", "vata", "topk", "hsr", "accept")}
+
+    def call_hsr(r, k):
+        S.spec_hsr_fuse(e[k:k + 1], h[k:k + 1], ws[r], y=y_hsr[k:k + 1], workspace=wsp["hsr"])
+
+    def call_vata(r, k):
+        S.spec_vata_attn(kvs[r], y_hsr[k:k + 1].view(1, 1, Hq, d), text_idx, text_len,
+                         scale=scale, out=o_vata[k:k + 1], lse=l_vata[k:k + 1],
+                         workspace=wsp["vata"])
+
+    def call_topk(r):
+        S.spec_topk_attn(kvs[r], q_last, top_k, scale=scale, sel_idx=sel, out=o_topk,
+                         lse=l_topk, workspace=wsp["topk"])
+
+    def call_verify(r):
+        S.spec_verify_attn(kvs[r], q, scale=scale, out=o_ver, lse=l_ver,
+                           workspace=wsp["verify"])
+
+    def call_accept(r):
+        S.spec_accept(logits[r], draft, target_tok=t_tok, accept_len=a_len, next_tok=n_tok,
+                      workspace=wsp["accept"])
+
+    def step(r):
+        for k in range(gamma):
+            call_hsr(r, k)
+            call_vata(r, k)
+        call_topk(r)
+        call_verify(r)
+        call_accept(r)
+
+    # eager warm-up (sizes every workspace before capture)
+    for r in range(R):
+        step(r)
+    torch.cuda.synchronize()
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        return g
+
+    stream = torch.cuda.current_stream(dev)
+
+    def time_graph(g, replays):
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(replays):
+            g.replay()
+        t1.record(stream)
+        t1.synchronize()
+        return t0.elapsed_time(t1) / replays   # ms per replay
+
+    result = {}
+    parts = {}
+    only = args.only
+
+    # ---- per-entry-point graphs: R back-to-back calls over R buffer copies
+    if only in (None, "verify"):
+        g = capture(lambda: [call_verify(r) for r in range(R)])
+        parts["verify_us"] = time_graph(g, args.reps) * 1e3 / R
+    if only in (None, "vata"):
+        g = capture(lambda: [call_vata(r, 0) for r in range(R)])
+        parts["vata_us"] = time_graph(g, args.reps) * 1e3 / R
+    if only in (None, "hsr"):
+        g = capture(lambda: [call_hsr(r, 0) for r in range(R)])
+        parts["hsr_us"] = time_graph(g, args.reps) * 1e3 / R
+    if only in (None, "topk"):
+        g = capture(lambda: [call_topk(r) for r in range(R)])
+        parts["topk_us"] = time_graph(g, args.reps) * 1e3 / R
+    if only in (None, "accept"):
+        g = capture(lambda: [call_accept(r) for r in range(R)])
+        parts["accept_us"] = time_graph(g, args.reps) * 1e3 / R
+    if only in (None, "vata", "hsr"):
+        g = capture(lambda: [(call_hsr(r, 0), call_vata(r, 0)) for r in range(R)])
+        parts["draft_step_us"] = time_graph(g, args.reps) * 1e3 / R
+
+    # ---- the timed region: exactly `steps` whole steps, one graph per copy
+    ms_per_step = None
+    if only in (None, "step"):
+        graphs = [capture(lambda r=r: step(r)) for r in range(R)]
+        for i in range(args.warmup):
+            graphs[i % R].replay()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for i in range(args.steps):
+            graphs[i % R].replay()
+        t1.record(stream)
+        t1.synchronize()
+        ms_per_step = t0.elapsed_time(t1) / args.steps
+
+    # ---- algorithmic bytes (per call)
+    kv_bytes = 2 * L * Hkv * d * 2
+    verify_bytes = kv_bytes + 2 * (n * Hq * d * 2) + n * Hq * 4
+    vata_bytes = 2 * int(attn.text_len[0]) * Hkv * d * 2 + int(attn.text_len[0]) * 4 + \
+        2 * Hq * d * 2 + Hq * 4
+    hsr_bytes = D * 2 * D * 2 + 2 * D * 2 + D * 2
+    hsr_flops = 2 * 1 * D * 2 * D
+    topk_bytes = L * Hkv * d * 2 + 2 * top_k * Hkv * d * 2 + Hq * d * 4 + Hkv * top_k * 4
+    accept_bytes = n * V * 2 + gamma * 4 + (n + 2) * 4
+
+    # ---- parity of the timed outputs (sampled units of the verification)
+    import oracle
+    torch.cuda.synchronize()
+    call_verify(0)
+    torch.cuda.synchronize()
+    ro, rl = oracle.verify_attention(attn.q.values, attn.k.values, attn.v.values, attn.kv_len,
+                                     attn.q_len, Hkv, scale, units=[(0, 0), (0, 3)])
+    o = o_ver.float().cpu().numpy()
+    err = float(max(np.abs(o[0, :, g * 7:(g + 1) * 7] - ro[0, :, g * 7:(g + 1) * 7]).max()
+                    for g in (0, 3)))
+
+    # ---- CPU baseline: the oracle as it stands, on the host cores
+    cpu = None
+    if not args.no_cpu_baseline and only is None:
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
+        except Exception:
+            threads = 1
+        t_start = time.perf_counter()
+        calls = 0
+        while True:
+            oracle.verify_attention(attn.q.values, attn.k.values, attn.v.values, attn.kv_len,
+                                    attn.q_len, Hkv, scale)
+            calls += 1
+            if time.perf_counter() - t_start >= args.cpu_seconds:
+                break
+        secs = (time.perf_counter() - t_start) / calls
+        cpu = {"value": round(verify_bytes / secs / 1e9, 4), "unit": "GB/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"{calls} full verification call(s) of this workload (4 KV heads x 42 "
+                         f"rows x 25,512 keys, fp64 numpy), {secs:.2f} s each"}
+
+    traffic = None
+    src_hash = _source_hash(KERNEL_SOURCES)
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("source_hash") == src_hash:
+            traffic = tr.get("bytes_per_launch")
+
+    verify_us = parts.get("verify_us")
+    value = verify_bytes / (verify_us * 1e-6) / 1e9 if verify_us else None
+    roof = None
+    if verify_us:
+        roof = {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(value / HBM_PEAK_GBS, 4), "traffic": traffic}
+    draft_us = parts.get("draft_step_us")
+    result = {
+        "metric": "verify-attn HBM GB/s (% peak) + draft steps/s at 25k visual tokens, 1 GPU",
+        "value": round(value, 1) if value else None,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4) if ms_per_step else None,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "sparrow-25k-visual-step", "batch": 1, "q_heads": Hq,
+                   "kv_heads": Hkv, "head_dim": d, "kv_len": L, "visual_tokens": 25000,
+                   "text_tokens": int(attn.text_len[0]), "gamma": gamma, "top_k": top_k,
+                   "hidden": D, "vocab": V, "rotate": R},
+        "pct_peak": round(100 * value / HBM_PEAK_GBS, 2) if value else None,
+        "draft_steps_per_s": round(1e6 / draft_us, 1) if draft_us else None,
+        "vata_steps_per_s": round(1e6 / parts["vata_us"], 1) if "vata_us" in parts else None,
+        "per_call_us": {k[:-3]: round(v, 3) for k, v in parts.items()},
+        "per_call_gbs": {k: round(b / (parts[k + "_us"] * 1e-6) / 1e9, 1)
+                         for k, b in (("verify", verify_bytes), ("vata", vata_bytes),
+                                      ("hsr", hsr_bytes), ("topk", topk_bytes),
+                                      ("accept", accept_bytes)) if k + "_us" in parts},
+        "hsr_tflops": round(hsr_flops / (parts["hsr_us"] * 1e-6) / 1e12, 2)
+        if "hsr_us" in parts else None,
+        "verify_max_abs_err_vs_oracle": err,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernel_source_hash": src_hash,
+    }
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -45,6 +45,9 @@ spec_status_t check_common(const spec_kv_t* kv, int32_t batch, const void* q, in
   if (!isfinite(scale)) return SPEC_ERR_SHAPE;
   if ((long long)n_max * (num_q_heads / kv->num_kv_heads) > 64) return SPEC_ERR_UNSUPPORTED;
   if ((long long)batch * kv->num_kv_heads > (1 << 24)) return SPEC_ERR_SHAPE;
+  // contiguous caches address rows with 32-bit indices
+  if (kv->page_size == 0 && (long long)batch * kv->num_kv_heads * kv->max_len >= (1LL << 32))
+    return SPEC_ERR_SHAPE;
   return SPEC_OK;
 }
 
@@ -109,7 +112,8 @@ size_t spec_verify_attn_workspace(const spec_kv_t* kv, int32_t batch, int32_t n_
       num_q_heads % kv->num_kv_heads)
     return 0;
   const int R = n_max * (num_q_heads / kv->num_kv_heads);
-  return plan_attention(batch * kv->num_kv_heads, kv->max_len, R, kv->head_dim).ws_bytes;
+  return plan_attention(batch * kv->num_kv_heads, kv->max_len, R, kv->head_dim,
+                        kv->page_size != 0).ws_bytes;
 }
 
 spec_status_t spec_verify_attn(const spec_kv_t* kv, int32_t batch, const void* q,
@@ -121,7 +125,8 @@ spec_status_t spec_verify_attn(const spec_kv_t* kv, int32_t batch, const void* q
   if (st != SPEC_OK) return st;
   AttnArgs a = make_args(kv, batch, q, n_max, q_len, num_q_heads, scale, out, out_dtype, lse);
   a.mode = 0;
-  const AttnPlan plan = plan_attention(batch * kv->num_kv_heads, kv->max_len, a.R, kv->head_dim);
+  const AttnPlan plan = plan_attention(batch * kv->num_kv_heads, kv->max_len, a.R, kv->head_dim,
+                                       kv->page_size != 0);
   st = check_ws(plan.ws_bytes, ws, ws_bytes);
   if (st != SPEC_OK) return st;
   return launch_attention(a, kv->head_dim, kv->dtype, plan, ws, stream);
@@ -135,7 +140,7 @@ size_t spec_vata_attn_workspace(const spec_kv_t* kv, int32_t batch, int32_t n_ma
       num_q_heads % kv->num_kv_heads)
     return 0;
   const int R = n_max * (num_q_heads / kv->num_kv_heads);
-  return plan_attention(batch * kv->num_kv_heads, t_max, R, kv->head_dim).ws_bytes;
+  return plan_attention(batch * kv->num_kv_heads, t_max, R, kv->head_dim, true).ws_bytes;
 }
 
 spec_status_t spec_vata_attn(const spec_kv_t* kv, int32_t batch, const void* q,
@@ -154,7 +159,7 @@ spec_status_t spec_vata_attn(const spec_kv_t* kv, int32_t batch, const void* q,
   a.slots = text_idx;
   a.slot_len = text_len;
   a.slot_stride = t_max;
-  const AttnPlan plan = plan_attention(batch * kv->num_kv_heads, t_max, a.R, kv->head_dim);
+  const AttnPlan plan = plan_attention(batch * kv->num_kv_heads, t_max, a.R, kv->head_dim, true);
   st = check_ws(plan.ws_bytes, ws, ws_bytes);
   if (st != SPEC_OK) return st;
   return launch_attention(a, kv->head_dim, kv->dtype, plan, ws, stream);

@@ -37,20 +37,48 @@ constexpr int kTK = 32;   // key slots per tile
 constexpr int kNW = 4;    // waves per workgroup
 constexpr int kPV = 20;   // dwords per LDS row of a transposed V tile (16 + 4 pad)
 
-__device__ __forceinline__ int slot_position(const AttnArgs& a, int b, int g, int t) {
-  if (a.mode == 0) return t;
-  if (a.mode == 1) return a.slots[(size_t)b * a.slot_stride + t];
-  return a.slots[((size_t)b * a.Hkv + g) * a.slot_stride + t];
-}
+constexpr int kMaxChunk = 4096;  // slots per split whose (position, row) are staged in LDS
 
-// Row index (in units of head_dim elements) of position `pos` of (b, g).
-__device__ __forceinline__ size_t kv_row(const AttnArgs& a, int b, int g, int pos) {
-  if (a.page_shift >= 0) {
-    const int page = a.page_table[(size_t)b * a.max_pages + (pos >> a.page_shift)];
-    const int slot = pos & ((1 << a.page_shift) - 1);
-    return (((size_t)page * a.Hkv + g) << a.page_shift) + slot;
+// Where the key slots of one split live.  Dense contiguous splits compute
+// position and row arithmetically; every other layout (a text index list, a
+// top-K list, a paged pool) is resolved once per workgroup into LDS before
+// the streaming loop, so the loop's only global loads are K and V rows.
+template <bool GATHER>
+struct SlotMap {
+  int t_beg;
+  uint32_t base_row;      // dense: first row of (b, g)
+  const int* pos;         // gather: LDS positions of slots t_beg..
+  const uint32_t* row;    // gather: LDS row indices of slots t_beg..
+  __device__ __forceinline__ int position(int slot) const {
+    return GATHER ? pos[slot - t_beg] : slot;
   }
-  return ((size_t)b * a.Hkv + g) * (size_t)a.max_len + pos;
+  __device__ __forceinline__ uint32_t rowof(int slot) const {
+    return GATHER ? row[slot - t_beg] : base_row + (uint32_t)slot;
+  }
+};
+
+// Resolves slots [t_beg, t_end) of (b, g) into LDS: logical position from the
+// slot list (or the slot itself), then the physical row through the page
+// table when the cache is paged.  Rows fit 32 bits for any pool that fits in
+// device memory.
+__device__ __forceinline__ void stage_slots(const AttnArgs& a, int b, int g, int t_beg, int t_end,
+                                            int* pos, uint32_t* row) {
+  for (int t = t_beg + (int)threadIdx.x; t < t_end; t += blockDim.x) {
+    int p;
+    if (a.mode == 0) p = t;
+    else if (a.mode == 1) p = a.slots[(size_t)b * a.slot_stride + t];
+    else p = a.slots[((size_t)b * a.Hkv + g) * a.slot_stride + t];
+    uint32_t r;
+    if (a.page_shift >= 0) {
+      const int page = a.page_table[(size_t)b * a.max_pages + (p >> a.page_shift)];
+      r = (((uint32_t)page * (uint32_t)a.Hkv + (uint32_t)g) << a.page_shift) +
+          (uint32_t)(p & ((1 << a.page_shift) - 1));
+    } else {
+      r = ((uint32_t)b * (uint32_t)a.Hkv + (uint32_t)g) * (uint32_t)a.max_len + (uint32_t)p;
+    }
+    pos[t - t_beg] = p;
+    row[t - t_beg] = r;
+  }
 }
 
 // Shared epilogue: merge the 4 waves' (m, l, l_rnd, acc) in LDS in a fixed
@@ -209,9 +237,9 @@ struct Bf16Tile {
   int kpos[2][4];
 };
 
-template <int D>
-__device__ __forceinline__ void bf16_load_k(const AttnArgs& a, int b, int g, int t0, int t_end,
-                                            int lane, Bf16Tile<D>& T) {
+template <int D, bool GATHER>
+__device__ __forceinline__ void bf16_load_k(const AttnArgs& a, const SlotMap<GATHER>& sm, int t0,
+                                            int t_end, int lane, Bf16Tile<D>& T) {
   constexpr int KS = D / 32;
   const int r16 = lane & 15, q4 = lane >> 4;
   const uint16_t* kb_ = reinterpret_cast<const uint16_t*>(a.k);
@@ -219,7 +247,7 @@ __device__ __forceinline__ void bf16_load_k(const AttnArgs& a, int b, int g, int
   for (int kb = 0; kb < 2; ++kb) {
     const int slot = t0 + 8 * (r16 >> 2) + 4 * kb + (r16 & 3);
     if (slot < t_end) {
-      const uint16_t* p = kb_ + kv_row(a, b, g, slot_position(a, b, g, slot)) * D + 8 * q4;
+      const uint16_t* p = kb_ + (size_t)sm.rowof(slot) * D + 8 * q4;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) T.k[kb][ks] = ld16(p + 32 * ks);
     } else {
@@ -229,9 +257,9 @@ __device__ __forceinline__ void bf16_load_k(const AttnArgs& a, int b, int g, int
   }
 }
 
-template <int D>
-__device__ __forceinline__ void bf16_load_v(const AttnArgs& a, int b, int g, int t0, int t_end,
-                                            int lane, Bf16Tile<D>& T) {
+template <int D, bool GATHER>
+__device__ __forceinline__ void bf16_load_v(const AttnArgs& a, const SlotMap<GATHER>& sm, int t0,
+                                            int t_end, int lane, Bf16Tile<D>& T) {
   const int q4 = lane >> 4;
   const uint16_t* vb_ = reinterpret_cast<const uint16_t*>(a.v);
   const int o = lane & 3, c = lane >> 2;
@@ -239,7 +267,7 @@ __device__ __forceinline__ void bf16_load_v(const AttnArgs& a, int b, int g, int
   for (int kk = 0; kk < 8; ++kk) {
     const int slot = t0 + 8 * o + kk;
     if (c < D / 8 && slot < t_end)
-      T.v[kk] = ld16(vb_ + kv_row(a, b, g, slot_position(a, b, g, slot)) * D + 8 * c);
+      T.v[kk] = ld16(vb_ + (size_t)sm.rowof(slot) * D + 8 * c);
     else
       T.v[kk] = u32x4_t{0, 0, 0, 0};
   }
@@ -248,7 +276,7 @@ __device__ __forceinline__ void bf16_load_v(const AttnArgs& a, int b, int g, int
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int slot = t0 + 8 * q4 + 4 * kb + i;
-      T.kpos[kb][i] = (slot < t_end) ? slot_position(a, b, g, slot) : 0x7fffffff;
+      T.kpos[kb][i] = (slot < t_end) ? sm.position(slot) : 0x7fffffff;
     }
 }
 
@@ -256,8 +284,9 @@ __device__ __forceinline__ void bf16_load_v(const AttnArgs& a, int b, int g, int
 // next tile's K loads are issued as soon as this tile's K registers are
 // consumed, and its V loads as soon as this tile's V is in LDS, so one
 // register set keeps a tile of loads in flight behind the softmax and PV.
-template <int D, int NB>
-__device__ __forceinline__ void bf16_tile(const AttnArgs& a, int b, int g, int t_next, int t_end,
+template <int D, int NB, bool GATHER>
+__device__ __forceinline__ void bf16_tile(const AttnArgs& a, const SlotMap<GATHER>& sm, int t_next,
+                                          int t_end,
                                           int lane, Bf16Tile<D>& T,
                                           const bf16x8_t (&qop)[NB][D / 32],
                                           const int (&rowP)[NB], uint32_t* vbuf,
@@ -281,7 +310,7 @@ __device__ __forceinline__ void bf16_tile(const AttnArgs& a, int b, int g, int t
         c4[i] = (T.kpos[kb][i] <= rowP[nb]) ? c4[i] * a.scale_log2 : -INFINITY;
       sc[nb][kb] = c4;
     }
-  if (more) bf16_load_k<D>(a, b, g, t_next, t_end, lane, T);
+  if (more) bf16_load_k<D, GATHER>(a, sm, t_next, t_end, lane, T);
 
   // V tile -> LDS as (key 2p, key 2p+1) bf16 pairs, one LDS row per d.
   const int o = lane & 3, c = lane >> 2;
@@ -299,7 +328,7 @@ __device__ __forceinline__ void bf16_tile(const AttnArgs& a, int b, int g, int t
       *reinterpret_cast<u32x4_t*>(vbuf + (8 * c + 2 * w + 1) * kPV + 4 * o) = hi;
     }
   }
-  if (more) bf16_load_v<D>(a, b, g, t_next, t_end, lane, T);
+  if (more) bf16_load_v<D, GATHER>(a, sm, t_next, t_end, lane, T);
 
   bf16x8_t pop[NB];
 #pragma unroll
@@ -334,12 +363,14 @@ __device__ __forceinline__ void bf16_tile(const AttnArgs& a, int b, int g, int t
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int D, int NB>
+template <int D, int NB, bool GATHER>
 __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
   constexpr int KS = D / 32, DB = D / 16, RP = NB * 16;
   constexpr int V_DW = kNW * D * kPV;
   constexpr int M_DW = RP * (D + 4) + 3 * kNW * RP + 3 * RP;
   __shared__ float smem[(V_DW > M_DW) ? V_DW : M_DW];
+  __shared__ int s_pos[GATHER ? kMaxChunk : 1];
+  __shared__ uint32_t s_row[GATHER ? kMaxChunk : 1];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, q4 = lane >> 4;
@@ -352,12 +383,22 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
   const int t_beg = s * a.chunk;
   const int t_end = min(T, t_beg + a.chunk);
 
+  SlotMap<GATHER> sm;
+  sm.t_beg = t_beg;
+  sm.base_row = ((uint32_t)b * (uint32_t)a.Hkv + (uint32_t)g) * (uint32_t)a.max_len;
+  sm.pos = s_pos;
+  sm.row = s_row;
+  if (GATHER) {
+    stage_slots(a, b, g, t_beg, t_end, s_pos, s_row);
+    __syncthreads();
+  }
+
   const int stride = kNW * kTK;
   int t0 = t_beg + wave * kTK;
   Bf16Tile<D> tile;
   if (t0 < t_end) {
-    bf16_load_k<D>(a, b, g, t0, t_end, lane, tile);
-    bf16_load_v<D>(a, b, g, t0, t_end, lane, tile);
+    bf16_load_k<D, GATHER>(a, sm, t0, t_end, lane, tile);
+    bf16_load_v<D, GATHER>(a, sm, t0, t_end, lane, tile);
   }
 
   bf16x8_t qop[NB][KS];
@@ -388,9 +429,312 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
   uint32_t* vbuf = reinterpret_cast<uint32_t*>(smem) + wave * D * kPV;
 
   for (; t0 < t_end; t0 += stride)
-    bf16_tile<D, NB>(a, b, g, t0 + stride, t_end, lane, tile, qop, rowP, vbuf, m_run, l_run,
-                     l_rnd, acc);
+    bf16_tile<D, NB, GATHER>(a, sm, t0 + stride, t_end, lane, tile, qop, rowP, vbuf, m_run,
+                             l_run, l_rnd, acc);
   finish_split<D, NB>(a, smem, wave, lane, u, s, b, g, nq, m_run, l_run, l_rnd, acc);
+}
+
+// ------------------------------------------------- bf16 d=128 pipeline ----
+// The streaming kernel every bf16 head_dim-128 call runs.  K and V rows go
+// straight from HBM into an LDS ring by DMA (global_load_lds_dwordx4), so
+// data in flight costs no registers and up to NS-1 tiles are outstanding
+// per workgroup.  Each of the 4 waves owns one 16-row query block (NB >= 3)
+// or one 32-key sub-tile of the tile (NB < 3, KP = 4/NB sub-tiles per tile).
+//
+// LDS layout of a 32-key sub-tile (K or V): key row r at r*256 bytes, its
+// 16-byte chunk c at slot c ^ swz(r), swz(r) = 2*(r&7) ^ ((r>>3)&1).  With
+// this swizzle the K operand reads (16 keys, one chunk) and the transposed V
+// reads (ds_read_b64_tr_b16 over 4 keys x 32 bytes per 16-lane group) both
+// hit 16 distinct 16-byte bank groups.
+//
+// Keys inside a sub-tile are in natural order: the S^T = K Q^T output gives
+// lane (q4, i) keys 16*kb + 4*q4 + i, which is exactly the order in which two
+// transposed reads (keys 4*q4.., 16 + 4*q4..) assemble the V^T operand.
+
+__device__ __forceinline__ uint32_t swz(uint32_t r) { return ((r & 7u) << 1) ^ ((r >> 3) & 1u); }
+
+// One 1 KB DMA: each lane copies 16 bytes from its own address g to LDS at
+// lds_byte_addr + 16*lane.  The LDS base goes through M0, which is set in the
+// same statement; no code of this library keeps a value in M0.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_byte_addr) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_byte_addr);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(base) : "memory");
+}
+
+// Waits until at most N of this wave's DMA loads are outstanding, then a
+// workgroup barrier; acts as a compiler memory barrier for LDS accesses.
+template <int N>
+__device__ __forceinline__ void wait_dma_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" :: "n"(N) : "memory");
+}
+
+template <int PER_WAVE>
+__device__ __forceinline__ void wait_tiles_barrier(int later_tiles) {
+  switch (later_tiles) {
+    case 0: wait_dma_barrier<0>(); break;
+    case 1: wait_dma_barrier<PER_WAVE * 1>(); break;
+    case 2: wait_dma_barrier<PER_WAVE * 2>(); break;
+    case 3: wait_dma_barrier<PER_WAVE * 3>(); break;
+    case 4: wait_dma_barrier<PER_WAVE * 4>(); break;
+    case 5: wait_dma_barrier<PER_WAVE * 5>(); break;
+    default: wait_dma_barrier<PER_WAVE * 6>(); break;
+  }
+}
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_t lds_short4_t;
+typedef __attribute__((address_space(3))) unsigned char lds_u8_t;
+
+template <int NB>
+struct PipeCfg {
+  static constexpr int KP = (NB >= 3) ? 1 : 4 / NB;     // 32-key sub-tiles per tile
+  static constexpr int TILE_KEYS = 32 * KP;
+  static constexpr int SUB_BYTES = 32 * 256;             // one sub-tile of K (or V)
+  static constexpr int TILE_BYTES = KP * 2 * SUB_BYTES;
+  static constexpr int RING_BYTES = 128 * 1024;
+  static constexpr int NS = RING_BYTES / TILE_BYTES;     // 8, 4 or 2 stages
+  static constexpr int INSTR = TILE_BYTES / 1024;        // 1 KB DMA instructions per tile
+  static constexpr int PER_WAVE = INSTR / 4;
+  static_assert(NS >= 2 && NS - 2 <= 6, "ring depth");
+  static_assert(PER_WAVE * (NS - 2) <= 63, "vmcnt range");
+};
+
+template <int NB, bool GATHER>
+__device__ __forceinline__ void pipe_issue_tile(const AttnArgs& a, const SlotMap<GATHER>& sm,
+                                                int tile_start, int t_end, uint32_t slot_lds,
+                                                int wave, int lane) {
+  using C = PipeCfg<NB>;
+  const unsigned char* kg = reinterpret_cast<const unsigned char*>(a.k);
+  const unsigned char* vg = reinterpret_cast<const unsigned char*>(a.v);
+#pragma unroll
+  for (int jj = 0; jj < C::PER_WAVE; ++jj) {
+    const int j = wave + 4 * jj;                 // DMA instruction index within the tile
+    const int p = j >> 4, kind = (j >> 3) & 1, grp = j & 7;
+    const int key = 4 * grp + (lane >> 4);       // key row inside the 32-key sub-tile
+    int slot = tile_start + 32 * p + key;
+    slot = slot < t_end ? slot : t_end - 1;      // past the end: any valid row (masked later)
+    const uint32_t chunk = (uint32_t)(lane & 15) ^ swz((uint32_t)key);
+    const unsigned char* src = (kind ? vg : kg) + (size_t)sm.rowof(slot) * 256 + chunk * 16;
+    dma16(src, slot_lds + (uint32_t)((2 * p + kind) * C::SUB_BYTES + grp * 1024));
+  }
+}
+
+// Epilogue of the pipelined kernel: wave (nb, p) holds rows nb*16.. of
+// sub-tile phase p.  Phases are merged in LDS in a fixed order.
+template <int NB>
+__device__ __forceinline__ void pipe_finish(const AttnArgs& a, float* smem, int wave, int lane,
+                                            bool active, int nb, int p, int u, int s, int b,
+                                            int g, int nq, float m_run, float l_run, float l_rnd,
+                                            f32x4_t (&acc)[8]) {
+  constexpr int D = 128, RP = NB * 16, DP = D + 4;
+  constexpr int KP = PipeCfg<NB>::KP;
+  float* macc = smem;                 // [RP][DP]
+  float* mm = macc + RP * DP;         // [KP][RP]
+  float* ml = mm + KP * RP;
+  float* mr = ml + KP * RP;
+  float* mrow = mr + KP * RP;         // [3][RP]
+  const int r16 = lane & 15, q4 = lane >> 4;
+  const float lt = sum_across_rows(l_run), rt = sum_across_rows(l_rnd);
+  __syncthreads();                    // the ring is free from here on
+  if (active && q4 == 0) {
+    mm[p * RP + nb * 16 + r16] = m_run;
+    ml[p * RP + nb * 16 + r16] = lt;
+    mr[p * RP + nb * 16 + r16] = rt;
+  }
+  __syncthreads();
+  if (threadIdx.x < RP) {
+    const int r = threadIdx.x;
+    float M = -INFINITY;
+    for (int k = 0; k < KP; ++k) M = fmaxf(M, mm[k * RP + r]);
+    const float Mu = (M == -INFINITY) ? 0.f : M;
+    float Ls = 0.f, Lr = 0.f;
+    for (int k = 0; k < KP; ++k) {
+      const float f = exp2f(mm[k * RP + r] - Mu);
+      Ls += ml[k * RP + r] * f;
+      Lr += mr[k * RP + r] * f;
+    }
+    mrow[r] = M;
+    mrow[RP + r] = Ls;
+    mrow[2 * RP + r] = Lr;
+  }
+  __syncthreads();
+  float f = 0.f;
+  if (active) {
+    const float M = mrow[nb * 16 + r16];
+    f = exp2f(m_run - ((M == -INFINITY) ? 0.f : M));
+  }
+  for (int k = 0; k < KP; ++k) {
+    if (active && p == k) {
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int idx = (nb * 16 + r16) * DP + db * 16 + q4 * 4 + i;
+          const float val = acc[db][i] * f;
+          macc[idx] = (k == 0) ? val : macc[idx] + val;
+        }
+    }
+    __syncthreads();
+  }
+  const int R = a.R;
+  if (a.S == 1) {
+    const int Hq = a.Hq, G = a.G;
+    for (int e = threadIdx.x; e < R * D; e += blockDim.x) {
+      const int r = e / D, d = e - r * D;
+      const int i = r / G, hh = r - i * G;
+      const float Ls = mrow[RP + r], Lr = mrow[2 * RP + r];
+      const bool live = (i < nq) && (Ls > 0.f);
+      const float o = live ? macc[r * DP + d] / Lr : 0.f;
+      const size_t oi = (((size_t)b * a.n_max + i) * Hq + g * G + hh) * D + d;
+      if (a.out_bf16)
+        reinterpret_cast<uint16_t*>(a.out)[oi] = (uint16_t)f32_to_bf16_bits(o);
+      else
+        reinterpret_cast<float*>(a.out)[oi] = o;
+      if (a.lse && d == 0)
+        a.lse[((size_t)b * a.n_max + i) * Hq + g * G + hh] =
+            live ? (mrow[r] + log2f(Ls)) * 0.69314718055994531f : -INFINITY;
+    }
+  } else {
+    const size_t base = (size_t)u * a.S + s;
+    float* pa = a.part_acc + base * R * D;
+    for (int e = threadIdx.x; e < R * D; e += blockDim.x) {
+      const int r = e / D, d = e - r * D;
+      pa[e] = macc[r * DP + d];
+    }
+    float* pm = a.part_ml + base * 3 * R;
+    for (int r = threadIdx.x; r < R; r += blockDim.x) {
+      pm[r] = mrow[r];
+      pm[R + r] = mrow[RP + r];
+      pm[2 * R + r] = mrow[2 * RP + r];
+    }
+  }
+}
+
+template <int NB, bool GATHER>
+__global__ __launch_bounds__(256, 1) void attn_bf16_pipe_kernel(AttnArgs a) {
+  using C = PipeCfg<NB>;
+  constexpr int D = 128;
+  __shared__ __align__(16) unsigned char ring[C::RING_BYTES];
+  __shared__ int s_pos[GATHER ? kMaxChunk : 1];
+  __shared__ uint32_t s_row[GATHER ? kMaxChunk : 1];
+  static_assert((NB * 16) * (D + 4) * 4 + 7 * C::KP * NB * 16 * 4 <= C::RING_BYTES, "merge fits");
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, q4 = lane >> 4;
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int u = wg / a.S, s = wg - u * a.S;
+  const int b = u / a.Hkv, g = u - b * a.Hkv;
+  const int L = a.kv_len[b];
+  const int nq = a.q_len ? a.q_len[b] : a.n_max;
+  const int T = (a.mode == 0) ? L : (a.mode == 1 ? a.slot_len[b] : min(a.slot_stride, L));
+  const int t_beg = s * a.chunk;
+  const int t_end = min(T, t_beg + a.chunk);
+  const int n_tiles = t_end > t_beg ? (t_end - t_beg + C::TILE_KEYS - 1) / C::TILE_KEYS : 0;
+
+  SlotMap<GATHER> sm;
+  sm.t_beg = t_beg;
+  sm.base_row = ((uint32_t)b * (uint32_t)a.Hkv + (uint32_t)g) * (uint32_t)a.max_len;
+  sm.pos = s_pos;
+  sm.row = s_row;
+  if (GATHER) {
+    stage_slots(a, b, g, t_beg, t_end, s_pos, s_row);
+    __syncthreads();
+  }
+
+  // this wave's rows and sub-tile phase
+  const int nb = (NB >= 3) ? wave : wave % NB;
+  const int p = (NB >= 3) ? 0 : wave / NB;
+  const bool active = nb < NB && p < C::KP;
+  const int n = nb * 16 + r16;
+  const bool valid = active && n < nq * a.G;
+  const int qi = n / a.G, hh = n - qi * a.G;
+  const int rowP = valid ? L - nq + qi : 0x7fffffff;
+  bf16x8_t qop[4];
+  {
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
+                         (((size_t)b * a.n_max + qi) * a.Hq + g * a.G + hh) * D + 8 * q4;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      qop[ks] = valid ? as_bf16x8(ld16(qp + 32 * ks)) : as_bf16x8(u32x4_t{0, 0, 0, 0});
+  }
+  // Q must be in registers before the DMA stream starts (the compiler does
+  // not count the DMA loads, so its own waits would over-wait later).
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  lds_u8_t* const ring_l = (lds_u8_t*)ring;        // the ring as an LDS-address-space pointer
+  const uint32_t ring_lds = (uint32_t)(size_t)ring_l;
+  for (int j = 0; j < C::NS - 1 && j < n_tiles; ++j)
+    pipe_issue_tile<NB, GATHER>(a, sm, t_beg + j * C::TILE_KEYS, t_end,
+                                ring_lds + (uint32_t)(j * C::TILE_BYTES), wave, lane);
+
+  float m_run = -INFINITY, l_run = 0.f, l_rnd = 0.f;
+  f32x4_t acc[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) acc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int later = min(C::NS - 2, n_tiles - 1 - t);
+    wait_tiles_barrier<C::PER_WAVE>(later);
+    if (t + C::NS - 1 < n_tiles)
+      pipe_issue_tile<NB, GATHER>(a, sm, t_beg + (t + C::NS - 1) * C::TILE_KEYS, t_end,
+                                  ring_lds + (uint32_t)(((t + C::NS - 1) % C::NS) * C::TILE_BYTES),
+                                  wave, lane);
+    if (!active) continue;
+    const uint32_t kofs = (uint32_t)((t % C::NS) * C::TILE_BYTES + (2 * p) * C::SUB_BYTES);
+    const uint32_t vofs = kofs + C::SUB_BYTES;
+    const int sub0 = t_beg + t * C::TILE_KEYS + 32 * p;
+
+    // S^T = K Q^T for keys 16*kb + m of the sub-tile
+    f32x4_t sc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const uint32_t row = 16 * kb + r16;
+      f32x4_t c4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const uint32_t chunk = (uint32_t)(4 * ks + q4) ^ swz(row);
+        const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(ring + kofs + row * 256 + chunk * 16);
+        c4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv), qop[ks], c4, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int slot = sub0 + 16 * kb + 4 * q4 + i;
+        const bool vis = slot < t_end && sm.position(min(slot, t_end - 1)) <= rowP;
+        c4[i] = vis ? c4[i] * a.scale_log2 : -INFINITY;
+      }
+      sc[kb] = c4;
+    }
+    float pr[8];
+    softmax_update<8, true>(sc, m_run, l_run, l_rnd, acc, pr);
+    u32x4_t pk;
+    pk[0] = pack_bf16x2(pr[0], pr[1]);
+    pk[1] = pack_bf16x2(pr[2], pr[3]);
+    pk[2] = pack_bf16x2(pr[4], pr[5]);
+    pk[3] = pack_bf16x2(pr[6], pr[7]);
+    const bf16x8_t pop = as_bf16x8(pk);
+
+    // O^T += V^T P^T: the V^T operand of lane (i, q4) is V[keys 4q4.. and
+    // 16+4q4..][d = 16*db + i], read transposed from LDS
+    const int sl = lane & 15;
+    const uint32_t r0 = (uint32_t)(4 * q4 + (sl >> 2)), r1 = r0 + 16;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const uint32_t chunk = (uint32_t)(2 * db + ((sl & 3) >> 1));
+      const uint32_t o0 = vofs + r0 * 256 + ((chunk ^ swz(r0)) * 16) + 8 * (sl & 1);
+      const uint32_t o1 = vofs + r1 * 256 + ((chunk ^ swz(r1)) * 16) + 8 * (sl & 1);
+      const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(ring_l + o0));
+      const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(ring_l + o1));
+      u32x4_t va;
+      va[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+      va[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+      va[2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+      va[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), pop, acc[db], 0, 0, 0);
+    }
+  }
+  pipe_finish<NB>(a, reinterpret_cast<float*>(ring), wave, lane, active, nb, p, u, s, b, g, nq,
+                  m_run, l_run, l_rnd, acc);
 }
 
 // ---------------------------------------------------------------- fp32 ----
@@ -402,11 +746,13 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
 // 16*(s/4) + 4*q4 + s%4 in lane row q4: exactly the probability that lane
 // already holds, and V rows read straight from global memory.
 
-template <int D, int NB>
+template <int D, int NB, bool GATHER>
 __global__ __launch_bounds__(256, 1) void attn_f32_kernel(AttnArgs a) {
   constexpr int DB = D / 16, Q4 = D / 4, RP = NB * 16;
   constexpr int M_DW = RP * (D + 4) + 3 * kNW * RP + 3 * RP;
   __shared__ float smem[M_DW];
+  __shared__ int s_pos[GATHER ? kMaxChunk : 1];
+  __shared__ uint32_t s_row[GATHER ? kMaxChunk : 1];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, q4 = lane >> 4;
@@ -421,6 +767,15 @@ __global__ __launch_bounds__(256, 1) void attn_f32_kernel(AttnArgs a) {
   const float* qf = reinterpret_cast<const float*>(a.q);
   const float* kf = reinterpret_cast<const float*>(a.k);
   const float* vf = reinterpret_cast<const float*>(a.v);
+  SlotMap<GATHER> sm;
+  sm.t_beg = t_beg;
+  sm.base_row = ((uint32_t)b * (uint32_t)a.Hkv + (uint32_t)g) * (uint32_t)a.max_len;
+  sm.pos = s_pos;
+  sm.row = s_row;
+  if (GATHER) {
+    stage_slots(a, b, g, t_beg, t_end, s_pos, s_row);
+    __syncthreads();
+  }
 
   float qop[NB][Q4];
   int rowP[NB];
@@ -452,7 +807,7 @@ __global__ __launch_bounds__(256, 1) void attn_f32_kernel(AttnArgs a) {
     for (int kb = 0; kb < 2; ++kb) {
       const int slot = t0 + 16 * kb + r16;
       if (slot < t_end) {
-        const float* p = kf + kv_row(a, b, g, slot_position(a, b, g, slot)) * D + q4 * Q4;
+        const float* p = kf + (size_t)sm.rowof(slot) * D + q4 * Q4;
 #pragma unroll
         for (int j = 0; j < Q4; ++j) kr[kb][j] = p[j];
       } else {
@@ -466,7 +821,7 @@ __global__ __launch_bounds__(256, 1) void attn_f32_kernel(AttnArgs a) {
     for (int st = 0; st < 8; ++st) {
       const int slot = t0 + 16 * (st >> 2) + 4 * q4 + (st & 3);
       if (slot < t_end) {
-        const float* p = vf + kv_row(a, b, g, slot_position(a, b, g, slot)) * D + r16;
+        const float* p = vf + (size_t)sm.rowof(slot) * D + r16;
 #pragma unroll
         for (int db = 0; db < DB; ++db) vr[st][db] = p[16 * db];
       } else {
@@ -480,7 +835,7 @@ __global__ __launch_bounds__(256, 1) void attn_f32_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int slot = t0 + 16 * kb + 4 * q4 + i;
-        kpos[kb][i] = (slot < t_end) ? slot_position(a, b, g, slot) : 0x7fffffff;
+        kpos[kb][i] = (slot < t_end) ? sm.position(slot) : 0x7fffffff;
       }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -515,27 +870,63 @@ __global__ __launch_bounds__(256, 1) void attn_f32_kernel(AttnArgs a) {
 
 // --------------------------------------------------------------- merge ----
 // One workgroup per (unit, row): combine the S partials with the log-sum-exp
-// rule in a fixed split order.
+// rule.  The split weights are computed once into LDS; then 256/D groups of
+// D threads each sum a strided subset of the splits (many loads in flight),
+// and the groups are added in a fixed order.
+constexpr int kMaxSplits = 4096;
+
 template <int D>
-__global__ __launch_bounds__(D) void attn_merge_kernel(AttnArgs a) {
-  const int R = a.R;
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
+  constexpr int NG = 256 / D;
+  __shared__ float w_s[kMaxSplits];
+  __shared__ float red[3][256 / 64];
+  __shared__ float part[NG][D];
+  const int R = a.R, S = a.S;
   const int u = blockIdx.x / R, r = blockIdx.x - (blockIdx.x / R) * R;
   const int b = u / a.Hkv, g = u - b * a.Hkv;
   const int nq = a.q_len ? a.q_len[b] : a.n_max;
   const int i = r / a.G, hh = r - i * a.G;
-  const int d = threadIdx.x;
-  const float* pm = a.part_ml + (size_t)u * a.S * 3 * R;
-  float M = -INFINITY;
-  for (int s = 0; s < a.S; ++s) M = fmaxf(M, pm[s * 3 * R + r]);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* pm = a.part_ml + (size_t)u * S * 3 * R;
+
+  float mx = -INFINITY;
+  for (int s = tid; s < S; s += 256) mx = fmaxf(mx, pm[s * 3 * R + r]);
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if (lane == 0) red[0][wave] = mx;
+  __syncthreads();
+  float M = red[0][0];
+  for (int w = 1; w < 4; ++w) M = fmaxf(M, red[0][w]);
   const float Mu = (M == -INFINITY) ? 0.f : M;
-  float Ls = 0.f, Lr = 0.f, o = 0.f;
-  const float* pa = a.part_acc + (size_t)u * a.S * R * D + (size_t)r * D + d;
-  for (int s = 0; s < a.S; ++s) {
+  float ls = 0.f, lr = 0.f;
+  for (int s = tid; s < S; s += 256) {
     const float w = exp2f(pm[s * 3 * R + r] - Mu);
-    Ls += pm[s * 3 * R + R + r] * w;
-    Lr += pm[s * 3 * R + 2 * R + r] * w;
-    o += pa[(size_t)s * R * D] * w;
+    w_s[s] = w;
+    ls += pm[s * 3 * R + R + r] * w;
+    lr += pm[s * 3 * R + 2 * R + r] * w;
   }
+  for (int o = 32; o > 0; o >>= 1) {
+    ls += __shfl_xor(ls, o);
+    lr += __shfl_xor(lr, o);
+  }
+  __syncthreads();
+  if (lane == 0) {
+    red[1][wave] = ls;
+    red[2][wave] = lr;
+  }
+  __syncthreads();
+  const float Ls = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+  const float Lr = red[2][0] + red[2][1] + red[2][2] + red[2][3];
+
+  const int d = tid % D, grp = tid / D;
+  const float* pa = a.part_acc + (size_t)u * S * R * D + (size_t)r * D + d;
+  float o = 0.f;
+#pragma unroll 8
+  for (int s = grp; s < S; s += NG) o += pa[(size_t)s * R * D] * w_s[s];
+  part[grp][d] = o;
+  __syncthreads();
+  if (grp != 0) return;
+  o = part[0][d];
+  for (int k = 1; k < NG; ++k) o += part[k][d];
   const bool live = (i < nq) && (Ls > 0.f);
   o = live ? o / Lr : 0.f;
   const size_t oi = (((size_t)b * a.n_max + i) * a.Hq + g * a.G + hh) * D + d;
@@ -548,23 +939,25 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(AttnArgs a) {
         live ? (M + log2f(Ls)) * 0.69314718055994531f : -INFINITY;
 }
 
-template <int D, int NB>
+template <int D, int NB, bool GATHER>
 hipError_t launch_d_nb(const AttnArgs& a, int dtype, int grid, hipStream_t st) {
-  if (dtype == SPEC_BF16)
-    hipLaunchKernelGGL((attn_bf16_kernel<D, NB>), dim3(grid), dim3(256), 0, st, a);
+  if (dtype == SPEC_BF16 && D == 128)
+    hipLaunchKernelGGL((attn_bf16_pipe_kernel<NB, GATHER>), dim3(grid), dim3(256), 0, st, a);
+  else if (dtype == SPEC_BF16)
+    hipLaunchKernelGGL((attn_bf16_kernel<D, NB, GATHER>), dim3(grid), dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_f32_kernel<D, NB>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_f32_kernel<D, NB, GATHER>), dim3(grid), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool GATHER>
 hipError_t launch_d(const AttnArgs& a, int dtype, int grid, hipStream_t st) {
   const int nb = (a.R + 15) / 16;
   switch (nb) {
-    case 1: return launch_d_nb<D, 1>(a, dtype, grid, st);
-    case 2: return launch_d_nb<D, 2>(a, dtype, grid, st);
-    case 3: return launch_d_nb<D, 3>(a, dtype, grid, st);
-    default: return launch_d_nb<D, 4>(a, dtype, grid, st);
+    case 1: return launch_d_nb<D, 1, GATHER>(a, dtype, grid, st);
+    case 2: return launch_d_nb<D, 2, GATHER>(a, dtype, grid, st);
+    case 3: return launch_d_nb<D, 3, GATHER>(a, dtype, grid, st);
+    default: return launch_d_nb<D, 4, GATHER>(a, dtype, grid, st);
   }
 }
 
@@ -600,18 +993,22 @@ int device_cu_count() {
   return cached[dev];
 }
 
-AttnPlan plan_attention(int units, int t_max, int rows, int d) {
+AttnPlan plan_attention(int units, int t_max, int rows, int d, bool gather) {
   AttnPlan p;
   const int target = device_cu_count();            // about one workgroup per CU
-  const long total = (long)units * (long)(t_max > 0 ? t_max : 1);
+  const long T = t_max > 0 ? t_max : 1;
+  const long total = (long)units * T;
   long chunk = (total + target - 1) / target;
+  if (chunk < (T + kMaxSplits - 1) / kMaxSplits) chunk = (T + kMaxSplits - 1) / kMaxSplits;
   chunk = ((chunk + kTK - 1) / kTK) * kTK;
   if (chunk < kTK * kNW) chunk = kTK * kNW;        // every wave gets a tile
-  int S = (int)(((long)(t_max > 0 ? t_max : 1) + chunk - 1) / chunk);
+  if (gather && chunk > kMaxChunk) chunk = kMaxChunk;
+  int S = (int)((T + chunk - 1) / chunk);
   if (S < 1) S = 1;
   p.S = S;
   p.chunk = (int)chunk;
   p.grid = units * S;
+  p.gather = gather;
   if (S > 1) {
     const size_t acc_bytes = (size_t)units * S * rows * d * sizeof(float);
     p.off_ml = align_up(acc_bytes, 256);
@@ -632,15 +1029,20 @@ spec_status_t launch_attention(AttnArgs a, int d, int dtype, const AttnPlan& pla
     a.part_ml = nullptr;
   }
   if (plan.grid == 0) return SPEC_OK;
-  hipError_t e = (d == 64) ? launch_d<64>(a, dtype, plan.grid, stream)
-                           : launch_d<128>(a, dtype, plan.grid, stream);
+  hipError_t e;
+  if (plan.gather)
+    e = (d == 64) ? launch_d<64, true>(a, dtype, plan.grid, stream)
+                  : launch_d<128, true>(a, dtype, plan.grid, stream);
+  else
+    e = (d == 64) ? launch_d<64, false>(a, dtype, plan.grid, stream)
+                  : launch_d<128, false>(a, dtype, plan.grid, stream);
   if (e != hipSuccess) return SPEC_ERR_HIP;
   if (plan.S > 1) {
     const int blocks = a.B * a.Hkv * a.R;
     if (d == 64)
-      hipLaunchKernelGGL(attn_merge_kernel<64>, dim3(blocks), dim3(64), 0, stream, a);
+      hipLaunchKernelGGL(attn_merge_kernel<64>, dim3(blocks), dim3(256), 0, stream, a);
     else
-      hipLaunchKernelGGL(attn_merge_kernel<128>, dim3(blocks), dim3(128), 0, stream, a);
+      hipLaunchKernelGGL(attn_merge_kernel<128>, dim3(blocks), dim3(256), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
   }
   return SPEC_OK;

@@ -43,6 +43,7 @@ struct AttnPlan {
   int S = 1;
   int chunk = 0;
   int grid = 0;
+  bool gather = false;        // slots resolved through a list or a page table
   size_t ws_bytes = 0;
   size_t off_ml = 0;
 };
@@ -50,7 +51,8 @@ struct AttnPlan {
 int device_cu_count();
 
 // Split plan for U units of at most t_max slots and R rows of width d.
-AttnPlan plan_attention(int units, int t_max, int rows, int d);
+// `gather`: slot positions come from a list, or rows from a page table.
+AttnPlan plan_attention(int units, int t_max, int rows, int d, bool gather);
 
 spec_status_t launch_attention(AttnArgs a, int d, int dtype, const AttnPlan& plan, void* ws,
                                hipStream_t stream);

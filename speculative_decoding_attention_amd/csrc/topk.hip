@@ -344,7 +344,7 @@ TopkPlan plan_topk(int units, int max_len, int top_k, int rows, int d) {
   p.off_scores = 0;
   p.off_hist = align_up((size_t)units * max_len * sizeof(double), 256);
   p.off_attn = align_up(p.off_hist + (size_t)units * kHistBins * sizeof(uint32_t), 256);
-  p.attn = plan_attention(units, top_k, rows, d);
+  p.attn = plan_attention(units, top_k, rows, d, true);
   p.ws_bytes = p.off_attn + p.attn.ws_bytes;
   return p;
 }

@@ -154,7 +154,9 @@ def test_first_verify_row_equals_decode_on_device():
     od, ld = S.spec_verify_attn(kvd, dev(c.q)[:, :1].contiguous(), scale=c.scale,
                                 out_dtype=torch.float32)
     torch.cuda.synchronize()
-    assert (o[:, 0] - od[:, 0]).abs().max().item() < 2e-3 * o.abs().max().item()
+    # the two calls tile the keys differently, so bf16 probability rounding
+    # differs: same scale-aware bound as the oracle parity checks
+    assert (o[:, 0] - od[:, 0]).abs().max().item() < 1e-2 * o.abs().max().item()
     assert (l[:, 0] - ld[:, 0]).abs().max().item() < 1e-4
 
 

@@ -55,9 +55,15 @@ def test_hsr_identity_halves():
         assert np.array_equal(y, W.Stored.from_f32(want, W.BF16).values)
 
 
-def test_c2_hsr_single_row():
+def test_c2_hsr_draft_rows():
+    """The 25k-token step's HSR inputs, one row per draft step (M = 1) and all
+    five rows at once."""
     _, hsr, _ = W.c2_sparrow(0)
     _hsr_check(hsr, _hsr(hsr, torch.float32))
+    for k in range(hsr.e.shape[0]):
+        one = W.HsrCase("row", W.Stored(W.BF16, hsr.e.bits[k:k + 1].copy()),
+                        W.Stored(W.BF16, hsr.h.bits[k:k + 1].copy()), hsr.w)
+        _hsr_check(one, _hsr(one, torch.bfloat16))
 
 
 @pytest.fixture(scope="module")

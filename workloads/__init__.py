@@ -200,9 +200,10 @@ def c2_text_layout(Lvis: int = 25000, Ltxt: int = 512, n_interleaved: int = 64) 
 
 def c2_sparrow(seed: int = 0, Lvis: int = 25000, with_hsr: bool = True):
     """Sparrow-scale step, bf16: B=1, 28/4 heads, d=128, Lvis visual + 512
-    text positions (64 interleaved + 448 trailing), gamma=5.  Also returns a
-    one-row HSR input (hidden 3584) and bf16 acceptance logits (vocab 152064)
-    so that one speculative iteration can run on it end to end."""
+    text positions (64 interleaved + 448 trailing), gamma=5.  Also returns
+    HSR inputs (one row of hidden size 3584 per draft step) and bf16
+    acceptance logits (vocab 152064) so that one speculative iteration can
+    run on it end to end."""
     rng = np.random.default_rng(seed)
     B, Hq, Hkv, d, Ltxt, gamma = 1, 28, 4, 128, 512, 5
     L = Lvis + Ltxt
@@ -220,10 +221,10 @@ def c2_sparrow(seed: int = 0, Lvis: int = 25000, with_hsr: bool = True):
     if not with_hsr:
         return attn, None, None
     D, V = Hq * d, 152064
-    e = _normal(rng, (1, D), 0.02)
-    h = _normal(rng, (1, D), 0.02)
+    e = _normal(rng, (gamma, D), 0.02)      # one (e_t, h_{t-1}) row per draft step
+    h = _normal(rng, (gamma, D), 0.02)
     w = _normal(rng, (D, 2 * D), 0.02)
-    hsr = HsrCase("c2_hsr_m1", Stored.from_f32(e, BF16), Stored.from_f32(h, BF16),
+    hsr = HsrCase("c2_hsr", Stored.from_f32(e, BF16), Stored.from_f32(h, BF16),
                   Stored.from_f32(w, BF16))
     logits = _normal(rng, (B, n, V))
     draft = rng.integers(0, V, size=(B, gamma)).astype(np.int32)
