@@ -488,14 +488,19 @@ typedef __attribute__((address_space(3))) unsigned char lds_u8_t;
 
 template <int NB>
 struct PipeCfg {
-  static constexpr int KP = (NB >= 3) ? 1 : 4 / NB;     // 32-key sub-tiles per tile
+  // NB >= 3: 8 waves in two teams; each team's waves own one 16-row block and
+  // the teams take alternate 32-key sub-tiles, so every SIMD runs two waves.
+  // NB <= 2: 4 waves, the spare waves take further sub-tiles.
+  static constexpr int WAVES = (NB >= 3) ? 8 : 4;
+  static constexpr int SLOTS = (NB >= 3) ? 4 : NB;        // row-block slots per team
+  static constexpr int KP = WAVES / SLOTS;                 // 32-key sub-tiles per tile
   static constexpr int TILE_KEYS = 32 * KP;
-  static constexpr int SUB_BYTES = 32 * 256;             // one sub-tile of K (or V)
+  static constexpr int SUB_BYTES = 32 * 256;               // one sub-tile of K (or V)
   static constexpr int TILE_BYTES = KP * 2 * SUB_BYTES;
   static constexpr int RING_BYTES = 128 * 1024;
-  static constexpr int NS = RING_BYTES / TILE_BYTES;     // 8, 4 or 2 stages
-  static constexpr int INSTR = TILE_BYTES / 1024;        // 1 KB DMA instructions per tile
-  static constexpr int PER_WAVE = INSTR / 4;
+  static constexpr int NS = RING_BYTES / TILE_BYTES;       // 4 or 2 stages
+  static constexpr int INSTR = TILE_BYTES / 1024;          // 1 KB DMA instructions per tile
+  static constexpr int PER_WAVE = INSTR / WAVES;
   static_assert(NS >= 2 && NS - 2 <= 6, "ring depth");
   static_assert(PER_WAVE * (NS - 2) <= 63, "vmcnt range");
 };
@@ -509,7 +514,7 @@ __device__ __forceinline__ void pipe_issue_tile(const AttnArgs& a, const SlotMap
   const unsigned char* vg = reinterpret_cast<const unsigned char*>(a.v);
 #pragma unroll
   for (int jj = 0; jj < C::PER_WAVE; ++jj) {
-    const int j = wave + 4 * jj;                 // DMA instruction index within the tile
+    const int j = wave + C::WAVES * jj;          // DMA instruction index within the tile
     const int p = j >> 4, kind = (j >> 3) & 1, grp = j & 7;
     const int key = 4 * grp + (lane >> 4);       // key row inside the 32-key sub-tile
     int slot = tile_start + 32 * p + key;
@@ -612,7 +617,7 @@ __device__ __forceinline__ void pipe_finish(const AttnArgs& a, float* smem, int 
 }
 
 template <int NB, bool GATHER>
-__global__ __launch_bounds__(256, 1) void attn_bf16_pipe_kernel(AttnArgs a) {
+__global__ __launch_bounds__(PipeCfg<NB>::WAVES * 64, 1) void attn_bf16_pipe_kernel(AttnArgs a) {
   using C = PipeCfg<NB>;
   constexpr int D = 128;
   __shared__ __align__(16) unsigned char ring[C::RING_BYTES];
@@ -643,9 +648,9 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_pipe_kernel(AttnArgs a) {
   }
 
   // this wave's rows and sub-tile phase
-  const int nb = (NB >= 3) ? wave : wave % NB;
-  const int p = (NB >= 3) ? 0 : wave / NB;
-  const bool active = nb < NB && p < C::KP;
+  const int nb = wave % C::SLOTS;
+  const int p = wave / C::SLOTS;
+  const bool active = nb < NB;
   const int n = nb * 16 + r16;
   const bool valid = active && n < nq * a.G;
   const int qi = n / a.G, hh = n - qi * a.G;
@@ -685,7 +690,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_pipe_kernel(AttnArgs a) {
     const uint32_t vofs = kofs + C::SUB_BYTES;
     const int sub0 = t_beg + t * C::TILE_KEYS + 32 * p;
 
-    // S^T = K Q^T for keys 16*kb + m of the sub-tile
+    // S^T = K Q^T for keys 16*kb + m of the sub-tile (unscaled scores)
     f32x4_t sc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -697,21 +702,60 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_pipe_kernel(AttnArgs a) {
         const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(ring + kofs + row * 256 + chunk * 16);
         c4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv), qop[ks], c4, 0, 0, 0);
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int slot = sub0 + 16 * kb + 4 * q4 + i;
-        const bool vis = slot < t_end && sm.position(min(slot, t_end - 1)) <= rowP;
-        c4[i] = vis ? c4[i] * a.scale_log2 : -INFINITY;
-      }
       sc[kb] = c4;
     }
+    // causal / list / tail mask; a dense tile that lies entirely before the
+    // first query row's position and before the split end needs none
+    const bool full = !GATHER && sub0 + 32 <= t_end && sub0 + 31 <= L - nq;
+    if (!full) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int slot = sub0 + 16 * kb + 4 * q4 + i;
+          const bool vis = slot < t_end && sm.position(min(slot, t_end - 1)) <= rowP;
+          sc[kb][i] = vis ? sc[kb][i] : -INFINITY;
+        }
+    }
+    // Online softmax with a lazily moved reference max: the reference m_run
+    // (log2 units) is only raised when some score exceeds it by more than
+    // 2^8, so probabilities stay <= 256 and, in most tiles, no cross-lane
+    // reduction and no rescale of acc are needed.  Exact: every term uses the
+    // same reference as the running sums it joins.
+    float lmax = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                       fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    lmax *= a.scale_log2;
+    if (__builtin_amdgcn_ballot_w64(lmax > m_run + 8.0f)) {
+      const float m_new = fmaxf(m_run, max_across_rows(lmax));
+      const float alpha = exp2f(m_run - ((m_new == -INFINITY) ? 0.f : m_new));
+      m_run = m_new;
+      l_run *= alpha;
+      l_rnd *= alpha;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) acc[db] *= alpha;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     float pr[8];
-    softmax_update<8, true>(sc, m_run, l_run, l_rnd, acc, pr);
+    float ls = 0.f, lr = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i], a.scale_log2, -m_use));
+        ls += e;
+        pr[kb * 4 + i] = e;
+      }
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
     u32x4_t pk;
-    pk[0] = pack_bf16x2(pr[0], pr[1]);
-    pk[1] = pack_bf16x2(pr[2], pr[3]);
-    pk[2] = pack_bf16x2(pr[4], pr[5]);
-    pk[3] = pack_bf16x2(pr[6], pr[7]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x2_t h2 = {(__bf16)pr[2 * j], (__bf16)pr[2 * j + 1]};
+      const uint32_t w = __builtin_bit_cast(uint32_t, h2);
+      pk[j] = w;
+      lr += __uint_as_float(w << 16) + __uint_as_float(w & 0xFFFF0000u);
+    }
+    l_run += ls;
+    l_rnd += lr;
     const bf16x8_t pop = as_bf16x8(pk);
 
     // O^T += V^T P^T: the V^T operand of lane (i, q4) is V[keys 4q4.. and
@@ -942,7 +986,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
 template <int D, int NB, bool GATHER>
 hipError_t launch_d_nb(const AttnArgs& a, int dtype, int grid, hipStream_t st) {
   if (dtype == SPEC_BF16 && D == 128)
-    hipLaunchKernelGGL((attn_bf16_pipe_kernel<NB, GATHER>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_bf16_pipe_kernel<NB, GATHER>), dim3(grid),
+                       dim3(PipeCfg<NB>::WAVES * 64), 0, st, a);
   else if (dtype == SPEC_BF16)
     hipLaunchKernelGGL((attn_bf16_kernel<D, NB, GATHER>), dim3(grid), dim3(256), 0, st, a);
   else
