@@ -11,6 +11,8 @@
 // straight from HBM into registers (W is read exactly once per M band and
 // is the dominant byte stream), one block ahead of the MFMAs
 // (v_mfma_f32_16x16x32_bf16; A = X rows, B = W rows, both K-contiguous).
+#include <string.h>
+
 #include "common.h"
 #include "internal.h"
 
@@ -196,6 +198,99 @@ __global__ __launch_bounds__(256) void hsr_gemm_kernel(HsrArgs a) {
   if (tid == 0) a.tick[tile] = 0u;
 }
 
+
+// Small-M path (M <= 8 rows, the per-draft-step case): the FC is a stream of
+// W (2*D*D bf16) through HBM.  Each wave owns RW consecutive output columns
+// (W rows) and walks them in 16-byte chunks with U chunks per row in flight,
+// so a lane keeps U*RW independent loads outstanding; X (M rows of [e;h]) is
+// staged once per workgroup in LDS.  Products of bf16 values are exact in
+// fp32; each lane accumulates its chunks and the wave reduces by shuffles.
+template <int MM, int RW, int U>
+__global__ __launch_bounds__(256) void hsr_gemv_kernel(HsrArgs a) {
+  extern __shared__ __align__(16) unsigned char xs[];   // [MM][Kd] bf16
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int Kd = 2 * a.D, chunks = Kd / 8;
+  for (int e = tid; e < MM * chunks; e += blockDim.x) {
+    const int m = e / chunks, c = e - (e / chunks) * chunks;
+    u32x4_t v = {0, 0, 0, 0};
+    if (m < a.M) {
+      const int k = c * 8;
+      v = ld16((k < a.D) ? a.e + (size_t)m * a.D + k : a.h + (size_t)m * a.D + (k - a.D));
+    }
+    *reinterpret_cast<u32x4_t*>(xs + ((size_t)m * chunks + c) * 16) = v;
+  }
+  __syncthreads();
+  const int n0 = (blockIdx.x * 4 + wave) * RW;
+  if (n0 >= a.D) return;
+  float acc[RW][MM];
+#pragma unroll
+  for (int r = 0; r < RW; ++r)
+#pragma unroll
+    for (int m = 0; m < MM; ++m) acc[r][m] = 0.f;
+  const uint16_t* wr = a.w + (size_t)n0 * Kd;
+  for (int c0 = lane; c0 < chunks; c0 += 64 * U) {
+    u32x4_t wv[U][RW];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int r = 0; r < RW; ++r) {
+        const int c = c0 + 64 * u;
+        wv[u][r] = (c < chunks && n0 + r < a.D) ? ld16(wr + (size_t)r * Kd + c * 8)
+                                                 : u32x4_t{0, 0, 0, 0};
+      }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + 64 * u;
+      if (c >= chunks) break;
+#pragma unroll
+      for (int m = 0; m < MM; ++m) {
+        const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(xs + ((size_t)m * chunks + c) * 16);
+        float xf[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          xf[2 * j] = __uint_as_float(xv[j] << 16);
+          xf[2 * j + 1] = __uint_as_float(xv[j] & 0xFFFF0000u);
+        }
+#pragma unroll
+        for (int r = 0; r < RW; ++r) {
+          float s = acc[r][m];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            s = __builtin_fmaf(__uint_as_float(wv[u][r][j] << 16), xf[2 * j], s);
+            s = __builtin_fmaf(__uint_as_float(wv[u][r][j] & 0xFFFF0000u), xf[2 * j + 1], s);
+          }
+          acc[r][m] = s;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RW; ++r)
+#pragma unroll
+    for (int m = 0; m < MM; ++m) {
+      float v = acc[r][m];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+      acc[r][m] = v;
+    }
+  if (lane < RW * MM) {
+    const int r = lane / MM, m = lane - (lane / MM) * MM;
+    float v = 0.f;
+#pragma unroll
+    for (int rr = 0; rr < RW; ++rr)
+#pragma unroll
+      for (int mm = 0; mm < MM; ++mm)
+        if (rr == r && mm == m) v = acc[rr][mm];
+    if (m < a.M && n0 + r < a.D) {
+      const size_t oi = (size_t)m * a.D + n0 + r;
+      if (a.out_bf16)
+        reinterpret_cast<uint16_t*>(a.y)[oi] = (uint16_t)f32_to_bf16_bits(v);
+      else
+        reinterpret_cast<float*>(a.y)[oi] = v;
+    }
+  }
+}
+
 struct HsrPlan {
   int MF, WNF, tiles_m, tiles_n, S, k_slice;
   size_t off_tick, ws_bytes;
@@ -221,10 +316,49 @@ HsrPlan plan_hsr(int m, int d) {
 
 }  // namespace
 
-size_t hsr_workspace(int m, int d_model) { return plan_hsr(m, d_model).ws_bytes; }
+size_t hsr_workspace(int m, int d_model) {
+  if (m <= 8 && (size_t)8 * 4 * d_model <= 160 * 1024) return 0;   // small-M path needs none
+  return plan_hsr(m, d_model).ws_bytes;
+}
+
+constexpr int kGemvMaxM = 8;
 
 spec_status_t launch_hsr(const void* e, const void* h, const void* w, int m, int d_model, void* y,
                          int out_bf16, void* ws, hipStream_t stream) {
+  if (m <= kGemvMaxM && (size_t)kGemvMaxM * 4 * d_model <= 160 * 1024) {
+    HsrArgs a;
+    memset(&a, 0, sizeof(a));
+    a.e = reinterpret_cast<const uint16_t*>(e);
+    a.h = reinterpret_cast<const uint16_t*>(h);
+    a.w = reinterpret_cast<const uint16_t*>(w);
+    a.y = y;
+    a.M = m;
+    a.D = d_model;
+    a.out_bf16 = out_bf16;
+    constexpr int RW = 4, U = 7;
+    const dim3 grid((d_model + 4 * RW - 1) / (4 * RW)), block(256);
+    const int mm = (m <= 1) ? 1 : (m <= 2) ? 2 : (m <= 4) ? 4 : 8;
+    const size_t lds = (size_t)mm * 4 * d_model;
+    switch (mm) {
+      case 1: hipLaunchKernelGGL((hsr_gemv_kernel<1, RW, U>), grid, block, lds, stream, a); break;
+      case 2: hipLaunchKernelGGL((hsr_gemv_kernel<2, RW, U>), grid, block, lds, stream, a); break;
+      case 4: hipLaunchKernelGGL((hsr_gemv_kernel<4, RW, U>), grid, block, lds, stream, a); break;
+      default: {
+        // more than the default 64 KiB of dynamic LDS: raise the limit once
+        static bool raised = false;
+        if (!raised) {
+          if (hipFuncSetAttribute(reinterpret_cast<const void*>(&hsr_gemv_kernel<8, RW, U>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  8 * 4 * 5120) != hipSuccess)
+            return SPEC_ERR_HIP;
+          raised = true;
+        }
+        hipLaunchKernelGGL((hsr_gemv_kernel<8, RW, U>), grid, block, lds, stream, a);
+        break;
+      }
+    }
+    return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+  }
   const HsrPlan p = plan_hsr(m, d_model);
   HsrArgs a;
   a.e = reinterpret_cast<const uint16_t*>(e);
