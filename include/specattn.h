@@ -19,11 +19,17 @@
  *   anything is enqueued, so nothing is partially written.
  * - Workspace: scratch memory comes from the caller (`ws`, `ws_bytes`), sized
  *   by the matching spec_*_workspace() query (which depends only on shapes;
- *   a size of 0 means the call needs none and `ws` may be NULL).  It needs no
- *   initialisation: a call clears the counters it uses, in stream order,
- *   before relying on them.  Calls that share a workspace must not run
- *   concurrently (same stream, or ordered by events); calls with distinct
- *   workspaces may run concurrently on different streams.
+ *   a size of 0 means the call needs none and `ws` may be NULL).  Its first
+ *   SPEC_WS_SYNC_BYTES bytes are a synchronisation region (arrival counters,
+ *   packed row maxima, selection histograms): the caller zero-fills a new
+ *   workspace once, before its first use, and every call returns the words
+ *   it used to zero before it completes, so a workspace can be reused by any
+ *   entry point and any shape without clearing it again (and inside captured
+ *   graphs).  The rest is scratch that needs no initialisation.  Calls that
+ *   share a workspace must not run concurrently (same stream, or ordered by
+ *   events); calls with distinct workspaces may run concurrently on
+ *   different streams.  A call cut short by a device fault can leave the
+ *   region dirty; zero it again after such an error.
  * - Query heads: q and out are [B, n_max, Hq, d] row-major; query head h
  *   reads KV head h / (Hq / Hkv) (consecutive query heads share a KV head).
  * - Positions: sequence b holds kv_len[b] KV positions, which include the
@@ -59,7 +65,11 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 1
+#define SPEC_ABI_VERSION 2
+
+/* Bytes at the start of every non-empty workspace that must be zero before
+ * its first use (see Workspace above). */
+#define SPEC_WS_SYNC_BYTES (1u << 20)
 
 typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype_t;
 

@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(_PKG, "libspecattn.so")
 
 SPEC_F32 = 0
 SPEC_BF16 = 1
-SPEC_ABI_VERSION = 1
+SPEC_ABI_VERSION = 2
+SPEC_WS_SYNC_BYTES = 1 << 20
 
 STATUS = {
     0: "SPEC_OK", 1: "SPEC_ERR_NULL", 2: "SPEC_ERR_SHAPE", 3: "SPEC_ERR_DTYPE",
@@ -123,9 +124,10 @@ def _check(fn: str, st: int):
 class Workspace:
     """A device scratch buffer, grown on demand.
 
-    The library clears whatever counters it uses at the start of each call,
-    so one workspace can serve consecutive calls of any entry point on one
-    stream (never two overlapping calls).
+    A new buffer is zero-filled once: its first SPEC_WS_SYNC_BYTES bytes hold
+    the library's synchronisation words, which every call leaves at zero, so
+    one workspace serves consecutive calls of any entry point on one stream
+    (never two overlapping calls).
     """
 
     def __init__(self, device=None):
@@ -136,7 +138,7 @@ class Workspace:
         if nbytes == 0:
             return None, 0
         if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
-            self.buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+            self.buf = torch.zeros(max(nbytes, SPEC_WS_SYNC_BYTES), dtype=torch.uint8, device=device)
         return ctypes.c_void_p(self.buf.data_ptr()), self.buf.numel()
 
 

@@ -95,14 +95,16 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(AcceptArgs a) {
     }
   }
   // every workgroup of the sequence arrives, including rows past gamma
+  // The maxima are device-scope atomics, read back with atomic exchanges, so
+  // no cache write-back is needed: thread 0 only waits for its own atomicMax
+  // to complete before it arrives.
   if (threadIdx.x == 0) {
-    __threadfence();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     s_tick = atomicAdd(&a.tick[b], 1u);
   }
   __syncthreads();
   if (s_tick != (uint32_t)(a.n_max * a.chunks - 1)) return;
   if (threadIdx.x == 0) {
-    __threadfence();
     int n = -1, nxt = 0;
     for (int r = 0; r < a.n_max; ++r) {
       unsigned long long* slot = &a.best[(size_t)b * a.n_max + r];
@@ -124,7 +126,8 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(AcceptArgs a) {
 
 struct AcceptPlan {
   int chunk, chunks, vec;
-  size_t off_tick, ws_bytes;
+  bool in_sync;
+  size_t off_best, off_tick, ws_bytes;
 };
 
 AcceptPlan plan_accept(int batch, int n_max, int vocab, bool bf16) {
@@ -135,8 +138,15 @@ AcceptPlan plan_accept(int batch, int n_max, int vocab, bool bf16) {
   p.vec = (vocab % vw == 0) ? 1 : 0;
   if (p.chunk > vocab) p.chunk = ((vocab + vw - 1) / vw) * vw;
   p.chunks = (vocab + p.chunk - 1) / p.chunk;
-  p.off_tick = align_up((size_t)batch * n_max * sizeof(unsigned long long), 256);
-  p.ws_bytes = p.off_tick + align_up((size_t)batch * sizeof(uint32_t), 256);
+  // The maxima and counters live in the sync region when they fit: the
+  // finishing workgroup of each sequence returns them to zero, so no clearing
+  // launch is needed.  Otherwise they sit in scratch and are cleared first.
+  const size_t best_bytes = align_up((size_t)batch * n_max * sizeof(unsigned long long), 256);
+  const size_t words = best_bytes + align_up((size_t)batch * sizeof(uint32_t), 256);
+  p.in_sync = words <= kSyncBytes;
+  p.off_best = p.in_sync ? 0 : kSyncBytes;
+  p.off_tick = p.off_best + best_bytes;
+  p.ws_bytes = p.in_sync ? kSyncBytes : kSyncBytes + words;
   return p;
 }
 
@@ -161,7 +171,7 @@ spec_status_t launch_accept(const void* logits, int dtype, int batch, int n_max,
   a.target_tok = target_tok;
   a.accept_len = accept_len;
   a.next_tok = next_tok;
-  a.best = reinterpret_cast<unsigned long long*>(ws);
+  a.best = reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(ws) + p.off_best);
   a.tick = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws) + p.off_tick);
   a.B = batch;
   a.n_max = n_max;
@@ -169,9 +179,11 @@ spec_status_t launch_accept(const void* logits, int dtype, int batch, int n_max,
   a.chunk = p.chunk;
   a.chunks = p.chunks;
   a.vec = p.vec;
-  // row maxima and arrival counters start at zero
-  const spec_status_t st = launch_zero(ws, p.off_tick + (size_t)batch * sizeof(uint32_t), stream);
-  if (st != SPEC_OK) return st;
+  if (!p.in_sync) {
+    const spec_status_t st =
+        launch_zero(a.best, p.off_tick - p.off_best + (size_t)batch * sizeof(uint32_t), stream);
+    if (st != SPEC_OK) return st;
+  }
   const dim3 grid((unsigned)batch * n_max * p.chunks), block(kAcceptThreads);
   if (bf16)
     hipLaunchKernelGGL(accept_kernel<true>, grid, block, 0, stream, a);

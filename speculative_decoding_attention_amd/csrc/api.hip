@@ -194,8 +194,7 @@ spec_status_t spec_topk_attn(const spec_kv_t* kv, int32_t batch, const void* q,
   a.mode = 2;
   a.slots = sel_idx;
   a.slot_stride = top_k;
-  return launch_attention(a, kv->head_dim, kv->dtype, plan.attn,
-                          reinterpret_cast<char*>(ws) + plan.off_attn, stream);
+  return launch_attention(a, kv->head_dim, kv->dtype, plan.attn, ws, stream);
 }
 
 // ---------------------------------------------------------------- HSR ----

@@ -1038,7 +1038,7 @@ int device_cu_count() {
   return cached[dev];
 }
 
-AttnPlan plan_attention(int units, int t_max, int rows, int d, bool gather) {
+AttnPlan plan_attention(int units, int t_max, int rows, int d, bool gather, size_t scratch_off) {
   AttnPlan p;
   const int target = device_cu_count();            // about one workgroup per CU
   const long T = t_max > 0 ? t_max : 1;
@@ -1055,8 +1055,8 @@ AttnPlan plan_attention(int units, int t_max, int rows, int d, bool gather) {
   p.grid = units * S;
   p.gather = gather;
   if (S > 1) {
-    const size_t acc_bytes = (size_t)units * S * rows * d * sizeof(float);
-    p.off_ml = align_up(acc_bytes, 256);
+    p.off_acc = align_up(scratch_off, 256);
+    p.off_ml = p.off_acc + align_up((size_t)units * S * rows * d * sizeof(float), 256);
     p.ws_bytes = p.off_ml + align_up((size_t)units * S * 3 * rows * sizeof(float), 256);
   }
   return p;
@@ -1067,7 +1067,7 @@ spec_status_t launch_attention(AttnArgs a, int d, int dtype, const AttnPlan& pla
   a.S = plan.S;
   a.chunk = plan.chunk;
   if (plan.S > 1) {
-    a.part_acc = reinterpret_cast<float*>(ws);
+    a.part_acc = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + plan.off_acc);
     a.part_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + plan.off_ml);
   } else {
     a.part_acc = nullptr;

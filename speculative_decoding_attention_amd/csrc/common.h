@@ -60,4 +60,28 @@ __device__ __forceinline__ float sum_across_rows(float x) {
   return x;
 }
 
+// Device-wide hand-off between workgroups without cache flushes.  Each XCD
+// has its own L2, so plain stores can sit in one XCD's L2 where another XCD
+// cannot see them, and a release fence writes back that whole L2 (costly:
+// tens of microseconds when every workgroup of a grid does it).  Instead the
+// data handed off is stored and loaded at agent scope: such stores write
+// through to the device-coherent level and complete (vmcnt) only once they
+// are visible there, and such loads bypass the non-coherent caches.  The
+// producer's waves wait for their own stores, meet at a workgroup barrier,
+// and only then does thread 0 signal with an agent-scope atomic; the
+// consumer reads the data only after it has seen the signal.
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __uint_as_float(__hip_atomic_load(const_cast<uint32_t*>(reinterpret_cast<const uint32_t*>(p)),
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+// Every wave's agent-scope stores have completed when this returns.
+__device__ __forceinline__ void block_stores_done() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
 }  // namespace spec

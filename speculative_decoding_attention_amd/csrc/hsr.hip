@@ -29,7 +29,7 @@ struct HsrArgs {
   const uint16_t* w;
   void* y;
   float* part;       // [S, M, D] split-K partials (S > 1)
-  uint32_t* tick;    // [tiles] arrival counters (S > 1), cleared per call
+  uint32_t* tick;    // [tiles] arrival counters (S > 1), in the sync region
   int32_t M, D, out_bf16;
   int32_t tiles_m, tiles_n, S, k_slice;
 };
@@ -166,15 +166,14 @@ __global__ __launch_bounds__(256) void hsr_gemm_kernel(HsrArgs a) {
       if (row >= a.M) continue;
 #pragma unroll
       for (int wn = 0; wn < WNF; ++wn)
-        mine[(size_t)row * a.D + n0 + 16 * wn + r16] = acc[mf][wn][i];
+        st_agent(mine + (size_t)row * a.D + n0 + 16 * wn + r16, acc[mf][wn][i]);
     }
-  __threadfence();
-  __syncthreads();
+  block_stores_done();   // partials visible device-wide before the arrival (see st_agent)
   const int tile = tn * a.tiles_m + tm;
-  if (tid == 0) s_tick = atomicAdd(&a.tick[tile], 1u);
+  if (tid == 0)
+    s_tick = __hip_atomic_fetch_add(&a.tick[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   if (s_tick != (uint32_t)(a.S - 1)) return;
-  __threadfence();
 #pragma unroll
   for (int mf = 0; mf < MF; ++mf)
 #pragma unroll
@@ -186,8 +185,7 @@ __global__ __launch_bounds__(256) void hsr_gemm_kernel(HsrArgs a) {
         const size_t oi = (size_t)row * a.D + n0 + 16 * wn + r16;
         float sum = 0.f;
         for (int s = 0; s < a.S; ++s) {
-          const float* p = a.part + (size_t)s * a.M * a.D + oi;
-          sum += *p;
+          sum += ld_agent(a.part + (size_t)s * a.M * a.D + oi);
         }
         if (a.out_bf16)
           reinterpret_cast<uint16_t*>(a.y)[oi] = (uint16_t)f32_to_bf16_bits(sum);
@@ -309,8 +307,10 @@ HsrPlan plan_hsr(int m, int d) {
   while (S < 16 && tiles * S * 2 <= target + target / 8 && (Kd % (2 * S * kBK)) == 0) S *= 2;
   p.S = S;
   p.k_slice = Kd / S;
-  p.off_tick = (S > 1) ? align_up((size_t)S * m * d * sizeof(float), 256) : 0;
-  p.ws_bytes = (S > 1) ? p.off_tick + align_up((size_t)tiles * sizeof(uint32_t), 256) : 0;
+  // split-K only when tiles * S <= about 1.1 x CUs, so the counters always fit
+  // the sync region; the finishing workgroup of a tile returns its counter to 0
+  p.off_tick = 0;
+  p.ws_bytes = (S > 1) ? kSyncBytes + align_up((size_t)S * m * d * sizeof(float), 256) : 0;
   return p;
 }
 
@@ -365,7 +365,7 @@ spec_status_t launch_hsr(const void* e, const void* h, const void* w, int m, int
   a.h = reinterpret_cast<const uint16_t*>(h);
   a.w = reinterpret_cast<const uint16_t*>(w);
   a.y = y;
-  a.part = (p.S > 1) ? reinterpret_cast<float*>(ws) : nullptr;
+  a.part = (p.S > 1) ? reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + kSyncBytes) : nullptr;
   a.tick = (p.S > 1) ? reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws) + p.off_tick)
                      : nullptr;
   a.M = m;
@@ -375,11 +375,6 @@ spec_status_t launch_hsr(const void* e, const void* h, const void* w, int m, int
   a.tiles_n = p.tiles_n;
   a.S = p.S;
   a.k_slice = p.k_slice;
-  if (p.S > 1) {   // split-K arrival counters start at zero
-    const spec_status_t st =
-        launch_zero(a.tick, (size_t)p.tiles_m * p.tiles_n * sizeof(uint32_t), stream);
-    if (st != SPEC_OK) return st;
-  }
   const dim3 grid(p.tiles_m * p.tiles_n * p.S), block(256);
   const int cfg = p.MF * 10 + p.WNF;
   switch (cfg) {

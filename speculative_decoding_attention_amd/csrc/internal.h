@@ -39,20 +39,30 @@ struct AttnArgs {
   float* lse;
 };
 
+// Every workspace starts with a reserved region of synchronisation words
+// (arrival counters, packed row maxima, selection histograms).  It must be
+// zero when the workspace is first used; every call leaves the words it used
+// at zero again, and no call keeps scratch data in it.  Scratch follows it.
+constexpr size_t kSyncBytes = SPEC_WS_SYNC_BYTES;
+
 struct AttnPlan {
   int S = 1;
   int chunk = 0;
   int grid = 0;
   bool gather = false;        // slots resolved through a list or a page table
-  size_t ws_bytes = 0;
+  size_t off_acc = 0;         // byte offsets of the partials in the workspace
   size_t off_ml = 0;
+  size_t ws_bytes = 0;
 };
 
 int device_cu_count();
 
 // Split plan for U units of at most t_max slots and R rows of width d.
 // `gather`: slot positions come from a list, or rows from a page table.
-AttnPlan plan_attention(int units, int t_max, int rows, int d, bool gather);
+// The partials start at byte `scratch_off` (at least kSyncBytes); ws_bytes is
+// the end of the whole layout, or 0 when a single split needs no workspace.
+AttnPlan plan_attention(int units, int t_max, int rows, int d, bool gather,
+                        size_t scratch_off = kSyncBytes);
 
 spec_status_t launch_attention(AttnArgs a, int d, int dtype, const AttnPlan& plan, void* ws,
                                hipStream_t stream);
@@ -61,8 +71,8 @@ spec_status_t launch_attention(AttnArgs a, int d, int dtype, const AttnPlan& pla
 struct TopkPlan {
   size_t off_scores = 0;    // fp64 [U, max_len]
   size_t off_hist = 0;      // uint32 [U, 4096]
-  size_t off_attn = 0;      // attention workspace
-  AttnPlan attn;
+  bool hist_in_sync = false;  // histogram inside the sync region (no clearing launch)
+  AttnPlan attn;            // offsets relative to the same workspace
   size_t ws_bytes = 0;
 };
 TopkPlan plan_topk(int units, int max_len, int top_k, int rows, int d);

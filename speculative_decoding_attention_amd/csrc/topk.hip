@@ -341,11 +341,18 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(TopkArgs a) {
 
 TopkPlan plan_topk(int units, int max_len, int top_k, int rows, int d) {
   TopkPlan p;
-  p.off_scores = 0;
-  p.off_hist = align_up((size_t)units * max_len * sizeof(double), 256);
-  p.off_attn = align_up(p.off_hist + (size_t)units * kHistBins * sizeof(uint32_t), 256);
-  p.attn = plan_attention(units, top_k, rows, d, true);
-  p.ws_bytes = p.off_attn + p.attn.ws_bytes;
+  const size_t hist_bytes = (size_t)units * kHistBins * sizeof(uint32_t);
+  p.hist_in_sync = hist_bytes <= kSyncBytes;
+  p.off_scores = kSyncBytes;
+  size_t end = align_up(p.off_scores + (size_t)units * max_len * sizeof(double), 256);
+  if (p.hist_in_sync) {
+    p.off_hist = 0;
+  } else {
+    p.off_hist = end;
+    end = align_up(end + hist_bytes, 256);
+  }
+  p.attn = plan_attention(units, top_k, rows, d, true, end);
+  p.ws_bytes = p.attn.ws_bytes > end ? p.attn.ws_bytes : end;
   return p;
 }
 
@@ -371,8 +378,11 @@ spec_status_t launch_topk_select(const AttnArgs& aa, int d, int dtype, int top_k
   a.sel_idx = sel_idx;
   const int units = a.B * a.Hkv;
   const int tiles = (a.max_len + kScoreKeys - 1) / kScoreKeys;
-  spec_status_t st = launch_zero(a.hist, (size_t)units * kHistBins * sizeof(uint32_t), stream);
-  if (st != SPEC_OK) return st;
+  if (!plan.hist_in_sync) {   // scratch holds arbitrary data; the select kernel clears it after use
+    const spec_status_t st =
+        launch_zero(a.hist, (size_t)units * kHistBins * sizeof(uint32_t), stream);
+    if (st != SPEC_OK) return st;
+  }
   const dim3 grid(units * tiles), block(256);
   if (dtype == SPEC_BF16) {
     if (d == 64) hipLaunchKernelGGL((topk_score_kernel<64, true>), grid, block, 0, stream, a);
