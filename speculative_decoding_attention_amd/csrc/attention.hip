@@ -616,6 +616,25 @@ __device__ __forceinline__ void pipe_finish(const AttnArgs& a, float* smem, int 
   }
 }
 
+// DMA of the unit's NB*16 query rows (256 bytes each, row-major) to LDS at
+// q_lds: 1 KB instructions of 4 rows, spread over the waves.  Rows past the
+// block (n >= n_max*G) fetch row 0 instead; every row that is not a live
+// query is masked when read.
+template <int NB>
+__device__ __forceinline__ void pipe_issue_q(const AttnArgs& a, int b, int g, uint32_t q_lds,
+                                             int wave, int lane) {
+  using C = PipeCfg<NB>;
+  for (int j = wave; j < NB * 4; j += C::WAVES) {
+    int n = 4 * j + (lane >> 4);
+    if (n >= a.R) n = 0;
+    const int qi = n / a.G, hh = n - qi * a.G;
+    const unsigned char* src = reinterpret_cast<const unsigned char*>(a.q) +
+                               ((((size_t)b * a.n_max + qi) * a.Hq + g * a.G + hh) * 128) * 2 +
+                               16 * (lane & 15);
+    dma16(src, q_lds + (uint32_t)(j * 1024));
+  }
+}
+
 template <int NB, bool GATHER>
 __global__ __launch_bounds__(PipeCfg<NB>::WAVES * 64, 1) void attn_bf16_pipe_kernel(AttnArgs a) {
   using C = PipeCfg<NB>;
@@ -630,6 +649,12 @@ __global__ __launch_bounds__(PipeCfg<NB>::WAVES * 64, 1) void attn_bf16_pipe_ker
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int u = wg / a.S, s = wg - u * a.S;
   const int b = u / a.Hkv, g = u - b * a.Hkv;
+  lds_u8_t* const ring_l = (lds_u8_t*)ring;        // the ring as an LDS-address-space pointer
+  const uint32_t ring_lds = (uint32_t)(size_t)ring_l;
+  constexpr uint32_t kQSlot = (uint32_t)((C::NS - 1) * C::TILE_BYTES);
+  // Dense splits: the query block goes out first, so its round trip overlaps
+  // the scalar loads of the lengths and the first K/V tiles.
+  if (!GATHER) pipe_issue_q<NB>(a, b, g, ring_lds + kQSlot, wave, lane);
   const int L = a.kv_len[b];
   const int nq = a.q_len ? a.q_len[b] : a.n_max;
   const int T = (a.mode == 0) ? L : (a.mode == 1 ? a.slot_len[b] : min(a.slot_stride, L));
@@ -653,22 +678,15 @@ __global__ __launch_bounds__(PipeCfg<NB>::WAVES * 64, 1) void attn_bf16_pipe_ker
   const bool active = nb < NB;
   const int n = nb * 16 + r16;
   const bool valid = active && n < nq * a.G;
-  const int qi = n / a.G, hh = n - qi * a.G;
+  const int qi = n / a.G;
   const int rowP = valid ? L - nq + qi : 0x7fffffff;
+  // Gathered splits resolve their slots first (plain loads the compiler
+  // waits for), then send the query block ahead of the first tiles.
+  if (GATHER) pipe_issue_q<NB>(a, b, g, ring_lds + kQSlot, wave, lane);
   bf16x8_t qop[4];
-  {
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
-                         (((size_t)b * a.n_max + qi) * a.Hq + g * a.G + hh) * D + 8 * q4;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      qop[ks] = valid ? as_bf16x8(ld16(qp + 32 * ks)) : as_bf16x8(u32x4_t{0, 0, 0, 0});
-  }
-  // Q must be in registers before the DMA stream starts (the compiler does
-  // not count the DMA loads, so its own waits would over-wait later).
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  for (int ks = 0; ks < 4; ++ks) qop[ks] = as_bf16x8(u32x4_t{0, 0, 0, 0});
 
-  lds_u8_t* const ring_l = (lds_u8_t*)ring;        // the ring as an LDS-address-space pointer
-  const uint32_t ring_lds = (uint32_t)(size_t)ring_l;
   for (int j = 0; j < C::NS - 1 && j < n_tiles; ++j)
     pipe_issue_tile<NB, GATHER>(a, sm, t_beg + j * C::TILE_KEYS, t_end,
                                 ring_lds + (uint32_t)(j * C::TILE_BYTES), wave, lane);
@@ -681,6 +699,17 @@ __global__ __launch_bounds__(PipeCfg<NB>::WAVES * 64, 1) void attn_bf16_pipe_ker
   for (int t = 0; t < n_tiles; ++t) {
     const int later = min(C::NS - 2, n_tiles - 1 - t);
     wait_tiles_barrier<C::PER_WAVE>(later);
+    if (t == 0) {
+      // the query block landed with (before) tile 0; every wave copies its
+      // rows out before tile NS-1 reuses the slot
+      if (valid) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          qop[ks] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(
+              ring + kQSlot + n * 256 + 16 * q4 + 64 * ks));
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
     if (t + C::NS - 1 < n_tiles)
       pipe_issue_tile<NB, GATHER>(a, sm, t_beg + (t + C::NS - 1) * C::TILE_KEYS, t_end,
                                   ring_lds + (uint32_t)(((t + C::NS - 1) % C::NS) * C::TILE_BYTES),
@@ -777,6 +806,7 @@ __global__ __launch_bounds__(PipeCfg<NB>::WAVES * 64, 1) void attn_bf16_pipe_ker
       acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), pop, acc[db], 0, 0, 0);
     }
   }
+  if (n_tiles == 0) wait_dma_barrier<0>();   // the query DMA still targets the ring
   pipe_finish<NB>(a, reinterpret_cast<float*>(ring), wave, lane, active, nb, p, u, s, b, g, nq,
                   m_run, l_run, l_rnd, acc);
 }
@@ -914,16 +944,19 @@ __global__ __launch_bounds__(256, 1) void attn_f32_kernel(AttnArgs a) {
 
 // --------------------------------------------------------------- merge ----
 // One workgroup per (unit, row): combine the S partials with the log-sum-exp
-// rule.  The split weights are computed once into LDS; then 256/D groups of
-// D threads each sum a strided subset of the splits (many loads in flight),
-// and the groups are added in a fixed order.
+// rule.  Every partial this thread needs is requested before the split
+// weights are known (they only scale the sum), so the kernel waits for one
+// round of loads; wave 0 meanwhile turns the splits' (m, l, l_rnd) into
+// weights in LDS.  Threads form 256/D groups over the splits; each group
+// sums its splits in order and the groups are added in a fixed order.
 constexpr int kMaxSplits = 4096;
 
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   constexpr int NG = 256 / D;
+  constexpr int PB = 32;                     // partials in flight per thread
   __shared__ float w_s[kMaxSplits];
-  __shared__ float red[3][256 / 64];
+  __shared__ float stat[3];
   __shared__ float part[NG][D];
   const int R = a.R, S = a.S;
   const int u = blockIdx.x / R, r = blockIdx.x - (blockIdx.x / R) * R;
@@ -931,46 +964,52 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   const int nq = a.q_len ? a.q_len[b] : a.n_max;
   const int i = r / a.G, hh = r - i * a.G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float* pm = a.part_ml + (size_t)u * S * 3 * R;
-
-  float mx = -INFINITY;
-  for (int s = tid; s < S; s += 256) mx = fmaxf(mx, pm[s * 3 * R + r]);
-  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-  if (lane == 0) red[0][wave] = mx;
-  __syncthreads();
-  float M = red[0][0];
-  for (int w = 1; w < 4; ++w) M = fmaxf(M, red[0][w]);
-  const float Mu = (M == -INFINITY) ? 0.f : M;
-  float ls = 0.f, lr = 0.f;
-  for (int s = tid; s < S; s += 256) {
-    const float w = exp2f(pm[s * 3 * R + r] - Mu);
-    w_s[s] = w;
-    ls += pm[s * 3 * R + R + r] * w;
-    lr += pm[s * 3 * R + 2 * R + r] * w;
-  }
-  for (int o = 32; o > 0; o >>= 1) {
-    ls += __shfl_xor(ls, o);
-    lr += __shfl_xor(lr, o);
-  }
-  __syncthreads();
-  if (lane == 0) {
-    red[1][wave] = ls;
-    red[2][wave] = lr;
-  }
-  __syncthreads();
-  const float Ls = red[1][0] + red[1][1] + red[1][2] + red[1][3];
-  const float Lr = red[2][0] + red[2][1] + red[2][2] + red[2][3];
-
   const int d = tid % D, grp = tid / D;
+  const float* pm = a.part_ml + (size_t)u * S * 3 * R;
   const float* pa = a.part_acc + (size_t)u * S * R * D + (size_t)r * D + d;
+
+  float v[PB];
+#pragma unroll
+  for (int j = 0; j < PB; ++j) {
+    const int sp = grp + NG * j;
+    v[j] = (sp < S) ? pa[(size_t)sp * R * D] : 0.f;
+  }
+  if (wave == 0) {
+    float mx = -INFINITY;
+    for (int sp = lane; sp < S; sp += 64) mx = fmaxf(mx, pm[sp * 3 * R + r]);
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    const float Mu = (mx == -INFINITY) ? 0.f : mx;
+    float ls = 0.f, lr = 0.f;
+    for (int sp = lane; sp < S; sp += 64) {
+      const float w = exp2f(pm[sp * 3 * R + r] - Mu);
+      w_s[sp] = w;
+      ls += pm[sp * 3 * R + R + r] * w;
+      lr += pm[sp * 3 * R + 2 * R + r] * w;
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+      ls += __shfl_xor(ls, o);
+      lr += __shfl_xor(lr, o);
+    }
+    if (lane == 0) {
+      stat[0] = mx;
+      stat[1] = ls;
+      stat[2] = lr;
+    }
+  }
+  __syncthreads();
   float o = 0.f;
-#pragma unroll 8
-  for (int s = grp; s < S; s += NG) o += pa[(size_t)s * R * D] * w_s[s];
+#pragma unroll
+  for (int j = 0; j < PB; ++j) {
+    const int sp = grp + NG * j;
+    if (sp < S) o += v[j] * w_s[sp];
+  }
+  for (int sp = grp + NG * PB; sp < S; sp += NG) o += pa[(size_t)sp * R * D] * w_s[sp];
   part[grp][d] = o;
   __syncthreads();
   if (grp != 0) return;
   o = part[0][d];
   for (int k = 1; k < NG; ++k) o += part[k][d];
+  const float M = stat[0], Ls = stat[1], Lr = stat[2];
   const bool live = (i < nq) && (Ls > 0.f);
   o = live ? o / Lr : 0.f;
   const size_t oi = (((size_t)b * a.n_max + i) * a.Hq + g * a.G + hh) * D + d;
