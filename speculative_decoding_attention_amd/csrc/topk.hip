@@ -31,6 +31,7 @@ namespace {
 constexpr int kHistBins = 4096;
 constexpr int kScoreKeys = 256;   // keys per score workgroup
 constexpr int kCandMax = 4096;    // candidates sortable in LDS
+constexpr int kSelBatch = 16;     // scores in flight per thread in the selection passes
 
 struct TopkArgs {
   const void* q;
@@ -75,6 +76,7 @@ __global__ __launch_bounds__(256) void topk_score_kernel(TopkArgs a) {
   __shared__ __align__(16) unsigned char krows[kScoreKeys * PITCH];
   __shared__ double qbar[D];
   __shared__ uint32_t hist[kHistBins];
+  __shared__ size_t rowidx[kScoreKeys];
 
   const int tiles = (a.max_len + kScoreKeys - 1) / kScoreKeys;
   const int u = blockIdx.x / tiles, tile = blockIdx.x - (blockIdx.x / tiles) * tiles;
@@ -95,15 +97,31 @@ __global__ __launch_bounds__(256) void topk_score_kernel(TopkArgs a) {
     }
     qbar[threadIdx.x] = s;
   }
-  // stage the K rows: ROW_B/16 chunks of 16 bytes per key
+  // resolve the tile's rows once (page table lookups), then stage the K rows
+  // (ROW_B/16 chunks of 16 bytes per key) with a batch of loads in flight
+  if ((int)threadIdx.x < nk) rowidx[threadIdx.x] = topk_row(a, b, g, j0 + threadIdx.x);
+  __syncthreads();
   constexpr int CH = ROW_B / 16;
+  constexpr int PB = 16;                                   // loads in flight per thread
   const unsigned char* kb = reinterpret_cast<const unsigned char*>(a.k);
-  for (int e = threadIdx.x; e < nk * CH; e += blockDim.x) {
-    const int key = e / CH, ch = e - (e / CH) * CH;
-    const u32x4_t v = ld16(kb + topk_row(a, b, g, j0 + key) * ROW_B + ch * 16);
-    uint2* dst = reinterpret_cast<uint2*>(krows + key * PITCH + ch * 16);   // 8-byte aligned
-    dst[0] = make_uint2(v[0], v[1]);
-    dst[1] = make_uint2(v[2], v[3]);
+  for (int e0 = 0; e0 < nk * CH; e0 += PB * 256) {
+    u32x4_t v[PB];
+#pragma unroll
+    for (int k = 0; k < PB; ++k) {
+      const int e = e0 + k * 256 + threadIdx.x;
+      const int key = e / CH, ch = e - (e / CH) * CH;
+      v[k] = (e < nk * CH) ? ld16(kb + rowidx[key] * ROW_B + ch * 16) : u32x4_t{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int k = 0; k < PB; ++k) {
+      const int e = e0 + k * 256 + threadIdx.x;
+      const int key = e / CH, ch = e - (e / CH) * CH;
+      if (e < nk * CH) {
+        uint2* dst = reinterpret_cast<uint2*>(krows + key * PITCH + ch * 16);   // 8-byte aligned
+        dst[0] = make_uint2(v[k][0], v[k][1]);
+        dst[1] = make_uint2(v[k][2], v[k][3]);
+      }
+    }
   }
   __syncthreads();
 
@@ -225,14 +243,23 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(TopkArgs a) {
   const uint32_t bstar = s_bin;
   int need = K - (int)s_above;                           // 1..count(bstar)
 
-  // (b) gather the boundary bin's keys
-  for (int j = tid; j < L; j += nt) {
-    const double s = sc[j];
-    if (coarse_bin(s) == bstar) {
-      const uint32_t p = atomicAdd(&s_ncand, 1u);
-      if (p < (uint32_t)kCandMax) {
-        ckey[p] = order_key64(s);
-        cidx[p] = j;
+  // (b) gather the boundary bin's keys, kSelBatch scores in flight per thread
+  for (int j0 = 0; j0 < L; j0 += nt * kSelBatch) {
+    double sv[kSelBatch];
+#pragma unroll
+    for (int k = 0; k < kSelBatch; ++k) {
+      const int j = j0 + k * nt + tid;
+      sv[k] = (j < L) ? sc[j] : 0.0;
+    }
+#pragma unroll
+    for (int k = 0; k < kSelBatch; ++k) {
+      const int j = j0 + k * nt + tid;
+      if (j < L && coarse_bin(sv[k]) == bstar) {
+        const uint32_t p = atomicAdd(&s_ncand, 1u);
+        if (p < (uint32_t)kCandMax) {
+          ckey[p] = order_key64(sv[k]);
+          cidx[p] = j;
+        }
       }
     }
   }
@@ -319,19 +346,32 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(TopkArgs a) {
     __syncthreads();
   }
 
-  // (d) ordered compaction of the selected keys
+  // (d) ordered compaction of the selected keys: each round gives every
+  //     thread a contiguous run of 32 keys, so one block scan of the run
+  //     counts places the whole round in ascending order
   const uint64_t tk = s_thr_key;
   const int ti = s_thr_idx;
   uint32_t base = 0;
-  for (int j0 = 0; j0 < L; j0 += nt) {
-    const int j = j0 + tid;
-    uint32_t f = 0;
-    if (j < L) {
-      const uint64_t kk = order_key64(sc[j]);
-      f = (kk > tk || (kk == tk && j <= ti)) ? 1u : 0u;
+  for (int r0 = 0; r0 < L; r0 += nt * 32) {
+    const int jl = r0 + tid * 32;
+    double sv[32];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) sv[k] = (jl + k < L) ? sc[jl + k] : 0.0;
+    uint32_t mask = 0;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const int j = jl + k;
+      const uint64_t kk = order_key64(sv[k]);
+      if (j < L && (kk > tk || (kk == tk && j <= ti))) mask |= 1u << k;
     }
-    const uint32_t ex = block_exclusive_scan(f, wsum, &s_total);
-    if (f && base + ex < (uint32_t)K) out[base + ex] = j;
+    const uint32_t ex = block_exclusive_scan((uint32_t)__popc(mask), wsum, &s_total);
+    uint32_t pos = base + ex;
+    while (mask) {
+      const int k = __ffs(mask) - 1;
+      mask &= mask - 1;
+      if (pos < (uint32_t)K) out[pos] = jl + k;
+      ++pos;
+    }
     base += s_total;
   }
   for (int j = K - 1 - tid; j >= (int)base; j -= nt) out[j] = -1;   // base == K here
