@@ -13,12 +13,17 @@
 //   coarse monotone key (the top 12 bits of the order-preserving bit pattern
 //   of float(score): sign, exponent, 3 mantissa bits).
 // topk_select_kernel: one 1024-thread workgroup per unit.  From the
-//   histogram it finds the bin holding the K-th key, gathers that bin's keys
-//   into LDS, sorts them by (score desc, index asc), which fixes the exact
-//   threshold (score*, index*), then writes the selected indices in ascending
-//   order with a block-wide ordered compaction.  If the boundary bin holds
-//   more keys than LDS can sort, an exact radix select over the 64-bit keys
-//   (8-bit digits) takes over.
+//   histogram it finds the bin holding the K-th key.  One pass over the
+//   scores sets an LDS selection bit for every key above that bin and
+//   gathers the bin's keys as candidates.  A second 4096-bin histogram over
+//   the next 12 bits of the float key narrows the candidates to one sub-bin,
+//   whose few keys are ranked by counting; that fixes the exact threshold
+//   (score*, index*).  The winners' bits are set and the selected indices are
+//   written in ascending order from the bits with one block scan.  Fallbacks
+//   keep every case exact: a bitonic sort of the candidates when one sub-bin
+//   holds many equal float keys, an exact radix select over the 64-bit keys
+//   when the bin holds more candidates than LDS, and compaction straight from
+//   the scores when the cache is longer than the LDS bit mask.
 #include <math.h>
 
 #include "common.h"
@@ -188,11 +193,31 @@ __device__ __forceinline__ bool cand_before(uint64_t ka, int ia, uint64_t kb, in
   return ka > kb || (ka == kb && ia < ib);   // (score desc, index asc)
 }
 
+// Inverse of order_key64 (for -0 folded onto +0 it returns +0).
+__device__ __forceinline__ double key64_to_double(uint64_t k) {
+  const uint64_t u = (k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k;
+  return __longlong_as_double((long long)u);
+}
+
+// Order-preserving 32-bit key of float(score); coarse_bin is its top 12 bits.
+__device__ __forceinline__ uint32_t fine_key32(double x) {
+  float f = (float)x;
+  if (f == 0.f) f = 0.f;
+  const uint32_t u = __float_as_uint(f);
+  return (u >> 31) ? ~u : (u | 0x80000000u);
+}
+
+constexpr int kMaskKeys = 131072;   // keys whose selection bits fit LDS
+constexpr int kSmall = 1024;        // boundary sub-bin sizes ranked by counting
+
 __global__ __launch_bounds__(1024) void topk_select_kernel(TopkArgs a) {
   __shared__ uint64_t ckey[kCandMax];
   __shared__ int32_t cidx[kCandMax];
+  __shared__ uint32_t selmask[kMaskKeys / 32];   // bit j: key j is selected
+  __shared__ uint32_t fh[kHistBins];             // second-level histogram of the candidates
+  __shared__ uint16_t small[kSmall];             // candidates of the boundary sub-bin
   __shared__ uint32_t wsum[16];
-  __shared__ uint32_t s_total, s_ncand, s_bin, s_above;
+  __shared__ uint32_t s_total, s_ncand, s_bin, s_above, s_nsmall;
   __shared__ uint64_t s_thr_key;
   __shared__ int32_t s_thr_idx;
   __shared__ uint32_t dh[256];
@@ -204,13 +229,14 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(TopkArgs a) {
   const double* sc = a.scores + (size_t)u * a.max_len;
   int32_t* out = a.sel_idx + (size_t)u * K;
   uint32_t* gh = a.hist + (size_t)u * kHistBins;
-  const int tid = threadIdx.x, nt = blockDim.x;
+  const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wave = tid >> 6;
 
   if (K >= L) {
     for (int j = tid; j < K; j += nt) out[j] = (j < L) ? j : -1;
     for (int i = tid; i < kHistBins; i += nt) gh[i] = 0;
     return;
   }
+  const bool use_mask = L <= kMaskKeys;
 
   // (a) boundary bin of the coarse histogram: highest bin whose suffix count
   //     reaches K.  Thread t owns bins [4t, 4t+4); counts scanned from the top.
@@ -243,7 +269,9 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(TopkArgs a) {
   const uint32_t bstar = s_bin;
   int need = K - (int)s_above;                           // 1..count(bstar)
 
-  // (b) gather the boundary bin's keys, kSelBatch scores in flight per thread
+  // (b) one pass over the scores, kSelBatch per thread in flight: keys above
+  //     the boundary bin set their selection bit (a wave's ballot covers 64
+  //     consecutive keys), keys in it are appended to the candidate list
   for (int j0 = 0; j0 < L; j0 += nt * kSelBatch) {
     double sv[kSelBatch];
 #pragma unroll
@@ -254,48 +282,113 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(TopkArgs a) {
 #pragma unroll
     for (int k = 0; k < kSelBatch; ++k) {
       const int j = j0 + k * nt + tid;
-      if (j < L && coarse_bin(sv[k]) == bstar) {
-        const uint32_t p = atomicAdd(&s_ncand, 1u);
-        if (p < (uint32_t)kCandMax) {
-          ckey[p] = order_key64(sv[k]);
-          cidx[p] = j;
+      const uint32_t cb = coarse_bin(sv[k]);
+      const bool above = j < L && cb > bstar;
+      const bool cand = j < L && cb == bstar;
+      const uint64_t ba = __builtin_amdgcn_ballot_w64(above);
+      const uint64_t bc = __builtin_amdgcn_ballot_w64(cand);
+      if (use_mask && lane == 0) {
+        const int w = (j0 + k * nt + wave * 64) >> 5;   // 64-aligned run of keys
+        selmask[w] = (uint32_t)ba;
+        selmask[w + 1] = (uint32_t)(ba >> 32);
+      }
+      if (bc) {
+        uint32_t wbase = 0;
+        if (lane == 0) wbase = atomicAdd(&s_ncand, (uint32_t)__popcll(bc));
+        wbase = __shfl(wbase, 0);
+        if (cand) {
+          const uint32_t pos = wbase + (uint32_t)__popcll(bc & ((1ull << lane) - 1ull));
+          if (pos < (uint32_t)kCandMax) {
+            ckey[pos] = order_key64(sv[k]);
+            cidx[pos] = j;
+          }
         }
       }
     }
   }
+  for (int i = tid; i < kHistBins; i += nt) fh[i] = 0;
+  if (tid == 0) s_nsmall = 0;
   __syncthreads();
   const uint32_t ncand = s_ncand;
 
   if (ncand <= (uint32_t)kCandMax) {
-    // (c) bitonic sort of the candidates, padded to a power of two
-    uint32_t n2 = 1;
-    while (n2 < ncand) n2 <<= 1;
-    for (uint32_t i = ncand + tid; i < n2; i += nt) {
-      ckey[i] = 0;          // below every real key
-      cidx[i] = 0x7fffffff;
-    }
+    need = max(1, min(need, (int)max(ncand, 1u)));        // guards a corrupted histogram
+    // (c1) second level: the next 12 bits of the float key split the boundary
+    //      bin; find the sub-bin holding the need-th candidate
+    for (uint32_t i = tid; i < ncand; i += nt)
+      atomicAdd(&fh[(fine_key32(key64_to_double(ckey[i])) >> 8) & 0xFFFu], 1u);
     __syncthreads();
-    for (uint32_t size = 2; size <= n2; size <<= 1) {
-      for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
-        for (uint32_t t = tid; t < n2 / 2; t += nt) {
-          const uint32_t lo = 2 * t - (t & (stride - 1));
-          const uint32_t hi = lo + stride;
-          const bool up = ((lo & size) == 0);   // "up" = (score desc, index asc) order
-          const uint64_t kl = ckey[lo], kh = ckey[hi];
-          const int il = cidx[lo], ih = cidx[hi];
-          const bool swap = up ? cand_before(kh, ih, kl, il) : cand_before(kl, il, kh, ih);
-          if (swap) {
-            ckey[lo] = kh; ckey[hi] = kl;
-            cidx[lo] = ih; cidx[hi] = il;
-          }
+    uint32_t f4[4];
+    uint32_t fm = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f4[i] = fh[kHistBins - 1 - (tid * 4 + i)];
+      fm += f4[i];
+    }
+    const uint32_t fbefore = block_exclusive_scan(fm, wsum, &s_total);
+    {
+      uint32_t run = fbefore;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (run < (uint32_t)need && run + f4[i] >= (uint32_t)need) {
+          s_bin = kHistBins - 1 - (tid * 4 + i);
+          s_above = run;
         }
-        __syncthreads();
+        run += f4[i];
       }
     }
-    need = max(1, min(need, (int)max(ncand, 1u)));        // guards a corrupted histogram
-    if (tid == 0) {
-      s_thr_key = ckey[need - 1];
-      s_thr_idx = cidx[need - 1];
+    __syncthreads();
+    const uint32_t fbin = s_bin;
+    const int need2 = need - (int)s_above;
+    const uint32_t fcount = fh[fbin];
+    if (fcount <= (uint32_t)kSmall) {
+      // (c2) rank the sub-bin's candidates by counting
+      for (uint32_t i = tid; i < ncand; i += nt)
+        if (((fine_key32(key64_to_double(ckey[i])) >> 8) & 0xFFFu) == fbin)
+          small[atomicAdd(&s_nsmall, 1u)] = (uint16_t)i;
+      __syncthreads();
+      const uint32_t m = s_nsmall;
+      for (uint32_t i = tid; i < m; i += nt) {
+        const uint64_t ki = ckey[small[i]];
+        const int ii = cidx[small[i]];
+        int rank = 0;
+        for (uint32_t j = 0; j < m; ++j)
+          rank += cand_before(ckey[small[j]], cidx[small[j]], ki, ii) ? 1 : 0;
+        if (rank == need2 - 1) {
+          s_thr_key = ki;
+          s_thr_idx = ii;
+        }
+      }
+    } else {
+      // (c2') many equal float keys: bitonic sort of all candidates
+      uint32_t n2 = 1;
+      while (n2 < ncand) n2 <<= 1;
+      for (uint32_t i = ncand + tid; i < n2; i += nt) {
+        ckey[i] = 0;          // below every real key
+        cidx[i] = 0x7fffffff;
+      }
+      __syncthreads();
+      for (uint32_t size = 2; size <= n2; size <<= 1) {
+        for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+          for (uint32_t t = tid; t < n2 / 2; t += nt) {
+            const uint32_t lo = 2 * t - (t & (stride - 1));
+            const uint32_t hi = lo + stride;
+            const bool up = ((lo & size) == 0);   // "up" = (score desc, index asc) order
+            const uint64_t kl = ckey[lo], kh = ckey[hi];
+            const int il = cidx[lo], ih = cidx[hi];
+            const bool swap = up ? cand_before(kh, ih, kl, il) : cand_before(kl, il, kh, ih);
+            if (swap) {
+              ckey[lo] = kh; ckey[hi] = kl;
+              cidx[lo] = ih; cidx[hi] = il;
+            }
+          }
+          __syncthreads();
+        }
+      }
+      if (tid == 0) {
+        s_thr_key = ckey[need - 1];
+        s_thr_idx = cidx[need - 1];
+      }
     }
     __syncthreads();
   } else {
@@ -345,34 +438,61 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(TopkArgs a) {
     if (tid == 0) s_thr_key = prefix;
     __syncthreads();
   }
-
-  // (d) ordered compaction of the selected keys: each round gives every
-  //     thread a contiguous run of 32 keys, so one block scan of the run
-  //     counts places the whole round in ascending order
   const uint64_t tk = s_thr_key;
   const int ti = s_thr_idx;
+
+  // (d) ordered compaction of the selected keys
   uint32_t base = 0;
-  for (int r0 = 0; r0 < L; r0 += nt * 32) {
-    const int jl = r0 + tid * 32;
-    double sv[32];
-#pragma unroll
-    for (int k = 0; k < 32; ++k) sv[k] = (jl + k < L) ? sc[jl + k] : 0.0;
-    uint32_t mask = 0;
-#pragma unroll
-    for (int k = 0; k < 32; ++k) {
-      const int j = jl + k;
-      const uint64_t kk = order_key64(sv[k]);
-      if (j < L && (kk > tk || (kk == tk && j <= ti))) mask |= 1u << k;
+  if (use_mask && ncand <= (uint32_t)kCandMax) {
+    // the boundary bin's winners join the bits of the keys above it; then
+    // thread t owns a contiguous run of mask words, so one scan orders all
+    for (uint32_t i = tid; i < ncand; i += nt) {
+      const uint64_t kk = ckey[i];
+      const int j = cidx[i];
+      if (kk > tk || (kk == tk && j <= ti)) atomicOr(&selmask[j >> 5], 1u << (j & 31));
     }
-    const uint32_t ex = block_exclusive_scan((uint32_t)__popc(mask), wsum, &s_total);
-    uint32_t pos = base + ex;
-    while (mask) {
-      const int k = __ffs(mask) - 1;
-      mask &= mask - 1;
-      if (pos < (uint32_t)K) out[pos] = jl + k;
-      ++pos;
+    __syncthreads();
+    const int nwords = (L + 31) >> 5;
+    const int per = (nwords + nt - 1) / nt;
+    const int w0 = min(nwords, tid * per), w1 = min(nwords, w0 + per);
+    uint32_t cnt = 0;
+    for (int w = w0; w < w1; ++w) cnt += (uint32_t)__popc(selmask[w]);
+    const uint32_t ex = block_exclusive_scan(cnt, wsum, &s_total);
+    uint32_t pos = ex;
+    for (int w = w0; w < w1; ++w) {
+      uint32_t bits = selmask[w];
+      while (bits) {
+        const int k = __ffs(bits) - 1;
+        bits &= bits - 1;
+        if (pos < (uint32_t)K) out[pos] = (w << 5) + k;
+        ++pos;
+      }
     }
-    base += s_total;
+    base = s_total;
+  } else {
+    // long caches: rounds of 32-key runs per thread straight from the scores
+    for (int r0 = 0; r0 < L; r0 += nt * 32) {
+      const int jl = r0 + tid * 32;
+      double sv[32];
+#pragma unroll
+      for (int k = 0; k < 32; ++k) sv[k] = (jl + k < L) ? sc[jl + k] : 0.0;
+      uint32_t mask = 0;
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        const int j = jl + k;
+        const uint64_t kk = order_key64(sv[k]);
+        if (j < L && (kk > tk || (kk == tk && j <= ti))) mask |= 1u << k;
+      }
+      const uint32_t ex = block_exclusive_scan((uint32_t)__popc(mask), wsum, &s_total);
+      uint32_t pos = base + ex;
+      while (mask) {
+        const int k = __ffs(mask) - 1;
+        mask &= mask - 1;
+        if (pos < (uint32_t)K) out[pos] = jl + k;
+        ++pos;
+      }
+      base += s_total;
+    }
   }
   for (int j = K - 1 - tid; j >= (int)base; j -= nt) out[j] = -1;   // base == K here
 }

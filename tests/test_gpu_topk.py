@@ -69,6 +69,24 @@ def test_topk_ties_straddling_the_cut():
     assert_attention_close(out, lse, ro, rl, np.ones(2, np.int32), W.BF16, "topk ties")
 
 
+def test_topk_large_tie_group_at_the_cut():
+    """2000 identical key rows spread over a 3000-key cache with the cut inside
+    the group: the boundary holds more equal keys than counting ranks, so
+    the candidates are sorted; the lowest indices of the group must win."""
+    rng = np.random.default_rng(9)
+    c = W.small_attn(23, 1, 8, 2, 128, 1, (3000,), W.BF16)
+    kb = c.k.bits.copy()
+    for g in range(2):
+        rows = rng.choice(3000, size=2000, replace=False)
+        kb[0, g, rows] = kb[0, g, rows[0]]
+    c.k = W.Stored(W.BF16, kb)
+    for top_k in (700, 1500):
+        sel, out, lse = _run(c, top_k)
+        rs, ro, rl = _ref(c, top_k)
+        assert np.array_equal(sel, rs)
+        assert_attention_close(out, lse, ro, rl, np.ones(1, np.int32), W.BF16, "topk tie group")
+
+
 def test_topk_all_equal_scores_uses_exact_fallback():
     """Every key identical: more keys share the boundary bin than the sort
     buffer holds, so the exact radix path must pick the lowest indices."""
