@@ -199,34 +199,52 @@ __global__ __launch_bounds__(256) void hsr_gemm_kernel(HsrArgs a) {
 
 // Small-M path (M <= 8 rows, the per-draft-step case): the FC is a stream of
 // W (2*D*D bf16) through HBM.  Each wave owns RW consecutive output columns
-// (W rows) and walks them in 16-byte chunks with U chunks per row in flight,
-// so a lane keeps U*RW independent loads outstanding; X (M rows of [e;h]) is
-// staged once per workgroup in LDS.  Products of bf16 values are exact in
-// fp32; each lane accumulates its chunks and the wave reduces by shuffles.
-template <int MM, int RW, int U>
-__global__ __launch_bounds__(256) void hsr_gemv_kernel(HsrArgs a) {
+// (W rows) and requests U 16-byte chunks of each of them at once (for
+// D = 3584 that is the whole row pair), before it waits for anything: the
+// workgroup's X loads (M rows of [e;h]) go out first, so staging X in LDS
+// overlaps the W stream.  Products of bf16 values are exact in fp32; each
+// lane accumulates its chunks in order and the wave reduces by shuffles.
+template <int MM, int RW, int U, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void hsr_gemv_kernel(HsrArgs a) {
   extern __shared__ __align__(16) unsigned char xs[];   // [MM][Kd] bf16
+  constexpr int XPT = 4;                                 // X chunks per thread per pass
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int Kd = 2 * a.D, chunks = Kd / 8;
-  for (int e = tid; e < MM * chunks; e += blockDim.x) {
-    const int m = e / chunks, c = e - (e / chunks) * chunks;
-    u32x4_t v = {0, 0, 0, 0};
-    if (m < a.M) {
-      const int k = c * 8;
-      v = ld16((k < a.D) ? a.e + (size_t)m * a.D + k : a.h + (size_t)m * a.D + (k - a.D));
-    }
-    *reinterpret_cast<u32x4_t*>(xs + ((size_t)m * chunks + c) * 16) = v;
-  }
-  __syncthreads();
-  const int n0 = (blockIdx.x * 4 + wave) * RW;
-  if (n0 >= a.D) return;
+  const int n0 = (blockIdx.x * WAVES + wave) * RW;
+  const uint16_t* wr = a.w + (size_t)min(n0, a.D - 1) * Kd;
   float acc[RW][MM];
 #pragma unroll
   for (int r = 0; r < RW; ++r)
 #pragma unroll
     for (int m = 0; m < MM; ++m) acc[r][m] = 0.f;
-  const uint16_t* wr = a.w + (size_t)n0 * Kd;
-  for (int c0 = lane; c0 < chunks; c0 += 64 * U) {
+
+  for (int cb = 0, pass = 0; cb < chunks; cb += 64 * U, ++pass) {   // uniform trip count
+    const int c0 = cb + lane;
+    // X: MM*chunks chunks, XPT per thread per pass, loaded before W so the
+    // compiler's wait for them does not cover the W loads
+    u32x4_t xv[XPT];
+    const bool stage = (pass == 0);
+    const int xper = WAVES * 64 * XPT;
+    for (int e0 = 0; stage && e0 < MM * chunks; e0 += xper) {
+#pragma unroll
+      for (int k = 0; k < XPT; ++k) {
+        const int e = e0 + k * WAVES * 64 + tid;
+        const int m = e / chunks, c = e - (e / chunks) * chunks;
+        xv[k] = u32x4_t{0, 0, 0, 0};
+        if (e < MM * chunks && m < a.M) {
+          const int kk = c * 8;
+          xv[k] = ld16((kk < a.D) ? a.e + (size_t)m * a.D + kk
+                                  : a.h + (size_t)m * a.D + (kk - a.D));
+        }
+      }
+      if (e0 + xper < MM * chunks) {   // more X than one pass: store now
+#pragma unroll
+        for (int k = 0; k < XPT; ++k) {
+          const int e = e0 + k * WAVES * 64 + tid;
+          if (e < MM * chunks) *reinterpret_cast<u32x4_t*>(xs + (size_t)e * 16) = xv[k];
+        }
+      }
+    }
     u32x4_t wv[U][RW];
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -236,32 +254,43 @@ __global__ __launch_bounds__(256) void hsr_gemv_kernel(HsrArgs a) {
         wv[u][r] = (c < chunks && n0 + r < a.D) ? ld16(wr + (size_t)r * Kd + c * 8)
                                                  : u32x4_t{0, 0, 0, 0};
       }
+    if (stage) {
+      // the last X pass is still in registers
+      const int e0 = ((MM * chunks - 1) / xper) * xper;
+#pragma unroll
+      for (int k = 0; k < XPT; ++k) {
+        const int e = e0 + k * WAVES * 64 + tid;
+        if (e < MM * chunks) *reinterpret_cast<u32x4_t*>(xs + (size_t)e * 16) = xv[k];
+      }
+      __syncthreads();
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = c0 + 64 * u;
       if (c >= chunks) break;
 #pragma unroll
       for (int m = 0; m < MM; ++m) {
-        const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(xs + ((size_t)m * chunks + c) * 16);
+        const u32x4_t x = *reinterpret_cast<const u32x4_t*>(xs + ((size_t)m * chunks + c) * 16);
         float xf[8];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          xf[2 * j] = __uint_as_float(xv[j] << 16);
-          xf[2 * j + 1] = __uint_as_float(xv[j] & 0xFFFF0000u);
+          xf[2 * j] = __uint_as_float(x[j] << 16);
+          xf[2 * j + 1] = __uint_as_float(x[j] & 0xFFFF0000u);
         }
 #pragma unroll
         for (int r = 0; r < RW; ++r) {
-          float s = acc[r][m];
+          float sacc = acc[r][m];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            s = __builtin_fmaf(__uint_as_float(wv[u][r][j] << 16), xf[2 * j], s);
-            s = __builtin_fmaf(__uint_as_float(wv[u][r][j] & 0xFFFF0000u), xf[2 * j + 1], s);
+            sacc = __builtin_fmaf(__uint_as_float(wv[u][r][j] << 16), xf[2 * j], sacc);
+            sacc = __builtin_fmaf(__uint_as_float(wv[u][r][j] & 0xFFFF0000u), xf[2 * j + 1], sacc);
           }
-          acc[r][m] = s;
+          acc[r][m] = sacc;
         }
       }
     }
   }
+  if (n0 >= a.D) return;
 #pragma unroll
   for (int r = 0; r < RW; ++r)
 #pragma unroll
@@ -335,25 +364,25 @@ spec_status_t launch_hsr(const void* e, const void* h, const void* w, int m, int
     a.M = m;
     a.D = d_model;
     a.out_bf16 = out_bf16;
-    constexpr int RW = 4, U = 7;
-    const dim3 grid((d_model + 4 * RW - 1) / (4 * RW)), block(256);
+    constexpr int RW = 2, U = 14, WV = 8;
+    const dim3 grid((d_model + WV * RW - 1) / (WV * RW)), block(WV * 64);
     const int mm = (m <= 1) ? 1 : (m <= 2) ? 2 : (m <= 4) ? 4 : 8;
     const size_t lds = (size_t)mm * 4 * d_model;
     switch (mm) {
-      case 1: hipLaunchKernelGGL((hsr_gemv_kernel<1, RW, U>), grid, block, lds, stream, a); break;
-      case 2: hipLaunchKernelGGL((hsr_gemv_kernel<2, RW, U>), grid, block, lds, stream, a); break;
-      case 4: hipLaunchKernelGGL((hsr_gemv_kernel<4, RW, U>), grid, block, lds, stream, a); break;
+      case 1: hipLaunchKernelGGL((hsr_gemv_kernel<1, RW, U, WV>), grid, block, lds, stream, a); break;
+      case 2: hipLaunchKernelGGL((hsr_gemv_kernel<2, RW, U, WV>), grid, block, lds, stream, a); break;
+      case 4: hipLaunchKernelGGL((hsr_gemv_kernel<4, RW, U, WV>), grid, block, lds, stream, a); break;
       default: {
         // more than the default 64 KiB of dynamic LDS: raise the limit once
         static bool raised = false;
         if (!raised) {
-          if (hipFuncSetAttribute(reinterpret_cast<const void*>(&hsr_gemv_kernel<8, RW, U>),
+          if (hipFuncSetAttribute(reinterpret_cast<const void*>(&hsr_gemv_kernel<8, RW, U, WV>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize,
                                   8 * 4 * 5120) != hipSuccess)
             return SPEC_ERR_HIP;
           raised = true;
         }
-        hipLaunchKernelGGL((hsr_gemv_kernel<8, RW, U>), grid, block, lds, stream, a);
+        hipLaunchKernelGGL((hsr_gemv_kernel<8, RW, U, WV>), grid, block, lds, stream, a);
         break;
       }
     }
