@@ -7,8 +7,8 @@
 // whose maximum is "largest value, then lowest index" in any reduction order,
 // and merges it into its row with a 64-bit atomic max.  The last workgroup of
 // each sequence (arrival counter) turns the row maxima into target tokens,
-// counts the matching prefix and writes the outputs.  The maxima and counters
-// are cleared by a fill kernel at the start of every call.
+// counts the matching prefix and writes the outputs, and returns the maxima
+// and its counter to zero for the next call.
 #include "common.h"
 #include "internal.h"
 
@@ -17,6 +17,7 @@ namespace spec {
 namespace {
 
 constexpr int kAcceptThreads = 256;
+constexpr int kAccLoads = 4;      // 16-byte loads in flight per thread
 
 struct AcceptArgs {
   const void* logits;
@@ -43,81 +44,101 @@ __device__ __forceinline__ unsigned long long umax64(unsigned long long a, unsig
 
 template <bool BF16>
 __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(AcceptArgs a) {
+  constexpr int EPV = BF16 ? 8 : 4;                 // elements per 16-byte load
+  constexpr int SCALAR = kAccLoads * EPV;           // scalar loads per thread (ragged vocab)
   __shared__ unsigned long long red[kAcceptThreads / 64];
   __shared__ uint32_t s_tick;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = blockIdx.x / a.chunks;              // b * n_max + i
   const int ch = blockIdx.x - row * a.chunks;
-  const int b = row / a.n_max, i = row - b * a.n_max;
-  const int gam = a.gamma ? min(max(a.gamma[b], 0), a.n_max - 1) : a.n_max - 1;
+  const int b = row / a.n_max;
   const int v0 = ch * a.chunk, v1 = min(a.V, v0 + a.chunk);
+  // Every row is scanned (rows past gamma are ignored at the end), so the
+  // loads do not wait for gamma; all of a thread's loads are in flight at once.
   unsigned long long best = 0;
-  if (i <= gam) {
-    if (BF16) {
-      const uint16_t* p = reinterpret_cast<const uint16_t*>(a.logits) + (size_t)row * a.V;
-      if (a.vec) {
-        for (int v = v0 + 8 * threadIdx.x; v < v1; v += 8 * kAcceptThreads) {
-          const u32x4_t w = ld16(p + v);
+  if (a.vec) {
+    const unsigned char* p = reinterpret_cast<const unsigned char*>(a.logits) +
+                             (size_t)row * a.V * (BF16 ? 2 : 4);
+    u32x4_t w[kAccLoads];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            best = umax64(best, pack_key(__uint_as_float(w[j] << 16), v + 2 * j));
-            best = umax64(best, pack_key(__uint_as_float(w[j] & 0xFFFF0000u), v + 2 * j + 1));
+    for (int k = 0; k < kAccLoads; ++k) {
+      const int v = v0 + (k * kAcceptThreads + tid) * EPV;
+      w[k] = (v < v1) ? ld16(p + (size_t)v * (BF16 ? 2 : 4)) : u32x4_t{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int k = 0; k < kAccLoads; ++k) {
+      const int v = v0 + (k * kAcceptThreads + tid) * EPV;
+      if (v < v1) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (BF16) {
+            best = umax64(best, pack_key(__uint_as_float(w[k][j] << 16), v + 2 * j));
+            best = umax64(best, pack_key(__uint_as_float(w[k][j] & 0xFFFF0000u), v + 2 * j + 1));
+          } else {
+            best = umax64(best, pack_key(__uint_as_float(w[k][j]), v + j));
           }
         }
-      } else {
-        for (int v = v0 + threadIdx.x; v < v1; v += kAcceptThreads)
-          best = umax64(best, pack_key(bf16_bits_to_f32(p[v]), v));
       }
-    } else {
-      const float* p = reinterpret_cast<const float*>(a.logits) + (size_t)row * a.V;
-      if (a.vec) {
-        for (int v = v0 + 4 * threadIdx.x; v < v1; v += 4 * kAcceptThreads) {
-          const u32x4_t w = ld16(p + v);
+    }
+  } else {
+    float x[SCALAR];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) best = umax64(best, pack_key(__uint_as_float(w[j]), v + j));
-        }
-      } else {
-        for (int v = v0 + threadIdx.x; v < v1; v += kAcceptThreads)
-          best = umax64(best, pack_key(p[v], v));
+    for (int k = 0; k < SCALAR; ++k) {
+      const int v = v0 + k * kAcceptThreads + tid;
+      x[k] = 0.f;
+      if (v < v1) {
+        x[k] = BF16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(a.logits)[(size_t)row * a.V + v])
+                    : reinterpret_cast<const float*>(a.logits)[(size_t)row * a.V + v];
       }
     }
-    for (int o = 32; o > 0; o >>= 1) {
-      const unsigned long long other =
-          ((unsigned long long)(uint32_t)__shfl_xor((int)(best >> 32), o) << 32) |
-          (uint32_t)__shfl_xor((int)(uint32_t)best, o);
-      best = umax64(best, other);
-    }
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = best;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      unsigned long long m = red[0];
-      for (int w = 1; w < kAcceptThreads / 64; ++w) m = umax64(m, red[w]);
-      atomicMax(&a.best[row], m);
+#pragma unroll
+    for (int k = 0; k < SCALAR; ++k) {
+      const int v = v0 + k * kAcceptThreads + tid;
+      if (v < v1) best = umax64(best, pack_key(x[k], v));
     }
   }
-  // every workgroup of the sequence arrives, including rows past gamma
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned long long other =
+        ((unsigned long long)(uint32_t)__shfl_xor((int)(best >> 32), o) << 32) |
+        (uint32_t)__shfl_xor((int)(uint32_t)best, o);
+    best = umax64(best, other);
+  }
+  if (lane == 0) red[wave] = best;
+  __syncthreads();
   // The maxima are device-scope atomics, read back with atomic exchanges, so
   // no cache write-back is needed: thread 0 only waits for its own atomicMax
   // to complete before it arrives.
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
+    unsigned long long m = red[0];
+    for (int w = 1; w < kAcceptThreads / 64; ++w) m = umax64(m, red[w]);
+    atomicMax(&a.best[row], m);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     s_tick = atomicAdd(&a.tick[b], 1u);
   }
   __syncthreads();
-  if (s_tick != (uint32_t)(a.n_max * a.chunks - 1)) return;
-  if (threadIdx.x == 0) {
-    int n = -1, nxt = 0;
-    for (int r = 0; r < a.n_max; ++r) {
-      unsigned long long* slot = &a.best[(size_t)b * a.n_max + r];
-      const unsigned long long k = atomicExch(slot, 0ull);
-      const int t = (r <= gam) ? (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull)) : -1;
-      a.target_tok[(size_t)b * a.n_max + r] = t;
-      if (r <= gam && n < 0) {
-        if (r == gam || a.draft[(size_t)b * (a.n_max - 1) + r] != t) {
-          n = r;
-          nxt = t;
-        }
-      }
+  if (s_tick != (uint32_t)(a.n_max * a.chunks - 1) || wave != 0) return;
+  // Last arrival of sequence b: lane r takes row r (64 rows per round), so
+  // the maxima, the draft tokens and the outputs move in one round trip.
+  const int gam = a.gamma ? min(max(a.gamma[b], 0), a.n_max - 1) : a.n_max - 1;
+  int n = -1, nxt = 0;
+  for (int r0 = 0; r0 < a.n_max; r0 += 64) {
+    const int r = r0 + lane;
+    unsigned long long k = 0;
+    int d = -1;
+    if (r < a.n_max) {
+      k = atomicExch(&a.best[(size_t)b * a.n_max + r], 0ull);
+      if (r < gam) d = a.draft[(size_t)b * (a.n_max - 1) + r];
     }
+    const int t = (r <= gam) ? (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull)) : -1;
+    if (r < a.n_max) a.target_tok[(size_t)b * a.n_max + r] = t;
+    const unsigned long long stop = __builtin_amdgcn_ballot_w64(r <= gam && (r == gam || d != t));
+    if (n < 0 && stop) {
+      const int first = __ffsll((long long)stop) - 1;
+      n = r0 + first;
+      nxt = __shfl(t, first);
+    }
+  }
+  if (lane == 0) {
     a.accept_len[b] = n;
     a.next_tok[b] = nxt;
     a.tick[b] = 0u;
@@ -132,9 +153,8 @@ struct AcceptPlan {
 
 AcceptPlan plan_accept(int batch, int n_max, int vocab, bool bf16) {
   AcceptPlan p;
-  const int elems_per_thread = bf16 ? 128 : 64;     // 256 B of logits per thread
-  p.chunk = kAcceptThreads * elems_per_thread;
   const int vw = bf16 ? 8 : 4;
+  p.chunk = kAcceptThreads * kAccLoads * vw;        // 64 B of logits per thread
   p.vec = (vocab % vw == 0) ? 1 : 0;
   if (p.chunk > vocab) p.chunk = ((vocab + vw - 1) / vw) * vw;
   p.chunks = (vocab + p.chunk - 1) / p.chunk;
