@@ -81,15 +81,14 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(AcceptArgs a) {
       }
     }
   } else {
+    // unconditional loads from clamped indices (a guarded load becomes a
+    // branch with its own wait); out-of-range lanes are masked below
     float x[SCALAR];
 #pragma unroll
     for (int k = 0; k < SCALAR; ++k) {
-      const int v = v0 + k * kAcceptThreads + tid;
-      x[k] = 0.f;
-      if (v < v1) {
-        x[k] = BF16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(a.logits)[(size_t)row * a.V + v])
-                    : reinterpret_cast<const float*>(a.logits)[(size_t)row * a.V + v];
-      }
+      const size_t v = (size_t)row * a.V + min(v0 + k * kAcceptThreads + tid, v1 - 1);
+      x[k] = BF16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(a.logits)[v])
+                  : reinterpret_cast<const float*>(a.logits)[v];
     }
 #pragma unroll
     for (int k = 0; k < SCALAR; ++k) {

@@ -70,6 +70,7 @@ spec_status_t launch_attention(AttnArgs a, int d, int dtype, const AttnPlan& pla
 // Top-K: scores + selection into sel_idx, then attention via launch_attention.
 struct TopkPlan {
   size_t off_scores = 0;    // fp64 [U, max_len]
+  size_t off_key16 = 0;     // uint16 [U, max_len]
   size_t off_hist = 0;      // uint32 [U, 4096]
   bool hist_in_sync = false;  // histogram inside the sync region (no clearing launch)
   AttnPlan attn;            // offsets relative to the same workspace

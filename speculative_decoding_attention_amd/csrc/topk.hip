@@ -14,8 +14,9 @@
 //   of float(score): sign, exponent, 3 mantissa bits).
 // topk_select_kernel: one 1024-thread workgroup per unit.  From the
 //   histogram it finds the bin holding the K-th key.  One pass over the
-//   scores sets an LDS selection bit for every key above that bin and
-//   gathers the bin's keys as candidates.  A second 4096-bin histogram over
+//   16-bit float keys (also written by the score kernel) sets an LDS
+//   selection bit for every key above that bin and gathers the bin's keys as
+//   candidates, whose exact scores are then fetched.  A second 4096-bin histogram over
 //   the next 12 bits of the float key narrows the candidates to one sub-bin,
 //   whose few keys are ranked by counting; that fixes the exact threshold
 //   (score*, index*).  The winners' bits are set and the selected indices are
@@ -46,6 +47,7 @@ struct TopkArgs {
   int32_t max_pages, page_shift;
   int32_t B, Hq, Hkv, G, max_len, top_k;
   double* scores;       // [U, max_len]
+  uint16_t* key16;      // [U, max_len] top 16 bits of the ordered float key
   uint32_t* hist;       // [U, kHistBins]
   int32_t* sel_idx;     // [U, top_k]
 };
@@ -66,13 +68,18 @@ __device__ __forceinline__ uint64_t order_key64(double x) {
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
-__device__ __forceinline__ uint32_t coarse_bin(double x) {
-  float f = (float)x;                   // round to nearest: monotone non-decreasing
+// Order-preserving 32-bit key of float(score) (round to nearest: monotone
+// non-decreasing in the score); -0 is folded onto +0.
+__device__ __forceinline__ uint32_t fine_key32(double x) {
+  float f = (float)x;
   if (f == 0.f) f = 0.f;
   const uint32_t u = __float_as_uint(f);
-  const uint32_t k = (u >> 31) ? ~u : (u | 0x80000000u);
-  return k >> 20;
+  return (u >> 31) ? ~u : (u | 0x80000000u);
 }
+
+// Coarse histogram bin: the top 12 bits of that key (sign, exponent, 3
+// mantissa bits).
+__device__ __forceinline__ uint32_t coarse_bin(double x) { return fine_key32(x) >> 20; }
 
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void topk_score_kernel(TopkArgs a) {
@@ -80,7 +87,9 @@ __global__ __launch_bounds__(256) void topk_score_kernel(TopkArgs a) {
   constexpr int PITCH = ROW_B + 8;                  // padded LDS pitch
   __shared__ __align__(16) unsigned char krows[kScoreKeys * PITCH];
   __shared__ double qbar[D];
-  __shared__ uint32_t hist[kHistBins];
+  // two 16-bit bin counters per word (a tile has at most 256 keys), so the
+  // workgroup fits twice per CU's LDS
+  __shared__ uint32_t hist[kHistBins / 2];
   __shared__ size_t rowidx[kScoreKeys];
 
   const int tiles = (a.max_len + kScoreKeys - 1) / kScoreKeys;
@@ -91,7 +100,7 @@ __global__ __launch_bounds__(256) void topk_score_kernel(TopkArgs a) {
   if (j0 >= L) return;
   const int nk = min(kScoreKeys, L - j0);
 
-  for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) hist[i] = 0;
+  for (int i = threadIdx.x; i < kHistBins / 2; i += blockDim.x) hist[i] = 0;
   if (threadIdx.x < D) {
     double s = 0.0;
     for (int h = g * a.G; h < (g + 1) * a.G; ++h) {
@@ -154,12 +163,15 @@ __global__ __launch_bounds__(256) void topk_score_kernel(TopkArgs a) {
       }
     }
     a.scores[(size_t)u * a.max_len + j0 + key] = acc;
-    atomicAdd(&hist[coarse_bin(acc)], 1u);
+    const uint32_t k32 = fine_key32(acc);
+    a.key16[(size_t)u * a.max_len + j0 + key] = (uint16_t)(k32 >> 16);
+    const uint32_t bin = k32 >> 20;
+    atomicAdd(&hist[bin >> 1], (bin & 1u) ? 0x10000u : 1u);
   }
   __syncthreads();
   uint32_t* gh = a.hist + (size_t)u * kHistBins;
   for (int i = threadIdx.x; i < kHistBins; i += blockDim.x)
-    if (hist[i]) atomicAdd(&gh[i], hist[i]);
+    if (const uint32_t c = (hist[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) atomicAdd(&gh[i], c);
 }
 
 // Block-wide exclusive prefix sum of one value per thread (1024 threads).
@@ -197,14 +209,6 @@ __device__ __forceinline__ bool cand_before(uint64_t ka, int ia, uint64_t kb, in
 __device__ __forceinline__ double key64_to_double(uint64_t k) {
   const uint64_t u = (k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k;
   return __longlong_as_double((long long)u);
-}
-
-// Order-preserving 32-bit key of float(score); coarse_bin is its top 12 bits.
-__device__ __forceinline__ uint32_t fine_key32(double x) {
-  float f = (float)x;
-  if (f == 0.f) f = 0.f;
-  const uint32_t u = __float_as_uint(f);
-  return (u >> 31) ? ~u : (u | 0x80000000u);
 }
 
 constexpr int kMaskKeys = 131072;   // keys whose selection bits fit LDS
@@ -265,44 +269,48 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(TopkArgs a) {
   }
   if (tid == 0) s_ncand = 0;
   __syncthreads();
-  for (int i = tid; i < kHistBins; i += nt) gh[i] = 0;   // leave the histogram clean
   const uint32_t bstar = s_bin;
   int need = K - (int)s_above;                           // 1..count(bstar)
 
-  // (b) one pass over the scores, kSelBatch per thread in flight: keys above
-  //     the boundary bin set their selection bit (a wave's ballot covers 64
-  //     consecutive keys), keys in it are appended to the candidate list
+  // (b) one pass over the 16-bit keys (a quarter of the score bytes; one
+  //     workgroup streams them all), kSelBatch per thread in flight: keys
+  //     above the boundary bin set their selection bit (a wave's ballot
+  //     covers 64 consecutive keys), keys in it join the candidate list
+  const uint16_t* k16 = a.key16 + (size_t)u * a.max_len;
   for (int j0 = 0; j0 < L; j0 += nt * kSelBatch) {
-    double sv[kSelBatch];
+    uint32_t kv[kSelBatch];
+    // unconditional loads from clamped indices: a guarded load would be
+    // compiled as a branch with its own wait, one round trip per key
+#pragma unroll
+    for (int k = 0; k < kSelBatch; ++k) kv[k] = k16[min(j0 + k * nt + tid, L - 1)];
+    // ballots first, then one LDS reservation per wave for the whole batch
+    uint64_t bcs[kSelBatch];
+    uint32_t wtotal = 0;
 #pragma unroll
     for (int k = 0; k < kSelBatch; ++k) {
       const int j = j0 + k * nt + tid;
-      sv[k] = (j < L) ? sc[j] : 0.0;
-    }
-#pragma unroll
-    for (int k = 0; k < kSelBatch; ++k) {
-      const int j = j0 + k * nt + tid;
-      const uint32_t cb = coarse_bin(sv[k]);
-      const bool above = j < L && cb > bstar;
-      const bool cand = j < L && cb == bstar;
-      const uint64_t ba = __builtin_amdgcn_ballot_w64(above);
-      const uint64_t bc = __builtin_amdgcn_ballot_w64(cand);
+      const uint32_t cb = kv[k] >> 4;
+      const uint64_t ba = __builtin_amdgcn_ballot_w64(j < L && cb > bstar);
+      bcs[k] = __builtin_amdgcn_ballot_w64(j < L && cb == bstar);
+      wtotal += (uint32_t)__popcll(bcs[k]);
       if (use_mask && lane == 0) {
         const int w = (j0 + k * nt + wave * 64) >> 5;   // 64-aligned run of keys
         selmask[w] = (uint32_t)ba;
         selmask[w + 1] = (uint32_t)(ba >> 32);
       }
-      if (bc) {
-        uint32_t wbase = 0;
-        if (lane == 0) wbase = atomicAdd(&s_ncand, (uint32_t)__popcll(bc));
-        wbase = __shfl(wbase, 0);
-        if (cand) {
-          const uint32_t pos = wbase + (uint32_t)__popcll(bc & ((1ull << lane) - 1ull));
-          if (pos < (uint32_t)kCandMax) {
-            ckey[pos] = order_key64(sv[k]);
-            cidx[pos] = j;
-          }
+    }
+    if (wtotal) {
+      uint32_t wbase = 0;
+      if (lane == 0) wbase = atomicAdd(&s_ncand, wtotal);
+      wbase = __shfl(wbase, 0);
+      const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+      for (int k = 0; k < kSelBatch; ++k) {
+        if ((bcs[k] >> lane) & 1ull) {
+          const uint32_t pos = wbase + (uint32_t)__popcll(bcs[k] & below);
+          if (pos < (uint32_t)kCandMax) cidx[pos] = j0 + k * nt + tid;
         }
+        wbase += (uint32_t)__popcll(bcs[k]);
       }
     }
   }
@@ -310,6 +318,10 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(TopkArgs a) {
   if (tid == 0) s_nsmall = 0;
   __syncthreads();
   const uint32_t ncand = s_ncand;
+  if (ncand <= (uint32_t)kCandMax) {   // the candidates' exact scores, in one gather
+    for (uint32_t i = tid; i < ncand; i += nt) ckey[i] = order_key64(sc[cidx[i]]);
+    __syncthreads();
+  }
 
   if (ncand <= (uint32_t)kCandMax) {
     need = max(1, min(need, (int)max(ncand, 1u)));        // guards a corrupted histogram
@@ -475,7 +487,7 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(TopkArgs a) {
       const int jl = r0 + tid * 32;
       double sv[32];
 #pragma unroll
-      for (int k = 0; k < 32; ++k) sv[k] = (jl + k < L) ? sc[jl + k] : 0.0;
+      for (int k = 0; k < 32; ++k) sv[k] = sc[min(jl + k, L - 1)];   // clamped, unconditional
       uint32_t mask = 0;
 #pragma unroll
       for (int k = 0; k < 32; ++k) {
@@ -495,6 +507,8 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(TopkArgs a) {
     }
   }
   for (int j = K - 1 - tid; j >= (int)base; j -= nt) out[j] = -1;   // base == K here
+  // leave the histogram clean (last: stores count against the loads' waits)
+  for (int i = tid; i < kHistBins; i += nt) gh[i] = 0;
 }
 
 }  // namespace
@@ -504,7 +518,8 @@ TopkPlan plan_topk(int units, int max_len, int top_k, int rows, int d) {
   const size_t hist_bytes = (size_t)units * kHistBins * sizeof(uint32_t);
   p.hist_in_sync = hist_bytes <= kSyncBytes;
   p.off_scores = kSyncBytes;
-  size_t end = align_up(p.off_scores + (size_t)units * max_len * sizeof(double), 256);
+  p.off_key16 = align_up(p.off_scores + (size_t)units * max_len * sizeof(double), 256);
+  size_t end = align_up(p.off_key16 + (size_t)units * max_len * sizeof(uint16_t), 256);
   if (p.hist_in_sync) {
     p.off_hist = 0;
   } else {
@@ -534,6 +549,7 @@ spec_status_t launch_topk_select(const AttnArgs& aa, int d, int dtype, int top_k
   a.top_k = top_k;
   char* w = reinterpret_cast<char*>(ws);
   a.scores = reinterpret_cast<double*>(w + plan.off_scores);
+  a.key16 = reinterpret_cast<uint16_t*>(w + plan.off_key16);
   a.hist = reinterpret_cast<uint32_t*>(w + plan.off_hist);
   a.sel_idx = sel_idx;
   const int units = a.B * a.Hkv;
