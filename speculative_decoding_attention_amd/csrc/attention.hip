@@ -534,8 +534,9 @@ __device__ __forceinline__ void pipe_finish(const AttnArgs& a, float* smem, int 
                                             f32x4_t (&acc)[8]) {
   constexpr int D = 128, RP = NB * 16, DP = D + 4;
   constexpr int KP = PipeCfg<NB>::KP;
-  float* macc = smem;                 // [RP][DP]
-  float* mm = macc + RP * DP;         // [KP][RP]
+  constexpr int PARK = (KP > 1) ? KP - 1 : 1;
+  float* macc = smem;                 // [PARK][RP][DP] parked accumulators of phases 1..KP-1
+  float* mm = macc + PARK * RP * DP;  // [KP][RP]
   float* ml = mm + KP * RP;
   float* mr = ml + KP * RP;
   float* mrow = mr + KP * RP;         // [3][RP]
@@ -569,45 +570,57 @@ __device__ __forceinline__ void pipe_finish(const AttnArgs& a, float* smem, int 
     const float M = mrow[nb * 16 + r16];
     f = exp2f(m_run - ((M == -INFINITY) ? 0.f : M));
   }
-  for (int k = 0; k < KP; ++k) {
-    if (active && p == k) {
+  // Phases p >= 1 park their rescaled accumulators in LDS; phase 0 adds them
+  // in phase order and writes straight from registers: lane (r16, q4) of
+  // block db holds 4 consecutive d of row nb*16 + r16, one 16-byte store.
+  const int n = nb * 16 + r16;
+  if (active && p > 0) {
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+      *reinterpret_cast<f32x4_t*>(macc + ((p - 1) * RP + n) * DP + db * 16 + 4 * q4) = acc[db] * f;
+  }
+  __syncthreads();
+  const int R = a.R;
+  if (active && p == 0 && n < R) {
+    f32x4_t o[8];
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      o[db] = acc[db] * f;
+#pragma unroll
+      for (int k = 1; k < KP; ++k)
+        o[db] += *reinterpret_cast<const f32x4_t*>(macc + ((k - 1) * RP + n) * DP + db * 16 + 4 * q4);
+    }
+    if (a.S == 1) {
+      const int i = n / a.G, hh = n - i * a.G;
+      const float Ls = mrow[RP + n], Lr = mrow[2 * RP + n];
+      const bool live = (i < nq) && (Ls > 0.f);
+      const size_t ob = (((size_t)b * a.n_max + i) * a.Hq + g * a.G + hh) * D;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        f32x4_t v = o[db];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = live ? v[e] / Lr : 0.f;
+        const size_t oi = ob + db * 16 + 4 * q4;
+        if (a.out_bf16) {
+          const uint32_t lo = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+          const uint32_t hi = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + oi) = make_uint2(lo, hi);
+        } else {
+          *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.out) + oi) = v;
+        }
+      }
+      if (a.lse && q4 == 0)
+        a.lse[((size_t)b * a.n_max + i) * a.Hq + g * a.G + hh] =
+            live ? (mrow[n] + log2f(Ls)) * 0.69314718055994531f : -INFINITY;
+    } else {
+      float* pa = a.part_acc + ((size_t)u * a.S + s) * R * D + (size_t)n * D;
 #pragma unroll
       for (int db = 0; db < 8; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int idx = (nb * 16 + r16) * DP + db * 16 + q4 * 4 + i;
-          const float val = acc[db][i] * f;
-          macc[idx] = (k == 0) ? val : macc[idx] + val;
-        }
+        *reinterpret_cast<f32x4_t*>(pa + db * 16 + 4 * q4) = o[db];
     }
-    __syncthreads();
   }
-  const int R = a.R;
-  if (a.S == 1) {
-    const int Hq = a.Hq, G = a.G;
-    for (int e = threadIdx.x; e < R * D; e += blockDim.x) {
-      const int r = e / D, d = e - r * D;
-      const int i = r / G, hh = r - i * G;
-      const float Ls = mrow[RP + r], Lr = mrow[2 * RP + r];
-      const bool live = (i < nq) && (Ls > 0.f);
-      const float o = live ? macc[r * DP + d] / Lr : 0.f;
-      const size_t oi = (((size_t)b * a.n_max + i) * Hq + g * G + hh) * D + d;
-      if (a.out_bf16)
-        reinterpret_cast<uint16_t*>(a.out)[oi] = (uint16_t)f32_to_bf16_bits(o);
-      else
-        reinterpret_cast<float*>(a.out)[oi] = o;
-      if (a.lse && d == 0)
-        a.lse[((size_t)b * a.n_max + i) * Hq + g * G + hh] =
-            live ? (mrow[r] + log2f(Ls)) * 0.69314718055994531f : -INFINITY;
-    }
-  } else {
-    const size_t base = (size_t)u * a.S + s;
-    float* pa = a.part_acc + base * R * D;
-    for (int e = threadIdx.x; e < R * D; e += blockDim.x) {
-      const int r = e / D, d = e - r * D;
-      pa[e] = macc[r * DP + d];
-    }
-    float* pm = a.part_ml + base * 3 * R;
+  if (a.S > 1) {
+    float* pm = a.part_ml + ((size_t)u * a.S + s) * 3 * R;
     for (int r = threadIdx.x; r < R; r += blockDim.x) {
       pm[r] = mrow[r];
       pm[R + r] = mrow[RP + r];
@@ -642,7 +655,9 @@ __global__ __launch_bounds__(PipeCfg<NB>::WAVES * 64, 1) void attn_bf16_pipe_ker
   __shared__ __align__(16) unsigned char ring[C::RING_BYTES];
   __shared__ int s_pos[GATHER ? kMaxChunk : 1];
   __shared__ uint32_t s_row[GATHER ? kMaxChunk : 1];
-  static_assert((NB * 16) * (D + 4) * 4 + 7 * C::KP * NB * 16 * 4 <= C::RING_BYTES, "merge fits");
+  static_assert(((C::KP > 1) ? C::KP - 1 : 1) * (NB * 16) * (D + 4) * 4 + 7 * C::KP * NB * 16 * 4 <=
+                    C::RING_BYTES,
+                "epilogue fits the ring");
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, q4 = lane >> 4;
