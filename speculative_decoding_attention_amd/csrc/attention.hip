@@ -276,7 +276,8 @@ __device__ __forceinline__ void bf16_load_v(const AttnArgs& a, const SlotMap<GAT
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int slot = t0 + 8 * q4 + 4 * kb + i;
-      T.kpos[kb][i] = (slot < t_end) ? sm.position(slot) : 0x7fffffff;
+      const int pos = sm.position(min(slot, t_end - 1));   // unconditional read, no branch
+      T.kpos[kb][i] = (slot < t_end) ? pos : 0x7fffffff;
     }
 }
 
@@ -512,6 +513,10 @@ __device__ __forceinline__ void pipe_issue_tile(const AttnArgs& a, const SlotMap
   using C = PipeCfg<NB>;
   const unsigned char* kg = reinterpret_cast<const unsigned char*>(a.k);
   const unsigned char* vg = reinterpret_cast<const unsigned char*>(a.v);
+  // All source addresses first: a gathered row comes from LDS, and each DMA
+  // statement is a compiler memory barrier, so resolving rows between them
+  // would cost one LDS round trip per instruction.
+  const unsigned char* src[C::PER_WAVE];
 #pragma unroll
   for (int jj = 0; jj < C::PER_WAVE; ++jj) {
     const int j = wave + C::WAVES * jj;          // DMA instruction index within the tile
@@ -520,8 +525,13 @@ __device__ __forceinline__ void pipe_issue_tile(const AttnArgs& a, const SlotMap
     int slot = tile_start + 32 * p + key;
     slot = slot < t_end ? slot : t_end - 1;      // past the end: any valid row (masked later)
     const uint32_t chunk = (uint32_t)(lane & 15) ^ swz((uint32_t)key);
-    const unsigned char* src = (kind ? vg : kg) + (size_t)sm.rowof(slot) * 256 + chunk * 16;
-    dma16(src, slot_lds + (uint32_t)((2 * p + kind) * C::SUB_BYTES + grp * 1024));
+    src[jj] = (kind ? vg : kg) + (size_t)sm.rowof(slot) * 256 + chunk * 16;
+  }
+#pragma unroll
+  for (int jj = 0; jj < C::PER_WAVE; ++jj) {
+    const int j = wave + C::WAVES * jj;
+    const int p = j >> 4, kind = (j >> 3) & 1, grp = j & 7;
+    dma16(src[jj], slot_lds + (uint32_t)((2 * p + kind) * C::SUB_BYTES + grp * 1024));
   }
 }
 
@@ -757,7 +767,9 @@ __global__ __launch_bounds__(PipeCfg<NB>::WAVES * 64, 1) void attn_bf16_pipe_ker
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int slot = sub0 + 16 * kb + 4 * q4 + i;
-          const bool vis = slot < t_end && sm.position(min(slot, t_end - 1)) <= rowP;
+          // no short circuit: a guarded LDS read becomes a branch with its own wait
+          const int pos = sm.position(min(slot, t_end - 1));
+          const bool vis = (slot < t_end) & (pos <= rowP);
           sc[kb][i] = vis ? sc[kb][i] : -INFINITY;
         }
     }
@@ -924,7 +936,8 @@ __global__ __launch_bounds__(256, 1) void attn_f32_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int slot = t0 + 16 * kb + 4 * q4 + i;
-        kpos[kb][i] = (slot < t_end) ? sm.position(slot) : 0x7fffffff;
+        const int pos = sm.position(min(slot, t_end - 1));   // unconditional read, no branch
+        kpos[kb][i] = (slot < t_end) ? pos : 0x7fffffff;
       }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
