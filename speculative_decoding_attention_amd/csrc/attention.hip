@@ -454,38 +454,8 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
 
 __device__ __forceinline__ uint32_t swz(uint32_t r) { return ((r & 7u) << 1) ^ ((r >> 3) & 1u); }
 
-// One 1 KB DMA: each lane copies 16 bytes from its own address g to LDS at
-// lds_byte_addr + 16*lane.  The LDS base goes through M0, which is set in the
-// same statement; no code of this library keeps a value in M0.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds_byte_addr) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_byte_addr);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(g), "s"(base) : "memory");
-}
-
-// Waits until at most N of this wave's DMA loads are outstanding, then a
-// workgroup barrier; acts as a compiler memory barrier for LDS accesses.
-template <int N>
-__device__ __forceinline__ void wait_dma_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" :: "n"(N) : "memory");
-}
-
-template <int PER_WAVE>
-__device__ __forceinline__ void wait_tiles_barrier(int later_tiles) {
-  switch (later_tiles) {
-    case 0: wait_dma_barrier<0>(); break;
-    case 1: wait_dma_barrier<PER_WAVE * 1>(); break;
-    case 2: wait_dma_barrier<PER_WAVE * 2>(); break;
-    case 3: wait_dma_barrier<PER_WAVE * 3>(); break;
-    case 4: wait_dma_barrier<PER_WAVE * 4>(); break;
-    case 5: wait_dma_barrier<PER_WAVE * 5>(); break;
-    default: wait_dma_barrier<PER_WAVE * 6>(); break;
-  }
-}
-
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
-typedef __attribute__((address_space(3))) unsigned char lds_u8_t;
 
 template <int NB>
 struct PipeCfg {

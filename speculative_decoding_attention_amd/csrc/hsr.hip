@@ -1,16 +1,21 @@
-// Hidden-state-reuse fusion FC on the gfx950 matrix cores:
+// Hidden-state-reuse fusion FC on gfx950:
 //   Y[M, D] = X[M, 2D] W^T,  X[r] = concat(E[r], H[r]),  W [D, 2D] bf16.
-// The concatenation is never materialised: the A-operand loader reads
-// columns k < D from E and k >= D from H.
+// The concatenation is never materialised: loaders read columns k < D from E
+// and k >= D from H.
 //
-// Tiling.  A workgroup (4 waves) owns a BM x BN output tile (BM = 16*MF
-// rows, BN = 4 waves x 16*WNF columns) and a K-slice; split-K slices are
-// summed by the last workgroup of each tile in split order, so results are
-// bitwise reproducible.  Per 128-wide K block, the X rows of the tile are
-// staged in LDS (shared by the 4 waves); each wave streams its own W rows
-// straight from HBM into registers (W is read exactly once per M band and
-// is the dominant byte stream), one block ahead of the MFMAs
-// (v_mfma_f32_16x16x32_bf16; A = X rows, B = W rows, both K-contiguous).
+// Large M (the batched draft step): a tiled GEMM on the matrix cores
+// (v_mfma_f32_16x16x32_bf16, fp32 accumulation).  A workgroup owns a BM x BN
+// output tile (BM = 32*MT rows of X, BN = 32*NT rows of W) and a K range;
+// its 4 waves form a 2 x 2 grid of (16*MT) x (16*NT) blocks.  K advances in
+// 64-wide steps whose X and W slabs (BM and BN rows of 128 bytes) move from
+// HBM to LDS by DMA into a ring of NS stages, so data in flight costs no
+// registers.  Each 128-byte row keeps its 16-byte chunk c at slot
+// c ^ (row & 7): the fragment reads (16 rows x one chunk per lane group) then
+// spread over the LDS banks.  Split-K partials are summed by the last
+// workgroup of each tile in split order, so results are bitwise
+// reproducible.
+//
+// Small M (one draft token at a time): a stream of W through HBM, below.
 #include <string.h>
 
 #include "common.h"
@@ -20,8 +25,8 @@ namespace spec {
 
 namespace {
 
-constexpr int kBK = 128;          // K block staged per iteration
-constexpr int kAP = kBK * 2 + 16;  // LDS pitch (bytes) of one staged X row
+constexpr int kGemmBK = 64;                // K per step (128 bytes of a row)
+constexpr int kGemmRing = 128 * 1024;      // LDS ring bytes
 
 struct HsrArgs {
   const uint16_t* e;
@@ -31,171 +36,177 @@ struct HsrArgs {
   float* part;       // [S, M, D] split-K partials (S > 1)
   uint32_t* tick;    // [tiles] arrival counters (S > 1), in the sync region
   int32_t M, D, out_bf16;
-  int32_t tiles_m, tiles_n, S, k_slice;
+  int32_t tiles_m, tiles_n, S, ksteps;
 };
 
-template <int MF>
-__device__ __forceinline__ void load_a_block(const HsrArgs& a, int m0, int k0, u32x4_t (&ra)[3],
-                                             int tid) {
-  // MF*16 rows x 128 k = MF*16*16 chunks of 16 B; 256 threads -> <= 3 chunks each (MF <= 3)
+template <int MT, int NT>
+struct GemmCfg {
+  static constexpr int BM = 32 * MT, BN = 32 * NT;
+  static constexpr int STAGE = (BM + BN) * 128;          // bytes of one K step
+  static constexpr int NS = kGemmRing / STAGE;           // ring depth
+  static constexpr int INSTR = STAGE / 1024;             // 1 KB DMAs per step
+  static constexpr int PER_WAVE = INSTR / 4;
+  static_assert(INSTR % 4 == 0 && NS >= 3 && NS - 2 <= 6, "ring shape");
+  static_assert(PER_WAVE * (NS - 2) <= 63, "vmcnt range");
+};
+
+// DMA of K step `ks` (columns 64*ks..) of the tile's X rows m0.. and W rows
+// n0.. into one ring stage.  Instruction j moves 8 rows of 128 bytes; X rows
+// past M repeat row M-1 (their outputs are never stored).
+template <int MT, int NT>
+__device__ __forceinline__ void gemm_issue(const HsrArgs& a, int m0, int n0, int ks,
+                                           uint32_t stage_lds, int wave, int lane) {
+  using C = GemmCfg<MT, NT>;
+  const int k0 = ks * kGemmBK;
+  const int sub = lane >> 3, slot = lane & 7;
+  const unsigned char* src[C::PER_WAVE];
 #pragma unroll
-  for (int c = 0; c < 3; ++c) {
-    const int e = tid + c * 256;
-    if (e < MF * 16 * 16) {
-      const int r = e >> 4, ch = e & 15;
-      const int row = m0 + r, k = k0 + ch * 8;
-      if (row < a.M) {
-        const uint16_t* src = (k < a.D) ? a.e + (size_t)row * a.D + k
-                                        : a.h + (size_t)row * a.D + (k - a.D);
-        ra[c] = ld16(src);
-      } else {
-        ra[c] = u32x4_t{0, 0, 0, 0};
-      }
+  for (int jj = 0; jj < C::PER_WAVE; ++jj) {
+    const int j = wave + 4 * jj;
+    const int row = 8 * (j < C::BM / 8 ? j : j - C::BM / 8) + sub;
+    const int chunk = slot ^ (row & 7);
+    const int k = k0 + 8 * chunk;
+    if (j < C::BM / 8) {
+      const int m = min(m0 + row, a.M - 1);
+      const uint16_t* xr = (k0 < a.D) ? a.e + (size_t)m * a.D + k : a.h + (size_t)m * a.D + (k - a.D);
+      src[jj] = reinterpret_cast<const unsigned char*>(xr);
+    } else {
+      src[jj] = reinterpret_cast<const unsigned char*>(a.w + (size_t)(n0 + row) * (2 * a.D) + k);
     }
   }
-}
-
-template <int MF>
-__device__ __forceinline__ void store_a_block(unsigned char* buf, const u32x4_t (&ra)[3], int tid) {
 #pragma unroll
-  for (int c = 0; c < 3; ++c) {
-    const int e = tid + c * 256;
-    if (e < MF * 16 * 16) {
-      const int r = e >> 4, ch = e & 15;
-      *reinterpret_cast<u32x4_t*>(buf + r * kAP + ch * 16) = ra[c];
-    }
-  }
+  for (int jj = 0; jj < C::PER_WAVE; ++jj)
+    dma16(src[jj], stage_lds + (uint32_t)((wave + 4 * jj) * 1024));
 }
 
-template <int MF, int WNF>
-__global__ __launch_bounds__(256) void hsr_gemm_kernel(HsrArgs a) {
-  static_assert(MF * 16 * 16 <= 768, "A block must fit 3 chunks per thread");
-  __shared__ __align__(16) unsigned char abuf[2][MF * 16 * kAP];
+template <int MT, int NT>
+__global__ __launch_bounds__(256, 1) void hsr_mfma_kernel(HsrArgs a) {
+  using C = GemmCfg<MT, NT>;
+  __shared__ __align__(16) unsigned char ring[kGemmRing];
   __shared__ uint32_t s_tick;
-
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, q4 = lane >> 4;
-  // work item = (tile_n, split, tile_m): neighbours share W columns -> same XCD
+  const int wm = wave & 1, wn = wave >> 1;
+  // work item = (tile_n, split, tile_m): the tile_m neighbours share the W
+  // slab of the same K range and land on the same XCD
   const int item = xcd_remap(blockIdx.x, gridDim.x);
   const int tm = item % a.tiles_m;
   const int rest = item / a.tiles_m;
   const int sk = rest % a.S;
   const int tn = rest / a.S;
-  const int m0 = tm * MF * 16;
-  const int n0 = tn * (4 * WNF * 16) + wave * WNF * 16;
-  const int kb0 = sk * a.k_slice, kb1 = kb0 + a.k_slice;
-  const int Kd = 2 * a.D;
+  const int m0 = tm * C::BM, n0 = tn * C::BN;
+  const int ks0 = (int)(((long)sk * a.ksteps) / a.S), ks1 = (int)(((long)(sk + 1) * a.ksteps) / a.S);
+  const int nsteps = ks1 - ks0;
 
-  f32x4_t acc[MF][WNF];
-#pragma unroll
-  for (int mf = 0; mf < MF; ++mf)
-#pragma unroll
-    for (int wn = 0; wn < WNF; ++wn) acc[mf][wn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  lds_u8_t* const ring_l = (lds_u8_t*)ring;
+  const uint32_t ring_lds = (uint32_t)(size_t)ring_l;
+  for (int j = 0; j < C::NS - 1 && j < nsteps; ++j)
+    gemm_issue<MT, NT>(a, m0, n0, ks0 + j, ring_lds + (uint32_t)(j * C::STAGE), wave, lane);
 
-  // W rows of this lane: column n0 + 16*wn + r16, k offset 8*q4 within a 32-step
-  const uint16_t* wrow[WNF];
+  f32x4_t acc[MT][NT];
 #pragma unroll
-  for (int wn = 0; wn < WNF; ++wn) wrow[wn] = a.w + (size_t)(n0 + 16 * wn + r16) * Kd + 8 * q4;
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  u32x4_t ra[3];
-  u32x4_t wb[2][kBK / 32][WNF];
-  load_a_block<MF>(a, m0, kb0, ra, tid);
+  for (int t = 0; t < nsteps; ++t) {
+    wait_tiles_barrier<C::PER_WAVE>(min(C::NS - 2, nsteps - 1 - t));
+    if (t + C::NS - 1 < nsteps)
+      gemm_issue<MT, NT>(a, m0, n0, ks0 + t + C::NS - 1,
+                         ring_lds + (uint32_t)(((t + C::NS - 1) % C::NS) * C::STAGE), wave, lane);
+    const unsigned char* st = ring + (t % C::NS) * C::STAGE;
 #pragma unroll
-  for (int s = 0; s < kBK / 32; ++s)
+    for (int kk = 0; kk < 2; ++kk) {            // two 32-wide k steps of the MFMA
+      const int c = 4 * kk + q4;
+      bf16x8_t af[MT], bfr[NT];
 #pragma unroll
-    for (int wn = 0; wn < WNF; ++wn) wb[0][s][wn] = ld16(wrow[wn] + kb0 + 32 * s);
-  store_a_block<MF>(abuf[0], ra, tid);
-  __syncthreads();
-
-  int cur = 0;
-  for (int k0 = kb0; k0 < kb1; k0 += kBK) {
-    const int kn = k0 + kBK;
-    const bool more = kn < kb1;
-    if (more) {
-      load_a_block<MF>(a, m0, kn, ra, tid);
-#pragma unroll
-      for (int s = 0; s < kBK / 32; ++s)
-#pragma unroll
-        for (int wn = 0; wn < WNF; ++wn) wb[cur ^ 1][s][wn] = ld16(wrow[wn] + kn + 32 * s);
-    }
-    const unsigned char* ab = abuf[cur];
-#pragma unroll
-    for (int s = 0; s < kBK / 32; ++s) {
-#pragma unroll
-      for (int mf = 0; mf < MF; ++mf) {
-        const u32x4_t av =
-            *reinterpret_cast<const u32x4_t*>(ab + (mf * 16 + r16) * kAP + (32 * s + 8 * q4) * 2);
-#pragma unroll
-        for (int wn = 0; wn < WNF; ++wn)
-          acc[mf][wn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av),
-                                                                as_bf16x8(wb[cur][s][wn]),
-                                                                acc[mf][wn], 0, 0, 0);
+      for (int mt = 0; mt < MT; ++mt) {
+        const int row = wm * 16 * MT + 16 * mt + r16;
+        af[mt] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(st + row * 128 + ((c ^ (row & 7)) * 16)));
       }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int row = wn * 16 * NT + 16 * nt + r16;
+        bfr[nt] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(st + C::BM * 128 + row * 128 +
+                                                                 ((c ^ (row & 7)) * 16)));
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bfr[nt], acc[mt][nt], 0, 0, 0);
     }
-    if (more) store_a_block<MF>(abuf[cur ^ 1], ra, tid);
-    __syncthreads();
-    cur ^= 1;
   }
 
-  // acc[mf][wn][i] = Y[m0 + 16*mf + 4*q4 + i][n0 + 16*wn + r16]
+  // lane (r16, q4) of block (mt, nt) holds rows 4*q4+i, column r16
+  const int rb = m0 + wm * 16 * MT + 4 * q4, cb = n0 + wn * 16 * NT + r16;
   if (a.S == 1) {
 #pragma unroll
-    for (int mf = 0; mf < MF; ++mf)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = m0 + 16 * mf + 4 * q4 + i;
-        if (row >= a.M) continue;
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int wn = 0; wn < WNF; ++wn) {
-          const size_t oi = (size_t)row * a.D + n0 + 16 * wn + r16;
-          if (a.out_bf16)
-            reinterpret_cast<uint16_t*>(a.y)[oi] = (uint16_t)f32_to_bf16_bits(acc[mf][wn][i]);
-          else
-            reinterpret_cast<float*>(a.y)[oi] = acc[mf][wn][i];
+        for (int i = 0; i < 4; ++i) {
+          const int m = rb + 16 * mt + i;
+          if (m < a.M) {
+            const size_t oi = (size_t)m * a.D + cb + 16 * nt;
+            if (a.out_bf16)
+              reinterpret_cast<uint16_t*>(a.y)[oi] = (uint16_t)f32_to_bf16_bits(acc[mt][nt][i]);
+            else
+              reinterpret_cast<float*>(a.y)[oi] = acc[mt][nt][i];
+          }
         }
-      }
     return;
   }
-  // split-K: publish this slice, the last arrival sums all slices in order
+  // split-K: partials at agent scope (read back by another workgroup)
   float* mine = a.part + (size_t)sk * a.M * a.D;
 #pragma unroll
-  for (int mf = 0; mf < MF; ++mf)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = m0 + 16 * mf + 4 * q4 + i;
-      if (row >= a.M) continue;
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int wn = 0; wn < WNF; ++wn)
-        st_agent(mine + (size_t)row * a.D + n0 + 16 * wn + r16, acc[mf][wn][i]);
-    }
-  block_stores_done();   // partials visible device-wide before the arrival (see st_agent)
+      for (int i = 0; i < 4; ++i) {
+        const int m = rb + 16 * mt + i;
+        if (m < a.M) st_agent(mine + (size_t)m * a.D + cb + 16 * nt, acc[mt][nt][i]);
+      }
+  block_stores_done();
   const int tile = tn * a.tiles_m + tm;
   if (tid == 0)
     s_tick = __hip_atomic_fetch_add(&a.tick[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   if (s_tick != (uint32_t)(a.S - 1)) return;
+  // last arrival: sum the S partials of the tile in split order
+  constexpr int EPT = 8;                       // elements per thread per round
+  const int rows = min(C::BM, a.M - m0);
+  for (int e0 = 0; e0 < rows * C::BN; e0 += 256 * EPT) {
+    float sum[EPT];
 #pragma unroll
-  for (int mf = 0; mf < MF; ++mf)
+    for (int k = 0; k < EPT; ++k) sum[k] = 0.f;
+    for (int sp = 0; sp < a.S; ++sp) {
+      float v[EPT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = m0 + 16 * mf + 4 * q4 + i;
-      if (row >= a.M) continue;
+      for (int k = 0; k < EPT; ++k) {
+        const int e = min(e0 + k * 256 + tid, rows * C::BN - 1);   // clamped: no branch
+        v[k] = ld_agent(a.part + (size_t)sp * a.M * a.D + (size_t)(m0 + e / C::BN) * a.D + n0 +
+                        e % C::BN);
+      }
 #pragma unroll
-      for (int wn = 0; wn < WNF; ++wn) {
-        const size_t oi = (size_t)row * a.D + n0 + 16 * wn + r16;
-        float sum = 0.f;
-        for (int s = 0; s < a.S; ++s) {
-          sum += ld_agent(a.part + (size_t)s * a.M * a.D + oi);
-        }
+      for (int k = 0; k < EPT; ++k) sum[k] += v[k];
+    }
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+      const int e = e0 + k * 256 + tid;
+      if (e < rows * C::BN) {
+        const size_t oi = (size_t)(m0 + e / C::BN) * a.D + n0 + e % C::BN;
         if (a.out_bf16)
-          reinterpret_cast<uint16_t*>(a.y)[oi] = (uint16_t)f32_to_bf16_bits(sum);
+          reinterpret_cast<uint16_t*>(a.y)[oi] = (uint16_t)f32_to_bf16_bits(sum[k]);
         else
-          reinterpret_cast<float*>(a.y)[oi] = sum;
+          reinterpret_cast<float*>(a.y)[oi] = sum[k];
       }
     }
+  }
   if (tid == 0) a.tick[tile] = 0u;
 }
-
 
 // Small-M path (M <= 8 rows, the per-draft-step case): the FC is a stream of
 // W (2*D*D bf16) through HBM.  Each wave owns RW consecutive output columns
@@ -319,26 +330,26 @@ __global__ __launch_bounds__(WAVES * 64) void hsr_gemv_kernel(HsrArgs a) {
 }
 
 struct HsrPlan {
-  int MF, WNF, tiles_m, tiles_n, S, k_slice;
-  size_t off_tick, ws_bytes;
+  int MT, NT, tiles_m, tiles_n, S, ksteps;
+  size_t ws_bytes;
 };
 
 HsrPlan plan_hsr(int m, int d) {
   HsrPlan p;
-  p.MF = (m <= 16) ? 1 : (m <= 32 ? 2 : 3);
-  p.WNF = (m > 16 && d % 128 == 0) ? 2 : 1;
-  p.tiles_m = (m + 16 * p.MF - 1) / (16 * p.MF);
-  p.tiles_n = d / (64 * p.WNF);
-  const int Kd = 2 * d;
-  const int tiles = p.tiles_m * p.tiles_n;
-  const int target = device_cu_count();
-  int S = 1;
-  while (S < 16 && tiles * S * 2 <= target + target / 8 && (Kd % (2 * S * kBK)) == 0) S *= 2;
-  p.S = S;
-  p.k_slice = Kd / S;
-  // split-K only when tiles * S <= about 1.1 x CUs, so the counters always fit
-  // the sync region; the finishing workgroup of a tile returns its counter to 0
-  p.off_tick = 0;
+  p.MT = (m <= 64) ? 2 : 4;
+  p.NT = (d % 128 == 0) ? 4 : 2;
+  p.tiles_m = (m + 32 * p.MT - 1) / (32 * p.MT);
+  p.tiles_n = d / (32 * p.NT);
+  p.ksteps = 2 * d / kGemmBK;
+  const long tiles = (long)p.tiles_m * p.tiles_n;
+  const int cus = device_cu_count();
+  // split K until the grid covers the CUs, at least 4 steps per split
+  long S = (cus + tiles / 2) / tiles;
+  S = S < 1 ? 1 : (S > 8 ? 8 : S);
+  while (S > 1 && p.ksteps / S < 4) --S;
+  p.S = (int)S;
+  // split-K only when tiles < CUs, so the per-tile counters fit the sync
+  // region; the finishing workgroup of a tile returns its counter to 0
   p.ws_bytes = (S > 1) ? kSyncBytes + align_up((size_t)S * m * d * sizeof(float), 256) : 0;
   return p;
 }
@@ -395,23 +406,20 @@ spec_status_t launch_hsr(const void* e, const void* h, const void* w, int m, int
   a.w = reinterpret_cast<const uint16_t*>(w);
   a.y = y;
   a.part = (p.S > 1) ? reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + kSyncBytes) : nullptr;
-  a.tick = (p.S > 1) ? reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws) + p.off_tick)
-                     : nullptr;
+  a.tick = (p.S > 1) ? reinterpret_cast<uint32_t*>(ws) : nullptr;
   a.M = m;
   a.D = d_model;
   a.out_bf16 = out_bf16;
   a.tiles_m = p.tiles_m;
   a.tiles_n = p.tiles_n;
   a.S = p.S;
-  a.k_slice = p.k_slice;
+  a.ksteps = p.ksteps;
   const dim3 grid(p.tiles_m * p.tiles_n * p.S), block(256);
-  const int cfg = p.MF * 10 + p.WNF;
-  switch (cfg) {
-    case 11: hipLaunchKernelGGL((hsr_gemm_kernel<1, 1>), grid, block, 0, stream, a); break;
-    case 21: hipLaunchKernelGGL((hsr_gemm_kernel<2, 1>), grid, block, 0, stream, a); break;
-    case 22: hipLaunchKernelGGL((hsr_gemm_kernel<2, 2>), grid, block, 0, stream, a); break;
-    case 31: hipLaunchKernelGGL((hsr_gemm_kernel<3, 1>), grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL((hsr_gemm_kernel<3, 2>), grid, block, 0, stream, a); break;
+  switch (p.MT * 10 + p.NT) {
+    case 22: hipLaunchKernelGGL((hsr_mfma_kernel<2, 2>), grid, block, 0, stream, a); break;
+    case 24: hipLaunchKernelGGL((hsr_mfma_kernel<2, 4>), grid, block, 0, stream, a); break;
+    case 42: hipLaunchKernelGGL((hsr_mfma_kernel<4, 2>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((hsr_mfma_kernel<4, 4>), grid, block, 0, stream, a); break;
   }
   return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
