@@ -11,9 +11,8 @@
 // HBM to LDS by DMA into a ring of NS stages, so data in flight costs no
 // registers.  Each 128-byte row keeps its 16-byte chunk c at slot
 // c ^ (row & 7): the fragment reads (16 rows x one chunk per lane group) then
-// spread over the LDS banks.  Split-K partials are summed by the last
-// workgroup of each tile in split order, so results are bitwise
-// reproducible.
+// spread over the LDS banks.  Split-K partials are summed in split order
+// by a second small kernel, so results are bitwise reproducible.
 //
 // Small M (one draft token at a time): a stream of W through HBM, below.
 #include <string.h>
@@ -34,7 +33,6 @@ struct HsrArgs {
   const uint16_t* w;
   void* y;
   float* part;       // [S, M, D] split-K partials (S > 1)
-  uint32_t* tick;    // [tiles] arrival counters (S > 1), in the sync region
   int32_t M, D, out_bf16;
   int32_t tiles_m, tiles_n, S, ksteps;
 };
@@ -43,7 +41,7 @@ template <int MT, int NT>
 struct GemmCfg {
   static constexpr int BM = 32 * MT, BN = 32 * NT;
   static constexpr int STAGE = (BM + BN) * 128;          // bytes of one K step
-  static constexpr int NS = kGemmRing / STAGE;           // ring depth
+  static constexpr int NS = (kGemmRing / STAGE < 8) ? kGemmRing / STAGE : 8;   // ring depth
   static constexpr int INSTR = STAGE / 1024;             // 1 KB DMAs per step
   static constexpr int PER_WAVE = INSTR / 4;
   static_assert(INSTR % 4 == 0 && NS >= 3 && NS - 2 <= 6, "ring shape");
@@ -83,8 +81,7 @@ template <int MT, int NT>
 __global__ __launch_bounds__(256, 1) void hsr_mfma_kernel(HsrArgs a) {
   using C = GemmCfg<MT, NT>;
   __shared__ __align__(16) unsigned char ring[kGemmRing];
-  __shared__ uint32_t s_tick;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, q4 = lane >> 4;
   const int wm = wave & 1, wn = wave >> 1;
   // work item = (tile_n, split, tile_m): the tile_m neighbours share the W
@@ -158,7 +155,8 @@ __global__ __launch_bounds__(256, 1) void hsr_mfma_kernel(HsrArgs a) {
         }
     return;
   }
-  // split-K: partials at agent scope (read back by another workgroup)
+  // split-K: the partial goes to the workspace; hsr_reduce_kernel adds the
+  // splits in order once every split has finished
   float* mine = a.part + (size_t)sk * a.M * a.D;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -167,45 +165,33 @@ __global__ __launch_bounds__(256, 1) void hsr_mfma_kernel(HsrArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = rb + 16 * mt + i;
-        if (m < a.M) st_agent(mine + (size_t)m * a.D + cb + 16 * nt, acc[mt][nt][i]);
+        if (m < a.M) mine[(size_t)m * a.D + cb + 16 * nt] = acc[mt][nt][i];
       }
-  block_stores_done();
-  const int tile = tn * a.tiles_m + tm;
-  if (tid == 0)
-    s_tick = __hip_atomic_fetch_add(&a.tick[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  if (s_tick != (uint32_t)(a.S - 1)) return;
-  // last arrival: sum the S partials of the tile in split order
-  constexpr int EPT = 8;                       // elements per thread per round
-  const int rows = min(C::BM, a.M - m0);
-  for (int e0 = 0; e0 < rows * C::BN; e0 += 256 * EPT) {
-    float sum[EPT];
+}
+
+// Y = sum over splits s = 0..S-1 (in order) of the partials; 4 consecutive
+// outputs per thread, every split's load in flight at once.
+__global__ __launch_bounds__(256) void hsr_reduce_kernel(HsrArgs a) {
+  constexpr int SMAX = 8;
+  const size_t n4 = (size_t)a.M * a.D / 4;
+  const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= n4) return;
+  const size_t plane = (size_t)a.M * a.D;
+  f32x4_t v[SMAX];
 #pragma unroll
-    for (int k = 0; k < EPT; ++k) sum[k] = 0.f;
-    for (int sp = 0; sp < a.S; ++sp) {
-      float v[EPT];
+  for (int sp = 0; sp < SMAX; ++sp)   // clamped split index: no guarded loads
+    v[sp] = *reinterpret_cast<const f32x4_t*>(a.part + (size_t)min(sp, a.S - 1) * plane + 4 * e);
+  f32x4_t sum = v[0];
 #pragma unroll
-      for (int k = 0; k < EPT; ++k) {
-        const int e = min(e0 + k * 256 + tid, rows * C::BN - 1);   // clamped: no branch
-        v[k] = ld_agent(a.part + (size_t)sp * a.M * a.D + (size_t)(m0 + e / C::BN) * a.D + n0 +
-                        e % C::BN);
-      }
-#pragma unroll
-      for (int k = 0; k < EPT; ++k) sum[k] += v[k];
-    }
-#pragma unroll
-    for (int k = 0; k < EPT; ++k) {
-      const int e = e0 + k * 256 + tid;
-      if (e < rows * C::BN) {
-        const size_t oi = (size_t)(m0 + e / C::BN) * a.D + n0 + e % C::BN;
-        if (a.out_bf16)
-          reinterpret_cast<uint16_t*>(a.y)[oi] = (uint16_t)f32_to_bf16_bits(sum[k]);
-        else
-          reinterpret_cast<float*>(a.y)[oi] = sum[k];
-      }
-    }
+  for (int sp = 1; sp < SMAX; ++sp)
+    if (sp < a.S) sum += v[sp];
+  if (a.out_bf16) {
+    const uint32_t lo = f32_to_bf16_bits(sum[0]) | (f32_to_bf16_bits(sum[1]) << 16);
+    const uint32_t hi = f32_to_bf16_bits(sum[2]) | (f32_to_bf16_bits(sum[3]) << 16);
+    reinterpret_cast<uint2*>(a.y)[e] = make_uint2(lo, hi);
+  } else {
+    reinterpret_cast<f32x4_t*>(a.y)[e] = sum;
   }
-  if (tid == 0) a.tick[tile] = 0u;
 }
 
 // Small-M path (M <= 8 rows, the per-draft-step case): the FC is a stream of
@@ -348,24 +334,28 @@ HsrPlan plan_hsr(int m, int d) {
   S = S < 1 ? 1 : (S > 8 ? 8 : S);
   while (S > 1 && p.ksteps / S < 4) --S;
   p.S = (int)S;
-  // split-K only when tiles < CUs, so the per-tile counters fit the sync
-  // region; the finishing workgroup of a tile returns its counter to 0
   p.ws_bytes = (S > 1) ? kSyncBytes + align_up((size_t)S * m * d * sizeof(float), 256) : 0;
   return p;
 }
 
 }  // namespace
 
+// Up to kGemvMaxM rows the W stream kernel is used (measured faster than the
+// matrix-core tiles for one row; from two rows on the tiles win).
+constexpr int kGemvMaxM = 1;
+
+bool use_gemv(int m, int d_model) {
+  return m <= kGemvMaxM && (size_t)8 * 4 * d_model <= 160 * 1024;
+}
+
 size_t hsr_workspace(int m, int d_model) {
-  if (m <= 8 && (size_t)8 * 4 * d_model <= 160 * 1024) return 0;   // small-M path needs none
+  if (use_gemv(m, d_model)) return 0;   // the stream kernel needs no workspace
   return plan_hsr(m, d_model).ws_bytes;
 }
 
-constexpr int kGemvMaxM = 8;
-
 spec_status_t launch_hsr(const void* e, const void* h, const void* w, int m, int d_model, void* y,
                          int out_bf16, void* ws, hipStream_t stream) {
-  if (m <= kGemvMaxM && (size_t)kGemvMaxM * 4 * d_model <= 160 * 1024) {
+  if (use_gemv(m, d_model)) {
     HsrArgs a;
     memset(&a, 0, sizeof(a));
     a.e = reinterpret_cast<const uint16_t*>(e);
@@ -406,7 +396,6 @@ spec_status_t launch_hsr(const void* e, const void* h, const void* w, int m, int
   a.w = reinterpret_cast<const uint16_t*>(w);
   a.y = y;
   a.part = (p.S > 1) ? reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + kSyncBytes) : nullptr;
-  a.tick = (p.S > 1) ? reinterpret_cast<uint32_t*>(ws) : nullptr;
   a.M = m;
   a.D = d_model;
   a.out_bf16 = out_bf16;
@@ -420,6 +409,12 @@ spec_status_t launch_hsr(const void* e, const void* h, const void* w, int m, int
     case 24: hipLaunchKernelGGL((hsr_mfma_kernel<2, 4>), grid, block, 0, stream, a); break;
     case 42: hipLaunchKernelGGL((hsr_mfma_kernel<4, 2>), grid, block, 0, stream, a); break;
     default: hipLaunchKernelGGL((hsr_mfma_kernel<4, 4>), grid, block, 0, stream, a); break;
+  }
+  if (p.S > 1) {
+    if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
+    const size_t n4 = (size_t)m * d_model / 4;
+    hipLaunchKernelGGL(hsr_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
+                       a);
   }
   return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
