@@ -49,7 +49,7 @@ def _parse():
     ap.add_argument("--reps", type=int, default=40, help="replays of each per-entry-point graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=["verify", "vata", "hsr", "topk", "accept", "step"],
+    ap.add_argument("--only", choices=["verify", "vata", "hsr", "topk", "accept", "step", "c5"],
                     default=None, help="time one part only (for counter passes)")
     return ap.parse_args()
 
@@ -212,6 +212,55 @@ def main():
         t1.synchronize()
         ms_per_step = t0.elapsed_time(t1) / args.steps
 
+    # ---- the batched draft workload (64 sequences, gamma = 5): the fusion FC
+    # on the matrix cores (M = 320), text-anchored attention over 2048 text
+    # rows per sequence and acceptance over [64, 6, vocab] logits.  Seeded
+    # device-side normals of the workload's shapes and scales.
+    c5 = None
+    if only in (None, "c5"):
+        torch.manual_seed(0)
+        Bc, Lt, Mc = 64, 2048, 64 * gamma
+        ec = torch.randn(Mc, D, device=dev).mul_(0.02).to(torch.bfloat16)
+        hc = torch.randn(Mc, D, device=dev).mul_(0.02).to(torch.bfloat16)
+        yc = torch.empty(Mc, D, dtype=torch.bfloat16, device=dev)
+        g = capture(lambda: [S.spec_hsr_fuse(ec, hc, ws[r], y=yc, workspace=wsp["hsr"])
+                             for r in range(R)])
+        hsr_c5_us = time_graph(g, max(4, args.reps // 4)) * 1e3 / R
+        kvc = []
+        for _ in range(2):      # two copies: 2 x 268 MB, more than the 256 MiB cache
+            kc = torch.randn(Bc, Hkv, Lt, d, device=dev).mul_(0.5).to(torch.bfloat16)
+            vc = torch.randn(Bc, Hkv, Lt, d, device=dev).mul_(0.5).to(torch.bfloat16)
+            kvc.append(S.KVCache(kc, vc, torch.full((Bc,), Lt, dtype=torch.int32, device=dev)))
+        qc = yc.view(Bc, gamma, Hq, d)
+        tic = torch.arange(Lt, dtype=torch.int32, device=dev).repeat(Bc, 1)
+        tlc = torch.full((Bc,), Lt, dtype=torch.int32, device=dev)
+        oc = torch.empty((Bc, gamma, Hq, d), dtype=torch.bfloat16, device=dev)
+        lc = torch.empty((Bc, gamma, Hq), dtype=torch.float32, device=dev)
+        g = capture(lambda: [S.spec_vata_attn(kv, qc, tic, tlc, scale=scale, out=oc, lse=lc,
+                                              workspace=wsp["vata"]) for kv in kvc])
+        vata_c5_us = time_graph(g, max(4, args.reps // 4)) * 1e3 / len(kvc)
+        del kvc
+        lgc = [torch.randn(Bc, n, V, device=dev).to(torch.bfloat16) for _ in range(3)]
+        drc = torch.randint(0, V, (Bc, gamma), dtype=torch.int32, device=dev)
+        tc = torch.empty((Bc, n), dtype=torch.int32, device=dev)
+        ac = torch.empty((Bc,), dtype=torch.int32, device=dev)
+        nc = torch.empty((Bc,), dtype=torch.int32, device=dev)
+        g = capture(lambda: [S.spec_accept(lg, drc, target_tok=tc, accept_len=ac, next_tok=nc,
+                                           workspace=wsp["accept"]) for lg in lgc])
+        acc_c5_us = time_graph(g, max(4, args.reps // 4)) * 1e3 / len(lgc)
+        del lgc
+        hsr_c5_flops = 2 * Mc * D * 2 * D
+        vata_c5_bytes = 2 * Bc * Hkv * Lt * d * 2 + Bc * Lt * 4 + 2 * Bc * gamma * Hq * d * 2
+        acc_c5_bytes = Bc * n * V * 2
+        c5 = {"workload": "batched-draft-64x5", "hsr_us": round(hsr_c5_us, 2),
+              "hsr_tflops": round(hsr_c5_flops / (hsr_c5_us * 1e-6) / 1e12, 1),
+              "hsr_mfma_frac": round(hsr_c5_flops / (hsr_c5_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFS,
+                                     4),
+              "vata_us": round(vata_c5_us, 2),
+              "vata_gbs": round(vata_c5_bytes / (vata_c5_us * 1e-6) / 1e9, 1),
+              "accept_us": round(acc_c5_us, 2),
+              "accept_gbs": round(acc_c5_bytes / (acc_c5_us * 1e-6) / 1e9, 1)}
+
     # ---- algorithmic bytes (per call)
     kv_bytes = 2 * L * Hkv * d * 2
     verify_bytes = kv_bytes + 2 * (n * Hq * d * 2) + n * Hq * 4
@@ -297,6 +346,7 @@ def main():
                                       ("accept", accept_bytes)) if k + "_us" in parts},
         "hsr_tflops": round(hsr_flops / (parts["hsr_us"] * 1e-6) / 1e12, 2)
         if "hsr_us" in parts else None,
+        "batched_draft": c5,
         "verify_max_abs_err_vs_oracle": err,
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -1,14 +1,16 @@
 // Greedy acceptance on gfx950: per-row argmax over the vocabulary, then the
 // longest prefix of draft tokens that match, plus the bonus token.
 //
-// The vocabulary scan is split into chunks so every CU streams the logits.
-// A workgroup reduces its chunk to one packed 64-bit key
+// accept_scan_kernel: the vocabulary of every row is cut into chunks so that
+// every CU streams logits; a workgroup reduces its chunk to one packed
+// 64-bit key
 //   (order-preserving bits of the value) << 32 | (0xFFFFFFFF - index)
-// whose maximum is "largest value, then lowest index" in any reduction order,
-// and merges it into its row with a 64-bit atomic max.  The last workgroup of
-// each sequence (arrival counter) turns the row maxima into target tokens,
-// counts the matching prefix and writes the outputs, and returns the maxima
-// and its counter to zero for the next call.
+// whose maximum is "largest value, then lowest index" in any reduction
+// order, and stores it to its own slot (no atomics: device-scope atomics on
+// shared words serialise and cost tens of microseconds at batch 64).
+// accept_finish_kernel: one workgroup per sequence takes the maximum over
+// each row's slots, turns it into the target token and counts the matching
+// prefix.
 #include "common.h"
 #include "internal.h"
 
@@ -26,8 +28,7 @@ struct AcceptArgs {
   int32_t* target_tok;
   int32_t* accept_len;
   int32_t* next_tok;
-  unsigned long long* best;   // [B, n_max] packed maxima (cleared per call)
-  uint32_t* tick;             // [B] arrival counters (cleared per call)
+  unsigned long long* best;   // [B, n_max, chunks] packed chunk maxima (every slot written)
   int32_t B, n_max, V, chunk, chunks, vec;
 };
 
@@ -42,16 +43,19 @@ __device__ __forceinline__ unsigned long long umax64(unsigned long long a, unsig
   return a > b ? a : b;
 }
 
+__device__ __forceinline__ unsigned long long shfl_xor64(unsigned long long v, int o) {
+  return ((unsigned long long)(uint32_t)__shfl_xor((int)(v >> 32), o) << 32) |
+         (uint32_t)__shfl_xor((int)(uint32_t)v, o);
+}
+
 template <bool BF16>
-__global__ __launch_bounds__(kAcceptThreads) void accept_kernel(AcceptArgs a) {
+__global__ __launch_bounds__(kAcceptThreads) void accept_scan_kernel(AcceptArgs a) {
   constexpr int EPV = BF16 ? 8 : 4;                 // elements per 16-byte load
   constexpr int SCALAR = kAccLoads * EPV;           // scalar loads per thread (ragged vocab)
   __shared__ unsigned long long red[kAcceptThreads / 64];
-  __shared__ uint32_t s_tick;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = blockIdx.x / a.chunks;              // b * n_max + i
   const int ch = blockIdx.x - row * a.chunks;
-  const int b = row / a.n_max;
   const int v0 = ch * a.chunk, v1 = min(a.V, v0 + a.chunk);
   // Every row is scanned (rows past gamma are ignored at the end), so the
   // loads do not wait for gamma; all of a thread's loads are in flight at once.
@@ -96,58 +100,68 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(AcceptArgs a) {
       if (v < v1) best = umax64(best, pack_key(x[k], v));
     }
   }
-  for (int o = 32; o > 0; o >>= 1) {
-    const unsigned long long other =
-        ((unsigned long long)(uint32_t)__shfl_xor((int)(best >> 32), o) << 32) |
-        (uint32_t)__shfl_xor((int)(uint32_t)best, o);
-    best = umax64(best, other);
-  }
+  for (int o = 32; o > 0; o >>= 1) best = umax64(best, shfl_xor64(best, o));
   if (lane == 0) red[wave] = best;
   __syncthreads();
-  // The maxima are device-scope atomics, read back with atomic exchanges, so
-  // no cache write-back is needed: thread 0 only waits for its own atomicMax
-  // to complete before it arrives.
   if (tid == 0) {
     unsigned long long m = red[0];
     for (int w = 1; w < kAcceptThreads / 64; ++w) m = umax64(m, red[w]);
-    atomicMax(&a.best[row], m);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    s_tick = atomicAdd(&a.tick[b], 1u);
+    a.best[(size_t)row * a.chunks + ch] = m;
   }
-  __syncthreads();
-  if (s_tick != (uint32_t)(a.n_max * a.chunks - 1) || wave != 0) return;
-  // Last arrival of sequence b: lane r takes row r (64 rows per round), so
-  // the maxima, the draft tokens and the outputs move in one round trip.
+}
+
+// One workgroup per sequence: row r's target token is the maximum over its
+// chunk slots (every slot load in flight at once, reduced in LDS); wave 0
+// then takes rows 64 at a time, one per lane, and finds the first mismatch
+// with a ballot.
+__global__ __launch_bounds__(kAcceptThreads) void accept_finish_kernel(AcceptArgs a) {
+  constexpr int kRows = 64;                 // rows reduced per round
+  __shared__ unsigned long long rmax[kRows];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const int gam = a.gamma ? min(max(a.gamma[b], 0), a.n_max - 1) : a.n_max - 1;
   int n = -1, nxt = 0;
-  for (int r0 = 0; r0 < a.n_max; r0 += 64) {
-    const int r = r0 + lane;
-    unsigned long long k = 0;
-    int d = -1;
-    if (r < a.n_max) {
-      k = atomicExch(&a.best[(size_t)b * a.n_max + r], 0ull);
-      if (r < gam) d = a.draft[(size_t)b * (a.n_max - 1) + r];
+  for (int r0 = 0; r0 < a.n_max; r0 += kRows) {
+    const int rows = min(kRows, a.n_max - r0);
+    if (tid < kRows) rmax[tid] = 0ull;
+    __syncthreads();
+    const int total = rows * a.chunks;
+    const unsigned long long* src = a.best + ((size_t)b * a.n_max + r0) * a.chunks;
+    for (int i0 = 0; i0 < total; i0 += kAcceptThreads * 8) {
+      unsigned long long v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = src[min(i0 + k * kAcceptThreads + tid, total - 1)];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int i = i0 + k * kAcceptThreads + tid;
+        if (i < total) atomicMax(&rmax[i / a.chunks], v[k]);   // LDS atomic
+      }
     }
-    const int t = (r <= gam) ? (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull)) : -1;
-    if (r < a.n_max) a.target_tok[(size_t)b * a.n_max + r] = t;
-    const unsigned long long stop = __builtin_amdgcn_ballot_w64(r <= gam && (r == gam || d != t));
-    if (n < 0 && stop) {
-      const int first = __ffsll((long long)stop) - 1;
-      n = r0 + first;
-      nxt = __shfl(t, first);
+    __syncthreads();
+    if (tid < 64) {
+      const int r = r0 + lane;
+      const unsigned long long k = (lane < rows) ? rmax[lane] : 0ull;
+      const int d = (r < gam) ? a.draft[(size_t)b * (a.n_max - 1) + min(r, a.n_max - 2)] : -1;
+      const int t = (r <= gam) ? (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull)) : -1;
+      if (r < a.n_max) a.target_tok[(size_t)b * a.n_max + r] = t;
+      const unsigned long long stop =
+          __builtin_amdgcn_ballot_w64(r < a.n_max && r <= gam && (r == gam || d != t));
+      if (n < 0 && stop) {
+        const int first = __ffsll((long long)stop) - 1;
+        n = r0 + first;
+        nxt = __shfl(t, first);
+      }
     }
+    __syncthreads();
   }
-  if (lane == 0) {
+  if (tid == 0) {
     a.accept_len[b] = n;
     a.next_tok[b] = nxt;
-    a.tick[b] = 0u;
   }
 }
 
 struct AcceptPlan {
   int chunk, chunks, vec;
-  bool in_sync;
-  size_t off_best, off_tick, ws_bytes;
+  size_t ws_bytes;
 };
 
 AcceptPlan plan_accept(int batch, int n_max, int vocab, bool bf16) {
@@ -157,15 +171,9 @@ AcceptPlan plan_accept(int batch, int n_max, int vocab, bool bf16) {
   p.vec = (vocab % vw == 0) ? 1 : 0;
   if (p.chunk > vocab) p.chunk = ((vocab + vw - 1) / vw) * vw;
   p.chunks = (vocab + p.chunk - 1) / p.chunk;
-  // The maxima and counters live in the sync region when they fit: the
-  // finishing workgroup of each sequence returns them to zero, so no clearing
-  // launch is needed.  Otherwise they sit in scratch and are cleared first.
-  const size_t best_bytes = align_up((size_t)batch * n_max * sizeof(unsigned long long), 256);
-  const size_t words = best_bytes + align_up((size_t)batch * sizeof(uint32_t), 256);
-  p.in_sync = words <= kSyncBytes;
-  p.off_best = p.in_sync ? 0 : kSyncBytes;
-  p.off_tick = p.off_best + best_bytes;
-  p.ws_bytes = p.in_sync ? kSyncBytes : kSyncBytes + words;
+  // chunk maxima in scratch after the sync region; every slot is written
+  p.ws_bytes = kSyncBytes +
+               align_up((size_t)batch * n_max * p.chunks * sizeof(unsigned long long), 256);
   return p;
 }
 
@@ -190,24 +198,21 @@ spec_status_t launch_accept(const void* logits, int dtype, int batch, int n_max,
   a.target_tok = target_tok;
   a.accept_len = accept_len;
   a.next_tok = next_tok;
-  a.best = reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(ws) + p.off_best);
-  a.tick = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws) + p.off_tick);
+  a.best = reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(ws) + kSyncBytes);
   a.B = batch;
   a.n_max = n_max;
   a.V = vocab;
   a.chunk = p.chunk;
   a.chunks = p.chunks;
   a.vec = p.vec;
-  if (!p.in_sync) {
-    const spec_status_t st =
-        launch_zero(a.best, p.off_tick - p.off_best + (size_t)batch * sizeof(uint32_t), stream);
-    if (st != SPEC_OK) return st;
-  }
   const dim3 grid((unsigned)batch * n_max * p.chunks), block(kAcceptThreads);
   if (bf16)
-    hipLaunchKernelGGL(accept_kernel<true>, grid, block, 0, stream, a);
+    hipLaunchKernelGGL(accept_scan_kernel<true>, grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL(accept_kernel<false>, grid, block, 0, stream, a);
+    hipLaunchKernelGGL(accept_scan_kernel<false>, grid, block, 0, stream, a);
+  if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
+  hipLaunchKernelGGL(accept_finish_kernel, dim3((unsigned)batch), dim3(kAcceptThreads), 0, stream,
+                     a);
   return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 

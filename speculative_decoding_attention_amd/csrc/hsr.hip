@@ -194,7 +194,7 @@ __global__ __launch_bounds__(256) void hsr_reduce_kernel(HsrArgs a) {
   }
 }
 
-// Small-M path (M <= 8 rows, the per-draft-step case): the FC is a stream of
+// One-row path (the per-draft-step case): the FC is a stream of
 // W (2*D*D bf16) through HBM.  Each wave owns RW consecutive output columns
 // (W rows) and requests U 16-byte chunks of each of them at once (for
 // D = 3584 that is the whole row pair), before it waits for anything: the
@@ -345,7 +345,7 @@ HsrPlan plan_hsr(int m, int d) {
 constexpr int kGemvMaxM = 1;
 
 bool use_gemv(int m, int d_model) {
-  return m <= kGemvMaxM && (size_t)8 * 4 * d_model <= 160 * 1024;
+  return m <= kGemvMaxM && (size_t)4 * d_model <= 64 * 1024;   // X row in default dynamic LDS
 }
 
 size_t hsr_workspace(int m, int d_model) {
@@ -367,26 +367,8 @@ spec_status_t launch_hsr(const void* e, const void* h, const void* w, int m, int
     a.out_bf16 = out_bf16;
     constexpr int RW = 2, U = 14, WV = 8;
     const dim3 grid((d_model + WV * RW - 1) / (WV * RW)), block(WV * 64);
-    const int mm = (m <= 1) ? 1 : (m <= 2) ? 2 : (m <= 4) ? 4 : 8;
-    const size_t lds = (size_t)mm * 4 * d_model;
-    switch (mm) {
-      case 1: hipLaunchKernelGGL((hsr_gemv_kernel<1, RW, U, WV>), grid, block, lds, stream, a); break;
-      case 2: hipLaunchKernelGGL((hsr_gemv_kernel<2, RW, U, WV>), grid, block, lds, stream, a); break;
-      case 4: hipLaunchKernelGGL((hsr_gemv_kernel<4, RW, U, WV>), grid, block, lds, stream, a); break;
-      default: {
-        // more than the default 64 KiB of dynamic LDS: raise the limit once
-        static bool raised = false;
-        if (!raised) {
-          if (hipFuncSetAttribute(reinterpret_cast<const void*>(&hsr_gemv_kernel<8, RW, U, WV>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  8 * 4 * 5120) != hipSuccess)
-            return SPEC_ERR_HIP;
-          raised = true;
-        }
-        hipLaunchKernelGGL((hsr_gemv_kernel<8, RW, U, WV>), grid, block, lds, stream, a);
-        break;
-      }
-    }
+    static_assert(kGemvMaxM == 1, "one X row in LDS");
+    hipLaunchKernelGGL((hsr_gemv_kernel<1, RW, U, WV>), grid, block, (size_t)4 * d_model, stream, a);
     return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
   }
   const HsrPlan p = plan_hsr(m, d_model);
