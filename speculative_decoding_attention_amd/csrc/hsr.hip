@@ -10,8 +10,8 @@
 // 64-wide steps whose X and W slabs (BM and BN rows of 128 bytes) move from
 // HBM to LDS by DMA into a ring of NS stages, so data in flight costs no
 // registers.  Each 128-byte row keeps its 16-byte chunk c at slot
-// c ^ (row & 7): the fragment reads (16 rows x one chunk per lane group) then
-// spread over the LDS banks.  Split-K partials are summed in split order
+// c ^ ((row >> 1) & 7): two rows share a 256-byte bank line, so the 16 rows
+// of a fragment read (one chunk each) land on 16 distinct bank groups.  Split-K partials are summed in split order
 // by a second small kernel, so results are bitwise reproducible.
 //
 // Small M (one draft token at a time): a stream of W through HBM, below.
@@ -62,7 +62,7 @@ __device__ __forceinline__ void gemm_issue(const HsrArgs& a, int m0, int n0, int
   for (int jj = 0; jj < C::PER_WAVE; ++jj) {
     const int j = wave + 4 * jj;
     const int row = 8 * (j < C::BM / 8 ? j : j - C::BM / 8) + sub;
-    const int chunk = slot ^ (row & 7);
+    const int chunk = slot ^ ((row >> 1) & 7);
     const int k = k0 + 8 * chunk;
     if (j < C::BM / 8) {
       const int m = min(m0 + row, a.M - 1);
@@ -119,13 +119,13 @@ __global__ __launch_bounds__(256, 1) void hsr_mfma_kernel(HsrArgs a) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int row = wm * 16 * MT + 16 * mt + r16;
-        af[mt] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(st + row * 128 + ((c ^ (row & 7)) * 16)));
+        af[mt] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(st + row * 128 + ((c ^ ((row >> 1) & 7)) * 16)));
       }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const int row = wn * 16 * NT + 16 * nt + r16;
         bfr[nt] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(st + C::BM * 128 + row * 128 +
-                                                                 ((c ^ (row & 7)) * 16)));
+                                                                 ((c ^ ((row >> 1) & 7)) * 16)));
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)

@@ -29,7 +29,8 @@ def _hsr_check(case, y):
     return ref
 
 
-@pytest.mark.parametrize("m,d", [(1, 256), (5, 128), (16, 64), (17, 192), (40, 256), (77, 384)])
+@pytest.mark.parametrize("m,d", [(1, 256), (2, 128), (5, 128), (16, 64), (17, 192), (40, 256),
+                                 (64, 128), (65, 128), (77, 384), (130, 64), (200, 512)])
 def test_hsr_small(m, d):
     rng = np.random.default_rng(m * 1000 + d)
     case = W.HsrCase("small",
