@@ -945,14 +945,15 @@ __global__ __launch_bounds__(256, 1) void attn_f32_kernel(AttnArgs a) {
 // rule.  Every partial this thread needs is requested before the split
 // weights are known (they only scale the sum), so the kernel waits for one
 // round of loads; wave 0 meanwhile turns the splits' (m, l, l_rnd) into
-// weights in LDS.  Threads form 256/D groups over the splits; each group
+// weights in LDS.  Threads form kMergeThreads/D groups over the splits; each group
 // sums its splits in order and the groups are added in a fixed order.
 constexpr int kMaxSplits = 4096;
+constexpr int kMergeThreads = 1024;   // more groups over the splits: more loads in flight
 
 template <int D>
-__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
-  constexpr int NG = 256 / D;
-  constexpr int PB = 32;                     // partials in flight per thread
+__global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
+  constexpr int NG = kMergeThreads / D;
+  constexpr int PB = 8 * 1024 / kMergeThreads;   // partials in flight per thread
   __shared__ float w_s[kMaxSplits];
   __shared__ float stat[3];
   __shared__ float part[NG][D];
@@ -1122,9 +1123,9 @@ spec_status_t launch_attention(AttnArgs a, int d, int dtype, const AttnPlan& pla
   if (plan.S > 1) {
     const int blocks = a.B * a.Hkv * a.R;
     if (d == 64)
-      hipLaunchKernelGGL(attn_merge_kernel<64>, dim3(blocks), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL(attn_merge_kernel<64>, dim3(blocks), dim3(kMergeThreads), 0, stream, a);
     else
-      hipLaunchKernelGGL(attn_merge_kernel<128>, dim3(blocks), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL(attn_merge_kernel<128>, dim3(blocks), dim3(kMergeThreads), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
   }
   return SPEC_OK;
