@@ -179,6 +179,23 @@ def test_paged_equals_contiguous_on_device():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("dt", [W.BF16, W.F32])
+def test_rows_past_the_length_are_never_used(dt):
+    """Cache capacity beyond kv_len holds NaN keys and infinite values: the
+    output must still match the oracle (which never reads those rows)."""
+    L = (5000, 3100, 130)
+    c = W.small_attn(41, 3, 28, 4, 128, 6, L, dt, max_len=5600)
+    kb, vb = c.k.bits.copy(), c.v.bits.copy()
+    nan, inf = (0x7FC0, 0x7F80) if dt == W.BF16 else (np.nan, np.inf)   # bf16 bits / fp32 values
+    for b_ in range(3):
+        kb[b_, :, L[b_]:] = nan
+        vb[b_, :, L[b_]:] = inf
+    c.k, c.v = W.Stored(dt, kb), W.Stored(dt, vb)
+    out, lse, ro, rl = _verify_pair(c)
+    assert not torch.isnan(out).any() and not torch.isnan(lse).any()
+    assert_attention_close(out, lse, ro, rl, c.q_len, dt, "rows past the length")
+
+
 def test_repeated_calls_are_bitwise_identical():
     S = _lib()
     c = W.small_attn(17, 1, 28, 4, 128, 6, (25512,), W.BF16)
