@@ -5,8 +5,9 @@
 //
 // Large M (the batched draft step): a tiled GEMM on the matrix cores
 // (v_mfma_f32_16x16x32_bf16, fp32 accumulation).  A workgroup owns a BM x BN
-// output tile (BM = 32*MT rows of X, BN = 32*NT rows of W) and a K range;
-// its 4 waves form a 2 x 2 grid of (16*MT) x (16*NT) blocks.  K advances in
+// output tile (BM = 32*MT rows of X, BN = 16*NT*WN rows of W) and a K range;
+// its 2*WN waves form a 2 x WN grid of (16*MT) x (16*NT) blocks (eight waves:
+// two per SIMD hide each other's LDS and MFMA latency).  K advances in
 // 64-wide steps whose X and W slabs (BM and BN rows of 128 bytes) move from
 // HBM to LDS by DMA into a ring of NS stages, so data in flight costs no
 // registers.  Each 128-byte row keeps its 16-byte chunk c at slot
@@ -26,6 +27,7 @@ namespace {
 
 constexpr int kGemmBK = 64;                // K per step (128 bytes of a row)
 constexpr int kGemmRing = 128 * 1024;      // LDS ring bytes
+constexpr int kGemmWN = 4;                 // waves along N (2 x kGemmWN waves per workgroup)
 
 struct HsrArgs {
   const uint16_t* e;
@@ -37,30 +39,31 @@ struct HsrArgs {
   int32_t tiles_m, tiles_n, S, ksteps;
 };
 
-template <int MT, int NT>
+template <int MT, int NT, int WN>
 struct GemmCfg {
-  static constexpr int BM = 32 * MT, BN = 32 * NT;
+  static constexpr int WAVES = 2 * WN;                   // 2 x WN grid of waves
+  static constexpr int BM = 32 * MT, BN = 16 * NT * WN;
   static constexpr int STAGE = (BM + BN) * 128;          // bytes of one K step
   static constexpr int NS = (kGemmRing / STAGE < 8) ? kGemmRing / STAGE : 8;   // ring depth
   static constexpr int INSTR = STAGE / 1024;             // 1 KB DMAs per step
-  static constexpr int PER_WAVE = INSTR / 4;
-  static_assert(INSTR % 4 == 0 && NS >= 3 && NS - 2 <= 6, "ring shape");
+  static constexpr int PER_WAVE = INSTR / WAVES;
+  static_assert(INSTR % WAVES == 0 && NS >= 3 && NS - 2 <= 6, "ring shape");
   static_assert(PER_WAVE * (NS - 2) <= 63, "vmcnt range");
 };
 
 // DMA of K step `ks` (columns 64*ks..) of the tile's X rows m0.. and W rows
 // n0.. into one ring stage.  Instruction j moves 8 rows of 128 bytes; X rows
 // past M repeat row M-1 (their outputs are never stored).
-template <int MT, int NT>
+template <int MT, int NT, int WN>
 __device__ __forceinline__ void gemm_issue(const HsrArgs& a, int m0, int n0, int ks,
                                            uint32_t stage_lds, int wave, int lane) {
-  using C = GemmCfg<MT, NT>;
+  using C = GemmCfg<MT, NT, WN>;
   const int k0 = ks * kGemmBK;
   const int sub = lane >> 3, slot = lane & 7;
   const unsigned char* src[C::PER_WAVE];
 #pragma unroll
   for (int jj = 0; jj < C::PER_WAVE; ++jj) {
-    const int j = wave + 4 * jj;
+    const int j = wave + C::WAVES * jj;
     const int row = 8 * (j < C::BM / 8 ? j : j - C::BM / 8) + sub;
     const int chunk = slot ^ ((row >> 1) & 7);
     const int k = k0 + 8 * chunk;
@@ -74,12 +77,12 @@ __device__ __forceinline__ void gemm_issue(const HsrArgs& a, int m0, int n0, int
   }
 #pragma unroll
   for (int jj = 0; jj < C::PER_WAVE; ++jj)
-    dma16(src[jj], stage_lds + (uint32_t)((wave + 4 * jj) * 1024));
+    dma16(src[jj], stage_lds + (uint32_t)((wave + C::WAVES * jj) * 1024));
 }
 
-template <int MT, int NT>
-__global__ __launch_bounds__(256, 1) void hsr_mfma_kernel(HsrArgs a) {
-  using C = GemmCfg<MT, NT>;
+template <int MT, int NT, int WN>
+__global__ __launch_bounds__(128 * WN, 1) void hsr_mfma_kernel(HsrArgs a) {
+  using C = GemmCfg<MT, NT, WN>;
   __shared__ __align__(16) unsigned char ring[kGemmRing];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, q4 = lane >> 4;
@@ -98,7 +101,7 @@ __global__ __launch_bounds__(256, 1) void hsr_mfma_kernel(HsrArgs a) {
   lds_u8_t* const ring_l = (lds_u8_t*)ring;
   const uint32_t ring_lds = (uint32_t)(size_t)ring_l;
   for (int j = 0; j < C::NS - 1 && j < nsteps; ++j)
-    gemm_issue<MT, NT>(a, m0, n0, ks0 + j, ring_lds + (uint32_t)(j * C::STAGE), wave, lane);
+    gemm_issue<MT, NT, WN>(a, m0, n0, ks0 + j, ring_lds + (uint32_t)(j * C::STAGE), wave, lane);
 
   f32x4_t acc[MT][NT];
 #pragma unroll
@@ -109,7 +112,7 @@ __global__ __launch_bounds__(256, 1) void hsr_mfma_kernel(HsrArgs a) {
   for (int t = 0; t < nsteps; ++t) {
     wait_tiles_barrier<C::PER_WAVE>(min(C::NS - 2, nsteps - 1 - t));
     if (t + C::NS - 1 < nsteps)
-      gemm_issue<MT, NT>(a, m0, n0, ks0 + t + C::NS - 1,
+      gemm_issue<MT, NT, WN>(a, m0, n0, ks0 + t + C::NS - 1,
                          ring_lds + (uint32_t)(((t + C::NS - 1) % C::NS) * C::STAGE), wave, lane);
     const unsigned char* st = ring + (t % C::NS) * C::STAGE;
 #pragma unroll
@@ -316,16 +319,16 @@ __global__ __launch_bounds__(WAVES * 64) void hsr_gemv_kernel(HsrArgs a) {
 }
 
 struct HsrPlan {
-  int MT, NT, tiles_m, tiles_n, S, ksteps;
+  int MT, BN, tiles_m, tiles_n, S, ksteps;
   size_t ws_bytes;
 };
 
 HsrPlan plan_hsr(int m, int d) {
   HsrPlan p;
   p.MT = (m <= 64) ? 2 : 4;
-  p.NT = (d % 128 == 0) ? 4 : 2;
+  p.BN = (d % 128 == 0) ? 128 : 64;
   p.tiles_m = (m + 32 * p.MT - 1) / (32 * p.MT);
-  p.tiles_n = d / (32 * p.NT);
+  p.tiles_n = d / p.BN;
   p.ksteps = 2 * d / kGemmBK;
   const long tiles = (long)p.tiles_m * p.tiles_n;
   const int cus = device_cu_count();
@@ -385,12 +388,13 @@ spec_status_t launch_hsr(const void* e, const void* h, const void* w, int m, int
   a.tiles_n = p.tiles_n;
   a.S = p.S;
   a.ksteps = p.ksteps;
-  const dim3 grid(p.tiles_m * p.tiles_n * p.S), block(256);
-  switch (p.MT * 10 + p.NT) {
-    case 22: hipLaunchKernelGGL((hsr_mfma_kernel<2, 2>), grid, block, 0, stream, a); break;
-    case 24: hipLaunchKernelGGL((hsr_mfma_kernel<2, 4>), grid, block, 0, stream, a); break;
-    case 42: hipLaunchKernelGGL((hsr_mfma_kernel<4, 2>), grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL((hsr_mfma_kernel<4, 4>), grid, block, 0, stream, a); break;
+  const dim3 grid(p.tiles_m * p.tiles_n * p.S), block(128 * kGemmWN);
+  constexpr int N64 = 64 / (16 * kGemmWN), N128 = 128 / (16 * kGemmWN);
+  switch (p.MT * 1000 + p.BN) {
+    case 2064: hipLaunchKernelGGL((hsr_mfma_kernel<2, N64, kGemmWN>), grid, block, 0, stream, a); break;
+    case 2128: hipLaunchKernelGGL((hsr_mfma_kernel<2, N128, kGemmWN>), grid, block, 0, stream, a); break;
+    case 4064: hipLaunchKernelGGL((hsr_mfma_kernel<4, N64, kGemmWN>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((hsr_mfma_kernel<4, N128, kGemmWN>), grid, block, 0, stream, a); break;
   }
   if (p.S > 1) {
     if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
