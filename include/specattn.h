@@ -42,8 +42,16 @@
  * - Scores use the caller's `scale` (normally 1/sqrt(d)); Q and K are
  *   post-rotary.  Accumulation is fp32 for every input dtype.
  * - Contents of device index arrays (kv_len, q_len, text_idx, text_len,
- *   page_table, draft, gamma) are preconditions: values outside the stated
- *   ranges are undefined behaviour.
+ *   page_table, gamma) are preconditions: values outside the stated ranges
+ *   are undefined behaviour, unless debug mode is on (spec_set_debug, or
+ *   SPEC_DEBUG=1 in the environment at first use).  Then each call first
+ *   checks them on its stream, waits, and returns SPEC_ERR_SHAPE without
+ *   launching anything if one is out of range: 1 <= kv_len <= max_len;
+ *   1 <= q_len <= min(n_max, kv_len) (n_max <= kv_len without q_len);
+ *   0 <= text_len <= t_max; 0 <= text_idx < kv_len for listed entries; the
+ *   pages a sequence needs fit max_pages and their table entries are >= 0
+ *   (the pool size is not known to the library); 0 <= gamma <= n_max - 1.
+ *   Debug calls are synchronous and must not be captured into graphs.
  *
  * Sources (the pages this library implements; titles as published):
  * - "Sparrow: Text-Anchored Window Attention with Visual-Semantic Glimpsing
@@ -217,6 +225,10 @@ const char* spec_status_str(spec_status_t status);
 
 /* SPEC_ABI_VERSION of the loaded library. */
 int32_t spec_abi_version(void);
+
+/* Debug mode on (non-zero) or off for this process; returns the previous
+ * setting.  The initial setting comes from SPEC_DEBUG in the environment. */
+int32_t spec_set_debug(int32_t on);
 
 #ifdef __cplusplus
 }

@@ -55,6 +55,7 @@ SIGNATURES = {
     "spec_accept": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _S, _P]),
     "spec_status_str": (ctypes.c_char_p, [_I]),
     "spec_abi_version": (_I, []),
+    "spec_set_debug": (_I, [_I]),
 }
 
 
@@ -342,3 +343,10 @@ def spec_status_str(status: int) -> str:
 
 def spec_abi_version() -> int:
     return int(lib().spec_abi_version())
+
+
+def spec_set_debug(on: bool) -> bool:
+    """Debug mode on or off for this process: each call then checks its
+    device index arrays first (synchronously) and raises SpecError with
+    SPEC_ERR_SHAPE if one is out of range.  Returns the previous setting."""
+    return bool(lib().spec_set_debug(1 if on else 0))

@@ -78,6 +78,22 @@ AttnArgs make_args(const spec_kv_t* kv, int32_t batch, const void* q, int32_t n_
   return a;
 }
 
+// Debug mode: the device index arrays of an attention call.
+ValidateArgs kv_checks(const spec_kv_t* kv, int32_t batch, const int32_t* q_len, int32_t rows) {
+  ValidateArgs v;
+  v.B = batch;
+  v.kv_len = kv->kv_len;
+  v.max_len = kv->max_len;
+  v.q_len = q_len;
+  v.rows = rows;
+  if (kv->page_size) {
+    v.page_table = kv->page_table;
+    v.page_size = kv->page_size;
+    v.max_pages = kv->max_pages;
+  }
+  return v;
+}
+
 spec_status_t check_ws(size_t need, const void* ws, size_t ws_bytes) {
   if (need == 0) return SPEC_OK;
   if (!ws) return SPEC_ERR_NULL;
@@ -90,6 +106,8 @@ spec_status_t check_ws(size_t need, const void* ws, size_t ws_bytes) {
 extern "C" {
 
 int32_t spec_abi_version(void) { return SPEC_ABI_VERSION; }
+
+int32_t spec_set_debug(int32_t on) { return set_debug(on); }
 
 const char* spec_status_str(spec_status_t status) {
   switch (status) {
@@ -129,6 +147,8 @@ spec_status_t spec_verify_attn(const spec_kv_t* kv, int32_t batch, const void* q
                                        kv->page_size != 0);
   st = check_ws(plan.ws_bytes, ws, ws_bytes);
   if (st != SPEC_OK) return st;
+  if (debug_enabled() && (st = validate(kv_checks(kv, batch, q_len, n_max), stream)) != SPEC_OK)
+    return st;
   return launch_attention(a, kv->head_dim, kv->dtype, plan, ws, stream);
 }
 
@@ -162,6 +182,13 @@ spec_status_t spec_vata_attn(const spec_kv_t* kv, int32_t batch, const void* q,
   const AttnPlan plan = plan_attention(batch * kv->num_kv_heads, t_max, a.R, kv->head_dim, true);
   st = check_ws(plan.ws_bytes, ws, ws_bytes);
   if (st != SPEC_OK) return st;
+  if (debug_enabled()) {
+    ValidateArgs v = kv_checks(kv, batch, q_len, n_max);
+    v.text_idx = text_idx;
+    v.text_len = text_len;
+    v.t_max = t_max;
+    if ((st = validate(v, stream)) != SPEC_OK) return st;
+  }
   return launch_attention(a, kv->head_dim, kv->dtype, plan, ws, stream);
 }
 
@@ -189,6 +216,8 @@ spec_status_t spec_topk_attn(const spec_kv_t* kv, int32_t batch, const void* q,
   const TopkPlan plan = plan_topk(batch * kv->num_kv_heads, kv->max_len, top_k, a.R, kv->head_dim);
   st = check_ws(plan.ws_bytes, ws, ws_bytes);
   if (st != SPEC_OK) return st;
+  if (debug_enabled() && (st = validate(kv_checks(kv, batch, nullptr, 1), stream)) != SPEC_OK)
+    return st;
   st = launch_topk_select(a, kv->head_dim, kv->dtype, top_k, sel_idx, plan, ws, stream);
   if (st != SPEC_OK) return st;
   a.mode = 2;
@@ -233,8 +262,15 @@ spec_status_t spec_accept(const void* logits, int32_t dtype, int32_t batch, int3
   if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ERR_DTYPE;
   if (batch < 1 || n_max < 1 || vocab < 1 || vocab >= 0x7fffffff) return SPEC_ERR_SHAPE;
   if ((long long)batch * n_max > (1 << 24)) return SPEC_ERR_SHAPE;
-  const spec_status_t st = check_ws(accept_workspace(batch, n_max, vocab), ws, ws_bytes);
+  spec_status_t st = check_ws(accept_workspace(batch, n_max, vocab), ws, ws_bytes);
   if (st != SPEC_OK) return st;
+  if (debug_enabled() && gamma) {
+    ValidateArgs v;
+    v.B = batch;
+    v.gamma = gamma;
+    v.gamma_n = n_max;
+    if ((st = validate(v, stream)) != SPEC_OK) return st;
+  }
   return launch_accept(logits, dtype, batch, n_max, vocab, draft, gamma, target_tok, accept_len,
                        next_tok, ws, stream);
 }

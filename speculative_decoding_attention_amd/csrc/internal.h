@@ -93,6 +93,28 @@ spec_status_t launch_accept(const void* logits, int dtype, int batch, int n_max,
                             int32_t* accept_len, int32_t* next_tok, void* ws,
                             hipStream_t stream);
 
+// Debug-mode checks of device index arrays (see validate.hip).  Null
+// pointers and zero counts skip the corresponding check.
+struct ValidateArgs {
+  int32_t B = 0;
+  const int32_t* kv_len = nullptr;
+  int32_t max_len = 0;
+  const int32_t* q_len = nullptr;
+  int32_t rows = 0;                 // query rows per sequence (0: no check)
+  const int32_t* page_table = nullptr;
+  int32_t page_size = 0, max_pages = 0;
+  const int32_t* text_idx = nullptr;
+  const int32_t* text_len = nullptr;
+  int32_t t_max = 0;
+  const int32_t* gamma = nullptr;
+  int32_t gamma_n = 0;              // gamma[b] must be in [0, gamma_n - 1]
+};
+bool debug_enabled();
+int set_debug(int on);
+// Runs the checks on `stream` and waits for them: SPEC_ERR_SHAPE when a
+// value is out of range.
+spec_status_t validate(const ValidateArgs& v, hipStream_t stream);
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Clears `bytes` (a multiple of 4) at `p` with a fill kernel, so it is safe

@@ -121,3 +121,26 @@ def test_hsr_and_accept_rejections(L):
     assert need >= 64 * 6 * 8
     assert L.spec_accept(FAKE, 1, 64, 6, 152064, FAKE, None, FAKE, FAKE, FAKE, FAKE, need - 1,
                          None) == 4
+
+
+def test_set_debug_returns_the_previous_setting(L):
+    first = L.spec_set_debug(1)
+    try:
+        assert L.spec_set_debug(0) == 1
+        assert L.spec_set_debug(0) == 0
+        assert L.spec_set_debug(7) == 0
+        assert L.spec_set_debug(1) == 1
+    finally:
+        L.spec_set_debug(first)
+
+
+def test_debug_mode_leaves_host_checks_first(L):
+    """Host-side rejections come before any device check, so they need no GPU
+    in debug mode either."""
+    prev = L.spec_set_debug(1)
+    try:
+        assert L.spec_hsr_fuse(None, FAKE, FAKE, 1, 4, 64, FAKE, 1, None, 0, None) == 1
+        assert L.spec_accept(FAKE, 2, 1, 6, 100, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1 << 20,
+                             None) == 3
+    finally:
+        L.spec_set_debug(prev)

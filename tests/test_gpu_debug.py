@@ -1,0 +1,128 @@
+"""Debug mode (spec_set_debug / SPEC_DEBUG=1): valid inputs give the same
+results as with debug off, and each out-of-range device index array is
+reported as SPEC_ERR_SHAPE before anything is launched.
+
+Every invalid input below is chosen so that, were it to reach the kernels, all
+accesses would still stay inside allocated memory (an over-long first
+sequence reads into the next one's rows, a negative page number lands on a
+spare page placed in front of the pool)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_util import dev, kvcache
+
+pytestmark = pytest.mark.gpu
+
+SHAPE = 2
+
+
+@pytest.fixture
+def S():
+    import speculative_decoding_attention_amd as S
+    prev = S.spec_set_debug(True)
+    yield S
+    S.spec_set_debug(prev)
+
+
+def _case(page_size=0):
+    return W.small_attn(41, 2, 8, 2, 128, 6, (900, 700), W.BF16, page_size=page_size,
+                        max_len=1024 if not page_size else None)
+
+
+def _rejects(fn):
+    import speculative_decoding_attention_amd as S
+    with pytest.raises(S.SpecError) as e:
+        fn()
+    assert e.value.status == SHAPE, str(e.value)
+
+
+def _same(a, b):
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_valid_inputs_match_debug_off(S):
+    c = _case()
+    kv = kvcache(c)
+    q = dev(c.q)
+    q1 = q[:, -1:].contiguous()
+    idx, tl = dev(c.text_idx), dev(c.text_len)
+    rng = np.random.default_rng(2)
+    logits = dev(W.Stored.from_f32(rng.standard_normal((2, 6, 5000)).astype(np.float32), W.BF16))
+    draft = dev(rng.integers(0, 5000, size=(2, 5)).astype(np.int32))
+    gamma = dev(np.array([5, 2], np.int32))
+    calls = [
+        lambda: S.spec_verify_attn(kv, q, scale=c.scale, out_dtype=torch.float32),
+        lambda: S.spec_vata_attn(kv, q, idx, tl, scale=c.scale, out_dtype=torch.float32),
+        lambda: S.spec_topk_attn(kv, q1, 64, scale=c.scale, out_dtype=torch.float32),
+        lambda: S.spec_accept(logits, draft, gamma),
+    ]
+    on = [f() for f in calls]
+    torch.cuda.synchronize()
+    S.spec_set_debug(False)
+    off = [f() for f in calls]
+    torch.cuda.synchronize()
+    for a, b in zip(on, off):
+        _same(a, b)
+
+
+def test_bad_lengths_are_rejected(S):
+    c = _case()
+    q = dev(c.q)
+    q1 = q[:, -1:].contiguous()
+
+    def with_len(l0, l1=700):
+        c2 = _case()
+        c2.kv_len = np.array([l0, l1], np.int32)
+        return kvcache(c2)
+
+    over = with_len(1025)              # kv_len[0] > max_len
+    _rejects(lambda: S.spec_verify_attn(over, q, scale=c.scale))
+    _rejects(lambda: S.spec_topk_attn(over, q1, 64, scale=c.scale))
+    short = with_len(900, 3)           # fewer keys than the 6 query rows
+    _rejects(lambda: S.spec_verify_attn(short, q, scale=c.scale))
+    kv = kvcache(c)
+    _rejects(lambda: S.spec_verify_attn(kv, q, q_len=dev(np.array([0, 6], np.int32)),
+                                        scale=c.scale))
+    # q_len within bounds is fine
+    S.spec_verify_attn(kv, q, q_len=dev(np.array([1, 6], np.int32)), scale=c.scale)
+    torch.cuda.synchronize()
+
+
+def test_bad_text_lists_are_rejected(S):
+    c = _case()
+    kv = kvcache(c)
+    q = dev(c.q)
+    idx = c.text_idx.copy()
+    idx[0, 0] = c.kv_len[0]            # one past the last position, still < max_len
+    _rejects(lambda: S.spec_vata_attn(kv, q, dev(idx), dev(c.text_len), scale=c.scale))
+    tl = c.text_len.copy()
+    tl[0] = c.text_idx.shape[1] + 1    # longer than the list's row
+    _rejects(lambda: S.spec_vata_attn(kv, q, dev(c.text_idx), dev(tl), scale=c.scale))
+
+
+def test_bad_gamma_is_rejected(S):
+    rng = np.random.default_rng(3)
+    logits = dev(W.Stored.from_f32(rng.standard_normal((2, 6, 5000)).astype(np.float32), W.BF16))
+    draft = dev(rng.integers(0, 5000, size=(2, 5)).astype(np.int32))
+    _rejects(lambda: S.spec_accept(logits, draft, dev(np.array([6, 1], np.int32))))
+    S.spec_accept(logits, draft, dev(np.array([5, 0], np.int32)))
+    torch.cuda.synchronize()
+
+
+def test_negative_page_is_rejected(S):
+    from speculative_decoding_attention_amd import KVCache
+    c = _case(page_size=16)
+    k, v = dev(c.k), dev(c.v)
+    # a spare page in front of the pool, so page -1 is allocated memory
+    kf = torch.zeros((k.shape[0] + 1,) + tuple(k.shape[1:]), dtype=k.dtype, device=k.device)
+    vf = torch.zeros_like(kf)
+    kf[1:] = k
+    vf[1:] = v
+    pt = c.page_table.copy()
+    pt[0, 3] = -1
+    kv = KVCache(kf[1:], vf[1:], dev(c.kv_len), page_table=dev(pt), page_size=16,
+                 max_len=c.max_len)
+    _rejects(lambda: S.spec_verify_attn(kv, dev(c.q), scale=c.scale))
