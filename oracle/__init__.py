@@ -21,6 +21,12 @@ exact (widened) values of the stored inputs:
   score).
 * ``hsr_fuse``          -- FC over the concatenation [e_t ; h_{t-1}] (Sparrow zh
   explainer 3.1, hidden-state reuse).
+* ``std_prefill_scores`` / ``std_prefill_select`` / ``std_keep_list`` --
+  Sparse-to-Dense's prefill selection: per (sequence, KV head), the top-K
+  visual positions by the mean attention of the text tokens, kept with the
+  text positions (Sparse-to-Dense pt explainer, "Seleção de Cache KV").
+* ``sparse_attention``  -- the sparse draft attention over such a per-head
+  list plus the positions written since (same page, "Metodologia").
 * ``accept``            -- greedy acceptance: longest prefix of draft tokens that
   match the dense model's argmax, plus one bonus token (Sparse-to-Dense pt
   explainer, "Metodologia", decoding procedure).
@@ -34,7 +40,9 @@ from .attention import (verify_attention, vata_attention, topk_scores, topk_sele
                         topk_attention, paged_rows)
 from .hsr import hsr_fuse, hsr_fuse_loops
 from .accept import accept, argmax_lowest
+from .std import sparse_attention, std_keep_list, std_prefill_scores, std_prefill_select
 
 __all__ = ["verify_attention", "vata_attention", "topk_scores", "topk_select",
            "topk_attention", "paged_rows", "hsr_fuse", "hsr_fuse_loops", "accept",
-           "argmax_lowest"]
+           "argmax_lowest", "std_prefill_scores", "std_prefill_select", "std_keep_list",
+           "sparse_attention"]

@@ -149,6 +149,47 @@ class AcceptCase:
     planted_len: Optional[np.ndarray] = None
 
 
+@dataclasses.dataclass
+class StdCase:
+    """Inputs for Sparse-to-Dense prefill selection and its sparse decode.
+
+    ``q_text [B, t_max, Hq, d]``: row t is the prefill query of the text token
+    at ``text_idx[b, t]`` (ascending, distinct, t < text_len[b]).  K/V are laid
+    out as in AttnCase.  ``q [B, n, Hq, d]`` are draft query rows for the
+    decode that follows (row i at position kv_len[b] - q_len[b] + i).
+    """
+
+    name: str
+    dtype: str
+    q_text: Stored
+    k: Stored
+    v: Stored
+    q: Stored
+    kv_len: np.ndarray
+    q_len: np.ndarray
+    text_idx: np.ndarray
+    text_len: np.ndarray
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    max_len: int
+    top_k: int = 0
+    page_size: int = 0
+    page_table: Optional[np.ndarray] = None
+
+    @property
+    def batch(self) -> int:
+        return int(self.q_text.shape[0])
+
+    @property
+    def t_max(self) -> int:
+        return int(self.q_text.shape[1])
+
+    @property
+    def scale(self) -> float:
+        return float(1.0 / np.sqrt(self.head_dim))
+
+
 # --------------------------------------------------------------------------
 # the five workloads
 # --------------------------------------------------------------------------
@@ -393,3 +434,76 @@ def small_attn(seed: int, B: int, Hq: int, Hkv: int, d: int, n: int, L, dtype: s
         q=Stored.from_f32(q, dtype), k=Stored.from_f32(k, dtype), v=Stored.from_f32(v, dtype),
         kv_len=L, q_len=ql, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, max_len=max_len,
         page_size=page_size, page_table=page_table, text_idx=text_idx, text_len=text_len)
+
+
+def _text_positions(rng: np.random.Generator, L: int, n: int) -> np.ndarray:
+    """n distinct ascending text positions below L: half of them (rounded
+    up) trail the sequence, the rest are spread at random before them."""
+    n = min(n, L)
+    trail = (n + 1) // 2
+    inter = np.sort(rng.choice(L - trail, size=n - trail, replace=False)) if n > trail else \
+        np.zeros(0, np.int64)
+    return np.concatenate([inter, np.arange(L - trail, L)]).astype(np.int32)
+
+
+def std_small(seed: int, B: int, Hq: int, Hkv: int, d: int, L, dtype: str, n_text,
+              page_size: int = 0, top_k: int = 16, n: int = 1, max_len: Optional[int] = None,
+              q_scale: float = 1.0) -> StdCase:
+    """Random prefill-selection case at test sizes: ragged lengths, text
+    tokens interleaved with the visual ones and trailing them, optional
+    paging.  Draw order: K -> V -> text layout -> text queries -> draft rows."""
+    rng = np.random.default_rng(seed)
+    L = np.broadcast_to(np.asarray(L, dtype=np.int32), (B,)).copy()
+    nt = np.broadcast_to(np.asarray(n_text, dtype=np.int32), (B,)).copy()
+    max_len = int(L.max()) if max_len is None else max_len
+    if page_size:
+        npg = (L + page_size - 1) // page_size
+        P = int(npg.sum())
+        perm = rng.permutation(P).astype(np.int32)
+        page_table = np.zeros((B, int(npg.max()) + 1), np.int32)
+        off = 0
+        for b in range(B):
+            page_table[b, :npg[b]] = perm[off:off + npg[b]]
+            off += npg[b]
+        kv_shape = (P, Hkv, page_size, d)
+    else:
+        page_table = None
+        kv_shape = (B, Hkv, max_len, d)
+    k = _normal(rng, kv_shape, 0.5)
+    v = _normal(rng, kv_shape, 0.5)
+    t_max = max(1, int(nt.max()))
+    text_idx = np.zeros((B, t_max), np.int32)
+    text_len = np.zeros(B, np.int32)
+    for b in range(B):
+        x = _text_positions(rng, int(L[b]), int(nt[b]))
+        text_idx[b, :len(x)] = x
+        text_len[b] = len(x)
+    q_text = _normal(rng, (B, t_max, Hq, d), q_scale)
+    q = _normal(rng, (B, n, Hq, d))
+    return StdCase(
+        name=f"std_s{seed}", dtype=dtype, q_text=Stored.from_f32(q_text, dtype),
+        k=Stored.from_f32(k, dtype), v=Stored.from_f32(v, dtype), q=Stored.from_f32(q, dtype),
+        kv_len=L, q_len=np.full(B, n, np.int32), text_idx=text_idx, text_len=text_len,
+        num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, max_len=max_len, top_k=top_k,
+        page_size=page_size, page_table=page_table)
+
+
+def c2_std(seed: int = 0, top_k: int = 2048) -> StdCase:
+    """Sparse-to-Dense prefill selection at the 25k-visual-token shape, bf16:
+    B=1, 28/4 heads, d=128, 25000 visual + 512 text positions in the same
+    layout as the Sparrow-scale step (64 interleaved, 448 trailing), one
+    prefill query row per text token, K = 2048 kept visual positions, one
+    draft row.  Draw order: K -> V -> text queries -> draft row."""
+    rng = np.random.default_rng([seed, 2])
+    B, Hq, Hkv, d, Lvis, Ltxt = 1, 28, 4, 128, 25000, 512
+    L = Lvis + Ltxt
+    k = _normal(rng, (B, Hkv, L, d), 0.5)
+    v = _normal(rng, (B, Hkv, L, d), 0.5)
+    q_text = _normal(rng, (B, Ltxt, Hq, d))
+    q = _normal(rng, (B, 1, Hq, d))
+    return StdCase(
+        name="c2_std", dtype=BF16, q_text=Stored.from_f32(q_text, BF16),
+        k=Stored.from_f32(k, BF16), v=Stored.from_f32(v, BF16), q=Stored.from_f32(q, BF16),
+        kv_len=np.array([L], np.int32), q_len=np.array([1], np.int32),
+        text_idx=c2_text_layout(Lvis, Ltxt)[None, :], text_len=np.array([Ltxt], np.int32),
+        num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, max_len=L, top_k=top_k)
