@@ -6,6 +6,8 @@
  *   draft:   u = FC([e_t ; h_{t-1}])                    spec_hsr_fuse
  *            text-anchored attention over text rows     spec_vata_attn
  *            (or top-K sparse attention over all rows)  spec_topk_attn
+ *            (or lists kept since prefill:              spec_std_select
+ *             selection once, then attention)           spec_sparse_attn
  *   verify:  gamma+1 rows against the full KV cache     spec_verify_attn
  *   accept:  argmax + longest matching prefix           spec_accept
  *
@@ -50,7 +52,10 @@
  *   1 <= q_len <= min(n_max, kv_len) (n_max <= kv_len without q_len);
  *   0 <= text_len <= t_max; 0 <= text_idx < kv_len for listed entries; the
  *   pages a sequence needs fit max_pages and their table entries are >= 0
- *   (the pool size is not known to the library); 0 <= gamma <= n_max - 1.
+ *   (the pool size is not known to the library); 0 <= gamma <= n_max - 1;
+ *   for spec_std_select the text list is strictly ascending; for
+ *   spec_sparse_attn 0 <= list_len <= list_max, list entries lie in
+ *   [0, tail_start) and kv_len - tail_max <= tail_start <= kv_len.
  *   Debug calls are synchronous and must not be captured into graphs.
  *
  * Sources (the pages this library implements; titles as published):
@@ -181,6 +186,76 @@ spec_status_t spec_topk_attn(const spec_kv_t* kv, int32_t batch, const void* q,
                              int32_t q_dtype, int32_t num_q_heads, int32_t top_k, float scale,
                              int32_t* sel_idx, void* out, int32_t out_dtype, float* lse,
                              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * spec_std_select -- Sparse-to-Dense prefill KV selection ("Selecao de Cache
+ * KV": the top-K visual KV entries are chosen once, during prefill, by the
+ * mean attention that the text tokens pay to the visual tokens, separately
+ * per layer and attention head; the text KV is kept).  One call covers one
+ * layer; the selection is per (sequence b, KV head g).
+ *
+ * q_text:   [B, t_max, Hq, head_dim] in kv->dtype (q_dtype must match): row
+ *           t is the prefill query of the text token at text_idx[b, t].
+ * text_idx: device [B, t_max] int32, strictly ascending in [0, kv_len[b]) for
+ *           t < text_len[b]; text_len: device [B], 0 <= text_len <= t_max.
+ * Text row t sees positions j <= text_idx[b, t] (causal prefill); with
+ * A[h, t, j] its softmax weight (scale applied to the dot products),
+ *   mean[b, g, j] = 1/(G*T) * sum over the group's heads h and t < T of
+ *                   A[h, t, j]  (0 when T = 0), for j < kv_len[b].
+ * Visual positions (j < kv_len[b], not in the text list) are ranked by
+ * (mean descending, index ascending).
+ * sel_idx:  device [B, Hkv, top_k] out: the first min(top_k, #visual) in
+ *           ascending order, then -1.
+ * keep_idx: device [B, Hkv, top_k + t_max] out, or NULL: the ascending union
+ *           of the selection and the text positions, then -1;
+ *           keep_len: device [B, Hkv] out (required with keep_idx): its
+ *           length.  keep_idx/keep_len feed spec_sparse_attn.
+ * score:    device [B, Hkv, max_len] float out, or NULL: mean[b, g, j] for
+ *           j < kv_len[b] (text positions included); later entries are not
+ *           written.
+ * Precision: bf16 inputs use exact products with fp32 sums on the matrix
+ * cores, fp32 exponentials, and fp64 for the final sum over row blocks; the
+ * ranking is taken on those values, so positions whose means differ by less
+ * than about 1e-5 relative may rank in either order.  fp32 inputs use fp32
+ * FMAs.  Limits: t_max * (Hq / Hkv) <= 2^20 rows; top_k >= 1.
+ */
+size_t spec_std_select_workspace(const spec_kv_t* kv, int32_t batch, int32_t num_q_heads,
+                                 int32_t t_max, int32_t top_k);
+spec_status_t spec_std_select(const spec_kv_t* kv, int32_t batch, const void* q_text,
+                              int32_t q_dtype, int32_t num_q_heads, const int32_t* text_idx,
+                              const int32_t* text_len, int32_t t_max, int32_t top_k,
+                              float scale, int32_t* sel_idx, int32_t* keep_idx,
+                              int32_t* keep_len, float* score, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
+
+/*
+ * spec_sparse_attn -- Sparse-to-Dense draft attention over the kept lists
+ * ("Metodologia": the sparse mode of the same model attends only to the
+ * selected KV entries; decoding continues with the entries written since).
+ *
+ * For (b, KV head g) the attended positions are
+ *   list_idx[b, g, 0 .. list_len[b, g]-1]        (used as given), then
+ *   tail_start[b] .. kv_len[b]-1                  (none if tail_start NULL).
+ * Query row i < q_len[b] sits at P = kv_len[b] - q_len[b] + i and sees the
+ * members at positions <= P; rows past q_len are padding (O = 0,
+ * LSE = -inf), as for spec_verify_attn.
+ * list_idx: device [B, Hkv, list_max] int32, entries in [0, tail_start[b])
+ *           (in [0, kv_len[b]) without a tail); list_len: device [B, Hkv],
+ *           0 <= list_len <= list_max.
+ * tail_start: device [B] or NULL; kv_len[b] - tail_max <= tail_start[b] <=
+ *           kv_len[b].  tail_max: host bound on the tail (sizes the launch;
+ *           0 without a tail).
+ * q, out, lse, scale, dtypes: as spec_verify_attn.
+ */
+size_t spec_sparse_attn_workspace(const spec_kv_t* kv, int32_t batch, int32_t n_max,
+                                  int32_t num_q_heads, int32_t list_max, int32_t tail_max);
+spec_status_t spec_sparse_attn(const spec_kv_t* kv, int32_t batch, const void* q,
+                               int32_t q_dtype, int32_t n_max, const int32_t* q_len,
+                               int32_t num_q_heads, const int32_t* list_idx,
+                               const int32_t* list_len, int32_t list_max,
+                               const int32_t* tail_start, int32_t tail_max, float scale,
+                               void* out, int32_t out_dtype, float* lse, void* ws,
+                               size_t ws_bytes, hipStream_t stream);
 
 /*
  * spec_hsr_fuse -- hidden-state-reuse fusion FC (Sparrow, technical summary

@@ -51,11 +51,11 @@ def std_prefill_scores(q_text, k, kv_len, text_idx, text_len, num_kv_heads: int,
                 continue
             for t in range(T):
                 p = int(pos[t])
-                keys = kr[g, :p + 1]
-                for h in range(g * G, (g + 1) * G):
-                    s = scale * (keys @ np.asarray(q_text[b, t, h], np.float64))
-                    e = np.exp(s - s.max())
-                    sc[g, :p + 1] += e / e.sum()
+                keys = kr[g, :p + 1]                                   # [p+1, d]
+                qh = np.asarray(q_text[b, t, g * G:(g + 1) * G], np.float64)   # [G, d]
+                s = scale * (keys @ qh.T)                              # [p+1, G], one column per head
+                e = np.exp(s - s.max(axis=0))
+                sc[g, :p + 1] += (e / e.sum(axis=0)).sum(axis=1)
             sc[g] /= G * T
         res.append(sc)
     return res

@@ -54,6 +54,12 @@ SIGNATURES = {
     "spec_accept_workspace": (_S, [_I, _I, _I]),
     "spec_accept": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _S, _P]),
     "spec_status_str": (ctypes.c_char_p, [_I]),
+    "spec_std_select_workspace": (_S, [_KVP, _I, _I, _I, _I]),
+    "spec_std_select": (_I, [_KVP, _I, _P, _I, _I, _P, _P, _I, _I, _F, _P, _P, _P, _P, _P, _S,
+                             _P]),
+    "spec_sparse_attn_workspace": (_S, [_KVP, _I, _I, _I, _I, _I]),
+    "spec_sparse_attn": (_I, [_KVP, _I, _P, _I, _I, _P, _I, _P, _P, _I, _P, _I, _F, _P, _I, _P,
+                              _P, _S, _P]),
     "spec_abi_version": (_I, []),
     "spec_set_debug": (_I, [_I]),
 }
@@ -286,6 +292,77 @@ def spec_topk_attn(kv: KVCache, q: torch.Tensor, top_k: int, scale: Optional[flo
                           wsp, wsn, _stream(q.device))
     _check("spec_topk_attn", st)
     return sel_idx, out, lse
+
+
+def spec_std_select(kv: KVCache, q_text: torch.Tensor, text_idx: torch.Tensor,
+                    text_len: torch.Tensor, top_k: int, scale: Optional[float] = None,
+                    want_keep: bool = True, want_score: bool = False,
+                    sel_idx: Optional[torch.Tensor] = None,
+                    keep_idx: Optional[torch.Tensor] = None,
+                    keep_len: Optional[torch.Tensor] = None,
+                    score: Optional[torch.Tensor] = None,
+                    workspace: Optional[Workspace] = None):
+    """Sparse-to-Dense prefill selection for one layer; returns
+    (sel_idx, keep_idx, keep_len, score), the last three None unless asked."""
+    L = lib()
+    _dev(q_text, "q_text", kv.k.dtype)
+    _dev(text_idx, "text_idx", torch.int32)
+    _dev(text_len, "text_len", torch.int32)
+    B, t_max, Hq, d = q_text.shape
+    Hkv = kv.num_kv_heads
+    dev = q_text.device
+    if sel_idx is None:
+        sel_idx = torch.empty((B, Hkv, top_k), dtype=torch.int32, device=dev)
+    if want_keep and keep_idx is None:
+        keep_idx = torch.empty((B, Hkv, top_k + t_max), dtype=torch.int32, device=dev)
+    if keep_idx is not None and keep_len is None:
+        keep_len = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+    if want_score and score is None:
+        score = torch.empty((B, Hkv, kv.max_len), dtype=torch.float32, device=dev)
+    scale = float(d ** -0.5) if scale is None else float(scale)
+    need = L.spec_std_select_workspace(ctypes.byref(kv.struct), B, Hq, t_max, int(top_k))
+    wsp, wsn = _workspace(workspace, dev).get(need, dev)
+    st = L.spec_std_select(ctypes.byref(kv.struct), B, _ptr(q_text), _dtype_code(q_text.dtype), Hq,
+                           _ptr(text_idx), _ptr(text_len), t_max, int(top_k), scale,
+                           _ptr(sel_idx), _ptr(keep_idx), _ptr(keep_len), _ptr(score), wsp, wsn,
+                           _stream(dev))
+    _check("spec_std_select", st)
+    return sel_idx, keep_idx, keep_len, score
+
+
+def spec_sparse_attn(kv: KVCache, q: torch.Tensor, list_idx: torch.Tensor,
+                     list_len: torch.Tensor, tail_start: Optional[torch.Tensor] = None,
+                     tail_max: int = 0, q_len: Optional[torch.Tensor] = None,
+                     scale: Optional[float] = None, out_dtype: Optional[torch.dtype] = None,
+                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                     want_lse: bool = True, workspace: Optional[Workspace] = None):
+    """Draft attention over per-head kept lists plus a dense tail; returns
+    (out, lse)."""
+    L = lib()
+    _dev(q, "q", kv.k.dtype)
+    _dev(list_idx, "list_idx", torch.int32)
+    _dev(list_len, "list_len", torch.int32)
+    if tail_start is not None:
+        _dev(tail_start, "tail_start", torch.int32)
+    if q_len is not None:
+        _dev(q_len, "q_len", torch.int32)
+    B, n_max, Hq, d = q.shape
+    list_max = int(list_idx.shape[2])
+    out_dtype = out_dtype or q.dtype
+    if out is None:
+        out = torch.empty((B, n_max, Hq, d), dtype=out_dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, n_max, Hq), dtype=torch.float32, device=q.device)
+    scale = float(d ** -0.5) if scale is None else float(scale)
+    tail_max = int(tail_max) if tail_start is not None else 0
+    need = L.spec_sparse_attn_workspace(ctypes.byref(kv.struct), B, n_max, Hq, list_max, tail_max)
+    wsp, wsn = _workspace(workspace, q.device).get(need, q.device)
+    st = L.spec_sparse_attn(ctypes.byref(kv.struct), B, _ptr(q), _dtype_code(q.dtype), n_max,
+                            _ptr(q_len), Hq, _ptr(list_idx), _ptr(list_len), list_max,
+                            _ptr(tail_start), tail_max, scale, _ptr(out), _dtype_code(out.dtype),
+                            _ptr(lse), wsp, wsn, _stream(q.device))
+    _check("spec_sparse_attn", st)
+    return out, lse
 
 
 def spec_hsr_fuse(e: torch.Tensor, h: torch.Tensor, w: torch.Tensor,

@@ -17,7 +17,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libspecattn.so")
-SOURCES = ["api.hip", "attention.hip", "topk.hip", "hsr.hip", "accept.hip", "validate.hip"]
+SOURCES = ["api.hip", "attention.hip", "topk.hip", "hsr.hip", "accept.hip", "validate.hip", "std.hip"]
 ARCH = os.environ.get("SPEC_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

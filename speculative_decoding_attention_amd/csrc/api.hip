@@ -226,6 +226,118 @@ spec_status_t spec_topk_attn(const spec_kv_t* kv, int32_t batch, const void* q,
   return launch_attention(a, kv->head_dim, kv->dtype, plan.attn, ws, stream);
 }
 
+// ---------------------------------------------- Sparse-to-Dense prefill ----
+
+size_t spec_std_select_workspace(const spec_kv_t* kv, int32_t batch, int32_t num_q_heads,
+                                 int32_t t_max, int32_t top_k) {
+  if (check_kv(kv) != SPEC_OK || batch < 1 || num_q_heads < 1 || t_max < 1 || top_k < 1 ||
+      num_q_heads % kv->num_kv_heads)
+    return 0;
+  const int G = num_q_heads / kv->num_kv_heads;
+  if ((long long)t_max * G > (1 << 20)) return 0;
+  return plan_std(batch * kv->num_kv_heads, kv->max_len, t_max, G, top_k).ws_bytes;
+}
+
+spec_status_t spec_std_select(const spec_kv_t* kv, int32_t batch, const void* q_text,
+                              int32_t q_dtype, int32_t num_q_heads, const int32_t* text_idx,
+                              const int32_t* text_len, int32_t t_max, int32_t top_k,
+                              float scale, int32_t* sel_idx, int32_t* keep_idx,
+                              int32_t* keep_len, float* score, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+  spec_status_t st = check_kv(kv);
+  if (st != SPEC_OK) return st;
+  if (!q_text || !text_idx || !text_len || !sel_idx) return SPEC_ERR_NULL;
+  if (keep_idx && !keep_len) return SPEC_ERR_NULL;
+  if (batch < 1 || num_q_heads < 1 || num_q_heads % kv->num_kv_heads) return SPEC_ERR_SHAPE;
+  if (q_dtype != kv->dtype) return SPEC_ERR_DTYPE;
+  if (!isfinite(scale) || t_max < 1 || top_k < 1) return SPEC_ERR_SHAPE;
+  const int G = num_q_heads / kv->num_kv_heads;
+  if ((long long)t_max * G > (1 << 20)) return SPEC_ERR_UNSUPPORTED;
+  if ((long long)batch * kv->num_kv_heads * kv->max_len > (1LL << 31)) return SPEC_ERR_SHAPE;
+  if ((long long)batch * kv->num_kv_heads * ((long long)top_k + t_max) > (1LL << 31))
+    return SPEC_ERR_SHAPE;
+  const int units = batch * kv->num_kv_heads;
+  const StdPlan plan = plan_std(units, kv->max_len, t_max, G, top_k);
+  st = check_ws(plan.ws_bytes, ws, ws_bytes);
+  if (st != SPEC_OK) return st;
+  if (debug_enabled()) {
+    ValidateArgs v = kv_checks(kv, batch, nullptr, 0);
+    v.text_idx = text_idx;
+    v.text_len = text_len;
+    v.t_max = t_max;
+    v.text_sorted = true;
+    if ((st = validate(v, stream)) != SPEC_OK) return st;
+  }
+  StdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q_text;
+  a.k = kv->k;
+  a.kv_len = kv->kv_len;
+  a.page_table = kv->page_size ? kv->page_table : nullptr;
+  a.max_pages = kv->max_pages;
+  a.page_shift = kv->page_size ? log2_int(kv->page_size) : -1;
+  a.text_idx = text_idx;
+  a.text_len = text_len;
+  a.B = batch;
+  a.Hq = num_q_heads;
+  a.Hkv = kv->num_kv_heads;
+  a.G = G;
+  a.t_max = t_max;
+  a.max_len = kv->max_len;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return launch_std_select(a, kv->head_dim, kv->dtype, top_k, sel_idx, keep_idx, keep_len, score,
+                           plan, ws, stream);
+}
+
+// ------------------------------------------------ sparse (kept lists) ----
+
+size_t spec_sparse_attn_workspace(const spec_kv_t* kv, int32_t batch, int32_t n_max,
+                                  int32_t num_q_heads, int32_t list_max, int32_t tail_max) {
+  if (check_kv(kv) != SPEC_OK || batch < 1 || n_max < 1 || num_q_heads < 1 || list_max < 1 ||
+      tail_max < 0 || num_q_heads % kv->num_kv_heads)
+    return 0;
+  const int R = n_max * (num_q_heads / kv->num_kv_heads);
+  return plan_attention(batch * kv->num_kv_heads, list_max + tail_max, R, kv->head_dim, true)
+      .ws_bytes;
+}
+
+spec_status_t spec_sparse_attn(const spec_kv_t* kv, int32_t batch, const void* q,
+                               int32_t q_dtype, int32_t n_max, const int32_t* q_len,
+                               int32_t num_q_heads, const int32_t* list_idx,
+                               const int32_t* list_len, int32_t list_max,
+                               const int32_t* tail_start, int32_t tail_max, float scale,
+                               void* out, int32_t out_dtype, float* lse, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+  spec_status_t st =
+      check_common(kv, batch, q, q_dtype, n_max, num_q_heads, scale, out, out_dtype);
+  if (st != SPEC_OK) return st;
+  if (!list_idx || !list_len) return SPEC_ERR_NULL;
+  if (list_max < 1 || tail_max < 0) return SPEC_ERR_SHAPE;
+  if (!tail_start) tail_max = 0;
+  if ((long long)list_max + tail_max > (1 << 30)) return SPEC_ERR_SHAPE;
+  AttnArgs a = make_args(kv, batch, q, n_max, q_len, num_q_heads, scale, out, out_dtype, lse);
+  a.mode = 3;
+  a.slots = list_idx;
+  a.slot_len = list_len;
+  a.slot_stride = list_max;
+  a.tail_start = tail_start;
+  const AttnPlan plan =
+      plan_attention(batch * kv->num_kv_heads, list_max + tail_max, a.R, kv->head_dim, true);
+  st = check_ws(plan.ws_bytes, ws, ws_bytes);
+  if (st != SPEC_OK) return st;
+  if (debug_enabled()) {
+    ValidateArgs v = kv_checks(kv, batch, q_len, n_max);
+    v.Hkv = kv->num_kv_heads;
+    v.list_idx = list_idx;
+    v.list_len = list_len;
+    v.list_max = list_max;
+    v.tail_start = tail_start;
+    v.tail_max = tail_max;
+    if ((st = validate(v, stream)) != SPEC_OK) return st;
+  }
+  return launch_attention(a, kv->head_dim, kv->dtype, plan, ws, stream);
+}
+
 // ---------------------------------------------------------------- HSR ----
 
 size_t spec_hsr_fuse_workspace(int32_t m, int32_t d_model) {

@@ -63,11 +63,14 @@ struct SlotMap {
 // device memory.
 __device__ __forceinline__ void stage_slots(const AttnArgs& a, int b, int g, int t_beg, int t_end,
                                             int* pos, uint32_t* row) {
+  const size_t u = (size_t)b * a.Hkv + g;
+  const int n_list = (a.mode == 3) ? a.slot_len[u] : 0;
   for (int t = t_beg + (int)threadIdx.x; t < t_end; t += blockDim.x) {
     int p;
     if (a.mode == 0) p = t;
     else if (a.mode == 1) p = a.slots[(size_t)b * a.slot_stride + t];
-    else p = a.slots[((size_t)b * a.Hkv + g) * a.slot_stride + t];
+    else if (a.mode == 2 || t < n_list) p = a.slots[u * a.slot_stride + t];
+    else p = a.tail_start[b] + (t - n_list);
     uint32_t r;
     if (a.page_shift >= 0) {
       const int page = a.page_table[(size_t)b * a.max_pages + (p >> a.page_shift)];
@@ -79,6 +82,14 @@ __device__ __forceinline__ void stage_slots(const AttnArgs& a, int b, int g, int
     pos[t - t_beg] = p;
     row[t - t_beg] = r;
   }
+}
+
+// Number of key slots of unit (b, g) (see AttnArgs::mode).
+__device__ __forceinline__ int unit_slots(const AttnArgs& a, int b, int g, int L) {
+  if (a.mode == 0) return L;
+  if (a.mode == 1) return a.slot_len[b];
+  if (a.mode == 2) return min(a.slot_stride, L);
+  return a.slot_len[b * a.Hkv + g] + (a.tail_start ? max(0, L - a.tail_start[b]) : 0);
 }
 
 // Shared epilogue: merge the 4 waves' (m, l, l_rnd, acc) in LDS in a fixed
@@ -380,7 +391,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
   const int b = u / a.Hkv, g = u - b * a.Hkv;
   const int L = a.kv_len[b];
   const int nq = a.q_len ? a.q_len[b] : a.n_max;
-  const int T = (a.mode == 0) ? L : (a.mode == 1 ? a.slot_len[b] : min(a.slot_stride, L));
+  const int T = unit_slots(a, b, g, L);
   const int t_beg = s * a.chunk;
   const int t_end = min(T, t_beg + a.chunk);
 
@@ -652,7 +663,7 @@ __global__ __launch_bounds__(PipeCfg<NB>::WAVES * 64, 1) void attn_bf16_pipe_ker
   if (!GATHER) pipe_issue_q<NB>(a, b, g, ring_lds + kQSlot, wave, lane);
   const int L = a.kv_len[b];
   const int nq = a.q_len ? a.q_len[b] : a.n_max;
-  const int T = (a.mode == 0) ? L : (a.mode == 1 ? a.slot_len[b] : min(a.slot_stride, L));
+  const int T = unit_slots(a, b, g, L);
   const int t_beg = s * a.chunk;
   const int t_end = min(T, t_beg + a.chunk);
   const int n_tiles = t_end > t_beg ? (t_end - t_beg + C::TILE_KEYS - 1) / C::TILE_KEYS : 0;
@@ -832,7 +843,7 @@ __global__ __launch_bounds__(256, 1) void attn_f32_kernel(AttnArgs a) {
   const int b = u / a.Hkv, g = u - b * a.Hkv;
   const int L = a.kv_len[b];
   const int nq = a.q_len ? a.q_len[b] : a.n_max;
-  const int T = (a.mode == 0) ? L : (a.mode == 1 ? a.slot_len[b] : min(a.slot_stride, L));
+  const int T = unit_slots(a, b, g, L);
   const int t_beg = s * a.chunk;
   const int t_end = min(T, t_beg + a.chunk);
   const float* qf = reinterpret_cast<const float*>(a.q);

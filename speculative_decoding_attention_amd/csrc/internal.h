@@ -16,6 +16,8 @@ namespace spec {
 //   0  dense:        position = t,                         T_b = kv_len[b]
 //   1  text list:    position = slots[b*stride + t],       T_b = slot_len[b]
 //   2  top-K list:   position = slots[(b*Hkv+g)*stride+t], T_b = min(stride, kv_len[b])
+//   3  per-head list + tail: slots[(b*Hkv+g)*stride + t] for t < slot_len[b*Hkv+g],
+//                    then tail_start[b] + (t - slot_len[..]) up to kv_len[b]
 struct AttnArgs {
   const void* q;
   const void* k;
@@ -25,8 +27,14 @@ struct AttnArgs {
   const int32_t* page_table;  // paged layout when page_shift >= 0
   int32_t max_pages;
   int32_t page_shift;
+  // Key slots of a unit: mode 0 every position below kv_len; mode 1 a list
+  // per sequence (slots[b, :slot_len[b]]); mode 2 a list per unit of
+  // min(slot_stride, kv_len) entries; mode 3 a list per unit
+  // (slots[u, :slot_len[u]]) followed by positions tail_start[b]..kv_len-1
+  // (no tail when tail_start is null).
   const int32_t* slots;
   const int32_t* slot_len;
+  const int32_t* tail_start;
   int32_t slot_stride;
   int32_t mode;
   int32_t B, Hq, Hkv, G, n_max, R, max_len;
@@ -81,6 +89,45 @@ spec_status_t launch_topk_select(const AttnArgs& a, int d, int dtype, int top_k,
                                  int32_t* sel_idx, const TopkPlan& plan, void* ws,
                                  hipStream_t stream);
 
+// Sparse-to-Dense prefill selection (std.hip: the two score passes;
+// topk.hip: the mean, the ranking and the kept lists).
+struct StdArgs {
+  const void* q;               // [B, t_max, Hq, D] text-token queries
+  const void* k;
+  const int32_t* kv_len;
+  const int32_t* page_table;   // paged layout when page_shift >= 0
+  int32_t max_pages, page_shift;
+  const int32_t* text_idx;     // [B, t_max] ascending positions
+  const int32_t* text_len;     // [B]
+  int32_t B, Hq, Hkv, G, t_max, max_len;
+  int32_t RB, RBP;             // 128-row blocks per unit, and RB * 128
+  int32_t S, chunk;            // key splits and keys per split
+  float scale_log2;
+  float2* ml;                  // [U, S, RBP] per-split (reference max, sum of exp2)
+  float* colsum;               // [U, RB, max_len] per-row-block sums of attention
+};
+struct StdRankPlan {
+  size_t off_scores = 0;       // fp64 [U, max_len] ranking scores
+  size_t off_key16 = 0;        // uint16 [U, max_len]
+  size_t off_hist = 0;         // uint32 [U, 4096]
+  bool hist_in_sync = false;
+  size_t ws_bytes = 0;
+};
+struct StdPlan {
+  int RB = 0, RBP = 0, S = 1, chunk = 0, grid = 0;
+  size_t off_ml = 0, off_col = 0;
+  StdRankPlan rank;
+  size_t ws_bytes = 0;
+};
+StdPlan plan_std(int units, int max_len, int t_max, int G, int top_k);
+StdRankPlan plan_std_rank(int units, int max_len, size_t scratch_off);
+spec_status_t launch_std_select(StdArgs a, int d, int dtype, int top_k, int32_t* sel_idx,
+                                int32_t* keep_idx, int32_t* keep_len, float* score,
+                                const StdPlan& plan, void* ws, hipStream_t stream);
+spec_status_t launch_std_rank(const StdArgs& a, int top_k, int32_t* sel_idx, int32_t* keep_idx,
+                              int32_t* keep_len, float* score, const StdRankPlan& plan, void* ws,
+                              hipStream_t stream);
+
 // HSR fusion GEMM.
 size_t hsr_workspace(int m, int d_model);
 spec_status_t launch_hsr(const void* e, const void* h, const void* w, int m, int d_model,
@@ -106,8 +153,17 @@ struct ValidateArgs {
   const int32_t* text_idx = nullptr;
   const int32_t* text_len = nullptr;
   int32_t t_max = 0;
+  bool text_sorted = false;         // text list strictly ascending
   const int32_t* gamma = nullptr;
   int32_t gamma_n = 0;              // gamma[b] must be in [0, gamma_n - 1]
+  // per-unit lists (spec_sparse_attn): list_idx[b, g, :list_len[b, g]] in
+  // [0, tail_start[b]) (or [0, kv_len[b]) without a tail)
+  int32_t Hkv = 0;
+  const int32_t* list_idx = nullptr;
+  const int32_t* list_len = nullptr;
+  int32_t list_max = 0;
+  const int32_t* tail_start = nullptr;
+  int32_t tail_max = 0;
 };
 bool debug_enabled();
 int set_debug(int on);

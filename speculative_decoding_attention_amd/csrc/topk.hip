@@ -26,6 +26,7 @@
 //   when the bin holds more candidates than LDS, and compaction straight from
 //   the scores when the cache is longer than the LDS bit mask.
 #include <math.h>
+#include <string.h>
 
 #include "common.h"
 #include "internal.h"
@@ -511,7 +512,178 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(TopkArgs a) {
   for (int i = tid; i < kHistBins; i += nt) gh[i] = 0;
 }
 
+// ---------------------------------------------- Sparse-to-Dense ranking ----
+// Per key j < kv_len[b] of unit u: the mean attention of the text rows, i.e.
+// the row blocks' partial sums (from std.hip) added in block order in fp64
+// and divided by the row count (0 without text).  That mean goes to the
+// caller's fp32 score array; the ranking key is the mean for visual
+// positions and -inf for text positions, which are kept unconditionally and
+// must never displace a visual one.  Keys, 16-bit float keys and the coarse
+// histogram are laid out exactly as the selection kernel above expects.
+__global__ __launch_bounds__(256) void std_score_kernel(StdArgs s, TopkArgs a, float* score_out) {
+  __shared__ uint32_t hist[kHistBins / 2];
+  __shared__ uint32_t text_bits[kScoreKeys / 32];
+  const int tiles = (a.max_len + kScoreKeys - 1) / kScoreKeys;
+  const int u = blockIdx.x / tiles, tile = blockIdx.x - (blockIdx.x / tiles) * tiles;
+  const int b = u / a.Hkv;
+  const int L = a.kv_len[b];
+  const int j0 = tile * kScoreKeys;
+  if (j0 >= L) return;
+  const int T = s.text_len[b];
+  const int nrb = (T * s.G + 127) / 128;
+  for (int i = threadIdx.x; i < kHistBins / 2; i += blockDim.x) hist[i] = 0;
+  if (threadIdx.x < kScoreKeys / 32) text_bits[threadIdx.x] = 0;
+  __syncthreads();
+  const int* text = s.text_idx + (size_t)b * s.t_max;
+  for (int i = threadIdx.x; i < T; i += blockDim.x) {
+    const int x = text[i] - j0;
+    if (x >= 0 && x < kScoreKeys) atomicOr(&text_bits[x >> 5], 1u << (x & 31));
+  }
+  __syncthreads();
+  const int j = j0 + (int)threadIdx.x;
+  if (j < L) {
+    const float* col = s.colsum + (size_t)u * s.RB * a.max_len + j;
+    double sum = 0.0;
+    for (int r0 = 0; r0 < nrb; r0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = col[(size_t)min(r0 + i, nrb - 1) * a.max_len];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (r0 + i < nrb) sum += (double)v[i];
+    }
+    const double mean = T ? sum / (double)(T * s.G) : 0.0;
+    if (score_out) score_out[(size_t)u * a.max_len + j] = (float)mean;
+    const bool is_text = (text_bits[threadIdx.x >> 5] >> (threadIdx.x & 31)) & 1u;
+    const double key = is_text ? -INFINITY : mean;
+    a.scores[(size_t)u * a.max_len + j] = key;
+    const uint32_t k32 = fine_key32(key);
+    a.key16[(size_t)u * a.max_len + j] = (uint16_t)(k32 >> 16);
+    const uint32_t bin = k32 >> 20;
+    atomicAdd(&hist[bin >> 1], (bin & 1u) ? 0x10000u : 1u);
+  }
+  __syncthreads();
+  uint32_t* gh = a.hist + (size_t)u * kHistBins;
+  for (int i = threadIdx.x; i < kHistBins; i += blockDim.x)
+    if (const uint32_t c = (hist[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) atomicAdd(&gh[i], c);
+}
+
+// First index in the ascending array x[0, n) whose value is >= v.
+__device__ __forceinline__ int lower_bound(const int32_t* x, int n, int v) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (x[mid] < v) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// The i-th (from 0) position that is not in the ascending, distinct list
+// text[0, T): text[k] - k positions precede text[k] outside the list, a
+// non-decreasing count, so the answer is i plus the number of k with
+// text[k] - k <= i.
+__device__ __forceinline__ int ith_outside(const int32_t* text, int T, int i) {
+  int lo = 0, hi = T;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (text[mid] - mid <= i) lo = mid + 1;
+    else hi = mid;
+  }
+  return i + lo;
+}
+
+// The selection without text positions, and the kept list: the ascending
+// union of the selection and the text positions, each element placed at its
+// own index plus its rank in the other list.  When the sequence has no more
+// visual positions than K, every one of them is selected (the ranking then
+// also picked text positions, which are replaced here) and the kept list is
+// every position below kv_len.
+__global__ __launch_bounds__(256) void std_list_kernel(StdArgs s, int K, int32_t* sel,
+                                                       int32_t* keep, int32_t* keep_len) {
+  const int W = K + s.t_max;
+  const int per_u = (W + 255) / 256;
+  const int u = blockIdx.x / per_u;
+  const int item = (blockIdx.x - u * per_u) * 256 + (int)threadIdx.x;
+  const int b = u / s.Hkv;
+  const int L = s.kv_len[b], T = s.text_len[b];
+  const int nvis = L - T;
+  const int32_t* text = s.text_idx + (size_t)b * s.t_max;
+  int32_t* su = sel + (size_t)u * K;
+  int32_t* ku = keep ? keep + (size_t)u * W : nullptr;
+  if (nvis <= K) {
+    if (item < K) su[item] = (item < nvis) ? ith_outside(text, T, item) : -1;
+    if (ku && item < W) ku[item] = (item < L) ? item : -1;
+    if (keep_len && item == 0) keep_len[u] = L;
+  } else {
+    if (ku) {
+      if (item < K) {
+        const int v = su[item];
+        ku[item + lower_bound(text, T, v)] = v;
+      } else if (item < K + T) {
+        const int i = item - K, x = text[i];
+        ku[i + lower_bound(su, K, x)] = x;
+      } else if (item < W) {
+        ku[item] = -1;
+      }
+    }
+    if (keep_len && item == 0) keep_len[u] = K + T;
+  }
+}
+
 }  // namespace
+
+StdRankPlan plan_std_rank(int units, int max_len, size_t scratch_off) {
+  StdRankPlan p;
+  const size_t hist_bytes = (size_t)units * kHistBins * sizeof(uint32_t);
+  p.hist_in_sync = hist_bytes <= kSyncBytes;
+  p.off_scores = align_up(scratch_off, 256);
+  p.off_key16 = align_up(p.off_scores + (size_t)units * max_len * sizeof(double), 256);
+  size_t end = align_up(p.off_key16 + (size_t)units * max_len * sizeof(uint16_t), 256);
+  if (p.hist_in_sync) {
+    p.off_hist = 0;
+  } else {
+    p.off_hist = end;
+    end = align_up(end + hist_bytes, 256);
+  }
+  p.ws_bytes = end;
+  return p;
+}
+
+spec_status_t launch_std_rank(const StdArgs& s, int top_k, int32_t* sel_idx, int32_t* keep_idx,
+                              int32_t* keep_len, float* score, const StdRankPlan& plan, void* ws,
+                              hipStream_t stream) {
+  TopkArgs a;
+  memset(&a, 0, sizeof(a));
+  a.kv_len = s.kv_len;
+  a.B = s.B;
+  a.Hq = s.Hq;
+  a.Hkv = s.Hkv;
+  a.G = s.G;
+  a.max_len = s.max_len;
+  a.top_k = top_k;
+  char* w = reinterpret_cast<char*>(ws);
+  a.scores = reinterpret_cast<double*>(w + plan.off_scores);
+  a.key16 = reinterpret_cast<uint16_t*>(w + plan.off_key16);
+  a.hist = reinterpret_cast<uint32_t*>(w + plan.off_hist);
+  a.sel_idx = sel_idx;
+  const int units = s.B * s.Hkv;
+  if (!plan.hist_in_sync) {
+    const spec_status_t st =
+        launch_zero(a.hist, (size_t)units * kHistBins * sizeof(uint32_t), stream);
+    if (st != SPEC_OK) return st;
+  }
+  const int tiles = (s.max_len + kScoreKeys - 1) / kScoreKeys;
+  hipLaunchKernelGGL(std_score_kernel, dim3(units * tiles), dim3(256), 0, stream, s, a, score);
+  if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
+  hipLaunchKernelGGL(topk_select_kernel, dim3(units), dim3(1024), 0, stream, a);
+  if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
+  const int per_u = (top_k + s.t_max + 255) / 256;
+  hipLaunchKernelGGL(std_list_kernel, dim3(units * per_u), dim3(256), 0, stream, s, top_k,
+                     sel_idx, keep_idx, keep_len);
+  if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
+  return SPEC_OK;
+}
 
 TopkPlan plan_topk(int units, int max_len, int top_k, int rows, int d) {
   TopkPlan p;

@@ -22,8 +22,10 @@ __device__ __forceinline__ void flag(bool bad) {
 
 // Per sequence b: 1 <= kv_len <= max_len; 1 <= q_len <= min(rows, kv_len)
 // (rows <= kv_len without q_len); 0 <= text_len <= t_max and every listed
-// position in [0, kv_len); pages needed within max_pages and every used
-// page-table entry >= 0; 0 <= gamma <= gamma_n - 1.
+// position in [0, kv_len) (strictly ascending when asked); pages needed
+// within max_pages and every used page-table entry >= 0; 0 <= gamma <=
+// gamma_n - 1; per-unit list lengths in [0, list_max] and entries below the
+// tail start, which lies in [kv_len - tail_max, kv_len].
 __global__ __launch_bounds__(256) void check_kernel(ValidateArgs v) {
   const int b = blockIdx.x;
   const int L = v.kv_len ? v.kv_len[b] : 0;
@@ -58,6 +60,24 @@ __global__ __launch_bounds__(256) void check_kernel(ValidateArgs v) {
     for (int i = threadIdx.x; i < t; i += blockDim.x) {
       const int pos = v.text_idx[(size_t)b * v.t_max + i];
       flag(pos < 0 || pos >= L);
+      if (v.text_sorted && i > 0) flag(v.text_idx[(size_t)b * v.t_max + i - 1] >= pos);
+    }
+  }
+  if (v.list_idx && v.kv_len && len_ok) {
+    int end = L;
+    if (v.tail_start) {
+      end = v.tail_start[b];
+      if (threadIdx.x == 0) flag(end < L - v.tail_max || end > L);
+    }
+    for (int g = 0; g < v.Hkv; ++g) {
+      const size_t u = (size_t)b * v.Hkv + g;
+      const int n = v.list_len[u];
+      if (threadIdx.x == 0) flag(n < 0 || n > v.list_max);
+      const int nn = min(max(n, 0), v.list_max);
+      for (int i = threadIdx.x; i < nn; i += blockDim.x) {
+        const int pos = v.list_idx[u * v.list_max + i];
+        flag(pos < 0 || pos >= end);
+      }
     }
   }
 }
