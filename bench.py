@@ -49,7 +49,8 @@ def _parse():
     ap.add_argument("--reps", type=int, default=40, help="replays of each per-entry-point graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=["verify", "vata", "hsr", "topk", "accept", "step", "c5"],
+    ap.add_argument("--only", choices=["verify", "vata", "hsr", "topk", "accept", "step", "c5",
+                                       "std"],
                     default=None, help="time one part only (for counter passes)")
     return ap.parse_args()
 
@@ -261,6 +262,67 @@ def main():
               "accept_us": round(acc_c5_us, 2),
               "accept_gbs": round(acc_c5_bytes / (acc_c5_us * 1e-6) / 1e9, 1)}
 
+    # ---- Sparse-to-Dense at the same shape: the prefill selection of one
+    # layer (512 text queries x 28 heads over 25,512 positions, K = 2048) and
+    # the sparse draft step over the kept lists plus 64 decoded positions.
+    std = None
+    if only in (None, "std"):
+        cs = W.c2_std(0)
+        kv_s = S.KVCache(to_dev(cs.k), to_dev(cs.v), kv_len)
+        qt = to_dev(cs.q_text)
+        ti_s = torch.tensor(cs.text_idx, dtype=torch.int32, device=dev)
+        tl_s = torch.tensor(cs.text_len, dtype=torch.int32, device=dev)
+        sel_s = torch.empty((B, Hkv, cs.top_k), dtype=torch.int32, device=dev)
+        keep_s = torch.empty((B, Hkv, cs.top_k + cs.t_max), dtype=torch.int32, device=dev)
+        klen_s = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+        ws_std = S.Workspace(dev)
+
+        def call_select():
+            S.spec_std_select(kv_s, qt, ti_s, tl_s, cs.top_k, scale=scale, sel_idx=sel_s,
+                              keep_idx=keep_s, keep_len=klen_s, workspace=ws_std)
+        call_select()
+        torch.cuda.synchronize()
+        g = capture(call_select)
+        select_us = time_graph(g, max(4, args.reps // 4)) * 1e3
+        tail = 64
+        t0_s = torch.full((B,), L - tail, dtype=torch.int32, device=dev)
+        keep_tail = keep_s.clone()
+        # the kept positions at or past the tail start are the tail's own
+        keep_tail[keep_tail >= L - tail] = -1
+        klen_tail = (keep_tail >= 0).sum(dim=2).to(torch.int32)
+        keep_tail = torch.sort(torch.where(keep_tail < 0, torch.full_like(keep_tail, 1 << 30),
+                                           keep_tail), dim=2).values
+        keep_tail = torch.where(keep_tail == (1 << 30), torch.full_like(keep_tail, -1),
+                                keep_tail).contiguous()
+        o_sp = torch.empty((B, 1, Hq, d), dtype=torch.bfloat16, device=dev)
+        l_sp = torch.empty((B, 1, Hq), dtype=torch.float32, device=dev)
+        ws_sp = S.Workspace(dev)
+
+        def call_sparse(r):
+            S.spec_sparse_attn(kvs[r], q_last, keep_tail, klen_tail, tail_start=t0_s,
+                               tail_max=tail, scale=scale, out=o_sp, lse=l_sp, workspace=ws_sp)
+        for r in range(R):
+            call_sparse(r)
+        torch.cuda.synchronize()
+        g = capture(lambda: [call_sparse(r) for r in range(R)])
+        sparse_us = time_graph(g, args.reps) * 1e3 / R
+        # work of the selection: both passes form every visible score
+        pos = cs.text_idx[0, :cs.text_len[0]].astype(np.int64)
+        visible = int((pos + 1).sum()) * Hq          # (row, key) pairs over all heads
+        sel_flops = 2 * 2 * d * visible
+        kept = int(klen_tail.sum().item()) + Hkv * tail
+        sparse_bytes = 2 * kept * d * 2 + kept * 4 + 2 * Hq * d * 2 + Hq * 4
+        std = {"workload": "std-prefill-select-25k", "select_us": round(select_us, 2),
+               "select_tflops": round(sel_flops / (select_us * 1e-6) / 1e12, 1),
+               "select_mfma_frac": round(sel_flops / (select_us * 1e-6) / 1e12 /
+                                         MFMA_BF16_PEAK_TFS, 4),
+               "select_gexp_per_s": round(2 * visible / (select_us * 1e-6) / 1e9, 1),
+               "sparse_us": round(sparse_us, 3),
+               "sparse_gbs": round(sparse_bytes / (sparse_us * 1e-6) / 1e9, 1),
+               "sparse_steps_per_s": round(1e6 / sparse_us, 1),
+               "kept_per_head": round(kept / Hkv, 1)}
+        del kv_s
+
     # ---- algorithmic bytes (per call)
     kv_bytes = 2 * L * Hkv * d * 2
     verify_bytes = kv_bytes + 2 * (n * Hq * d * 2) + n * Hq * 4
@@ -347,6 +409,7 @@ def main():
         "hsr_tflops": round(hsr_flops / (parts["hsr_us"] * 1e-6) / 1e12, 2)
         if "hsr_us" in parts else None,
         "batched_draft": c5,
+        "std": std,
         "verify_max_abs_err_vs_oracle": err,
         "roofline": roof,
         "cpu_baseline": cpu,

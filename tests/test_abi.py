@@ -144,3 +144,36 @@ def test_debug_mode_leaves_host_checks_first(L):
                              None) == 3
     finally:
         L.spec_set_debug(prev)
+
+
+def test_std_and_sparse_rejections(L):
+    kv = _kv()
+    # spec_std_select(kv, B, q_text, q_dtype, Hq, text_idx, text_len, t_max, top_k, scale,
+    #                 sel, keep, keep_len, score, ws, ws_bytes, stream)
+    assert L.spec_std_select(ctypes.byref(kv), 1, None, 1, 28, FAKE, FAKE, 8, 4, 0.1, FAKE,
+                             None, None, None, None, 0, None) == 1
+    assert L.spec_std_select(ctypes.byref(kv), 1, FAKE, 1, 28, FAKE, FAKE, 8, 4, 0.1, FAKE,
+                             FAKE, None, None, None, 0, None) == 1      # keep without keep_len
+    assert L.spec_std_select(ctypes.byref(kv), 1, FAKE, 0, 28, FAKE, FAKE, 8, 4, 0.1, FAKE,
+                             None, None, None, None, 0, None) == 3      # q dtype != kv dtype
+    assert L.spec_std_select(ctypes.byref(kv), 1, FAKE, 1, 28, FAKE, FAKE, 0, 4, 0.1, FAKE,
+                             None, None, None, None, 0, None) == 2
+    assert L.spec_std_select(ctypes.byref(kv), 1, FAKE, 1, 28, FAKE, FAKE, 8, 0, 0.1, FAKE,
+                             None, None, None, None, 0, None) == 2
+    assert L.spec_std_select(ctypes.byref(kv), 1, FAKE, 1, 27, FAKE, FAKE, 8, 4, 0.1, FAKE,
+                             None, None, None, None, 0, None) == 2
+    need = L.spec_std_select_workspace(ctypes.byref(kv), 1, 28, 8, 4)
+    assert need > 0
+    assert L.spec_std_select(ctypes.byref(kv), 1, FAKE, 1, 28, FAKE, FAKE, 8, 4, 0.1, FAKE,
+                             None, None, None, FAKE, need - 1, None) == 4
+    # spec_sparse_attn(kv, B, q, q_dtype, n_max, q_len, Hq, list, list_len, list_max,
+    #                  tail_start, tail_max, scale, out, out_dtype, lse, ws, ws_bytes, stream)
+    assert L.spec_sparse_attn(ctypes.byref(kv), 1, FAKE, 1, 1, None, 28, None, FAKE, 16, None,
+                              0, 0.1, FAKE, 1, None, None, 0, None) == 1
+    assert L.spec_sparse_attn(ctypes.byref(kv), 1, FAKE, 1, 1, None, 28, FAKE, FAKE, 0, None,
+                              0, 0.1, FAKE, 1, None, None, 0, None) == 2
+    assert L.spec_sparse_attn(ctypes.byref(kv), 1, FAKE, 1, 1, None, 28, FAKE, FAKE, 16, FAKE,
+                              -1, 0.1, FAKE, 1, None, None, 0, None) == 2
+    assert L.spec_sparse_attn(ctypes.byref(kv), 1, FAKE, 1, 10, None, 28, FAKE, FAKE, 16, None,
+                              0, 0.1, FAKE, 1, None, None, 0, None) == 5    # 70 rows > 64
+    assert L.spec_sparse_attn_workspace(ctypes.byref(kv), 1, 1, 28, 16, 8) >= 0

@@ -126,3 +126,45 @@ def test_negative_page_is_rejected(S):
     kv = KVCache(kf[1:], vf[1:], dev(c.kv_len), page_table=dev(pt), page_size=16,
                  max_len=c.max_len)
     _rejects(lambda: S.spec_verify_attn(kv, dev(c.q), scale=c.scale))
+
+
+def test_std_and_sparse_lists_are_checked(S):
+    """A text list out of order for the prefill selection, and a kept list
+    that reaches into the tail, a list longer than its row, or a tail start
+    before the stated bound.  Reached anyway, each would stay inside the
+    arrays: the positions are below kv_len and the lengths within the row."""
+    c = W.std_small(13, 2, 8, 2, 128, (600, 500), W.BF16, n_text=(12, 8), top_k=32, n=1)
+    kv = kvcache_std(c)
+    ti = c.text_idx.copy()
+    ti[0, 2], ti[0, 3] = ti[0, 3], ti[0, 2]
+    _rejects(lambda: S.spec_std_select(kv, dev(c.q_text), dev(ti), dev(c.text_len), 32,
+                                       scale=c.scale))
+    sel, keep, keep_len, _ = S.spec_std_select(kv, dev(c.q_text), dev(c.text_idx),
+                                               dev(c.text_len), 32, scale=c.scale)
+    torch.cuda.synchronize()
+    lst = np.full((2, 2, 40), -1, np.int32)
+    ln = np.full((2, 2), 10, np.int32)
+    for b in range(2):
+        for g in range(2):
+            lst[b, g, :10] = np.arange(100, 110)
+    t0 = (c.kv_len - 20).astype(np.int32)
+    q = dev(c.q)
+    S.spec_sparse_attn(kv, q, dev(lst), dev(ln), tail_start=dev(t0), tail_max=20, scale=c.scale)
+    torch.cuda.synchronize()
+    bad = lst.copy()
+    bad[1, 1, 3] = t0[1]                 # inside the tail
+    _rejects(lambda: S.spec_sparse_attn(kv, q, dev(bad), dev(ln), tail_start=dev(t0),
+                                        tail_max=20, scale=c.scale))
+    long = ln.copy()
+    long[0, 1] = 41                      # longer than the row of 40
+    _rejects(lambda: S.spec_sparse_attn(kv, q, dev(lst), dev(long), tail_start=dev(t0),
+                                        tail_max=20, scale=c.scale))
+    early = t0.copy()
+    early[0] -= 1                        # a 21-position tail with tail_max = 20
+    _rejects(lambda: S.spec_sparse_attn(kv, q, dev(lst), dev(ln), tail_start=dev(early),
+                                        tail_max=20, scale=c.scale))
+
+
+def kvcache_std(c):
+    from speculative_decoding_attention_amd import KVCache
+    return KVCache(dev(c.k), dev(c.v), dev(c.kv_len.astype(np.int32)), max_len=c.max_len)
