@@ -41,6 +41,7 @@ constexpr int kBR = 128;            // rows per workgroup
 constexpr int kRG = kBR / 16;       // 16-row groups
 constexpr int kKeysPerIter = 64;    // 4 waves x 16 keys
 constexpr float kNoMax = -3.0e38f;  // finite "no key seen yet" reference
+constexpr int kMaxChunk = 2048;     // keys per split (their rows and sums are staged in LDS)
 
 __device__ __forceinline__ size_t key_row(const StdArgs& a, int b, int g, int j) {
   if (a.page_shift >= 0) {
@@ -123,80 +124,228 @@ __device__ __forceinline__ void load_q(const StdArgs& a, const Block& k, int r16
   }
 }
 
+// Key rows of this workgroup's split: computed for a contiguous cache, read
+// from LDS (resolved once through the page table) for a paged one, so the key
+// loop issues no dependent global loads.
+template <bool PAGED>
+struct KeyRows {
+  size_t base;          // contiguous: first row of (b, g)
+  const uint32_t* row;  // paged: LDS rows of keys k0..
+  int k0;
+  __device__ __forceinline__ size_t operator()(int key) const {
+    return PAGED ? (size_t)row[key - k0] : base + (size_t)key;
+  }
+};
+
+// 2^x on the transcendental unit (v_exp_f32) without the library's
+// denormal-result fix-up: every term here is a probability-like weight, and
+// results below 2^-126 are negligible against the sums they join.
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Per-wave LDS ring of key blocks.  Each wave streams its own 16-key blocks
+// through kNSW stages filled by global_load_lds_dwordx4 (no registers in
+// flight, and the loads cannot be moved by the compiler); only the wave that
+// fills a stage reads it, so a vmcnt wait is the only synchronisation.  A
+// stage holds 16 rows of D bf16; the 16-byte chunk c of row r sits at slot
+// c ^ swz(r), which makes the operand reads (16 rows, one chunk column)
+// bank-conflict free.
+constexpr int kNSW = 3;
+
 template <int D>
-__device__ __forceinline__ void load_k(const StdArgs& a, const Block& k, int key, int q4,
-                                       u32x4_t (&kf)[D / 32]) {
-  const uint16_t* kp = reinterpret_cast<const uint16_t*>(a.k) +
-                       key_row(a, k.b, k.g, min(key, k.L - 1)) * D;
+struct Stage {
+  static constexpr int ROWB = D * 2;             // bytes per key row
+  static constexpr int CH = D / 8;               // 16-byte chunks per row
+  static constexpr int BYTES = 16 * ROWB;
+  static constexpr int NDMA = BYTES / 1024;      // 1 KB DMA instructions per stage
+  static constexpr int RPD = 1024 / ROWB;        // rows per DMA instruction
+  __device__ static __forceinline__ int swz(int r) {
+    return CH == 16 ? (r & 15) : ((r >> 1) & 7);
+  }
+};
+
+template <int D, bool PAGED>
+__device__ __forceinline__ void issue_stage(const StdArgs& a, const KeyRows<PAGED>& kr, int kb,
+                                            int kend, uint32_t lds, int lane) {
+  using St = Stage<D>;
+  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(a.k);
 #pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks) kf[ks] = ld16(kp + 32 * ks + 8 * q4);
+  for (int j = 0; j < St::NDMA; ++j) {
+    const int row = j * St::RPD + lane / St::CH;
+    const int chunk = (lane % St::CH) ^ St::swz(row);
+    const int key = min(kb + row, kend - 1);           // a row that exists
+    dma16(kbase + kr(key) * St::ROWB + chunk * 16, lds + (uint32_t)(j * 1024));
+  }
 }
 
-template <int D, int PASS>
+// This lane's operand for chunk c: row r16 of the stage.
+template <int D>
+__device__ __forceinline__ u32x4_t read_op(const unsigned char* stage, int r16, int c) {
+  using St = Stage<D>;
+  return *reinterpret_cast<const u32x4_t*>(stage + r16 * St::ROWB + 16 * (c ^ St::swz(r16)));
+}
+
+template <int D>
+__device__ __forceinline__ void read_block(const unsigned char* stage, int r16, int q4,
+                                           u32x4_t (&kc)[D / 32]) {
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) kc[ks] = read_op<D>(stage, r16, 4 * ks + q4);
+}
+
+// Waits until at most N of this wave's vector memory operations are pending.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+// Pass A on one 16-key block: S^T = K Q^T, lane (r16, q4) holds keys
+// kb + 4*q4 + i of row 16*rg + r16; per-lane lazily re-referenced sums.
+template <int D>
+__device__ __forceinline__ void tile_rows(const StdArgs& a, const u32x4_t (&kc)[D / 32],
+                                          const bf16x8_t (&qop)[kRG][D / 32], int kb,
+                                          bool need_mask, int q4, const int (&pos)[kRG],
+                                          float (&m)[kRG], float (&l)[kRG]) {
+#pragma unroll
+  for (int rg = 0; rg < kRG; ++rg) {
+    f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks)
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kc[ks]), qop[rg][ks], c, 0, 0, 0);
+    float sv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sv[i] = c[i];
+      if (need_mask) sv[i] = (kb + 4 * q4 + i <= pos[rg]) ? sv[i] : -INFINITY;
+    }
+    // the scale is positive, so the maximum can be taken before scaling
+    const float tmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])) * a.scale_log2;
+    // lazily raised reference: terms stay <= 2^8 and rescales are rare
+    if (tmax > m[rg] + 8.f) {
+      l[rg] *= ex2(m[rg] - tmax);
+      m[rg] = tmax;
+    }
+    const float nm = -m[rg];
+    l[rg] += (ex2(fmaf(sv[0], a.scale_log2, nm)) + ex2(fmaf(sv[1], a.scale_log2, nm))) +
+             (ex2(fmaf(sv[2], a.scale_log2, nm)) + ex2(fmaf(sv[3], a.scale_log2, nm)));
+  }
+}
+
+// Pass B on one 16-key block: S = Q K^T, lane (r16, q4) holds rows
+// 16*rg + 4*q4 + i of key kb + r16; returns the key's sum over the 128 rows.
+template <int D>
+__device__ __forceinline__ float tile_keys(const StdArgs& a, const u32x4_t (&kc)[D / 32],
+                                           const bf16x8_t (&qop)[kRG][D / 32], int key,
+                                           bool need_mask, int q4, const int* s_pos,
+                                           const float (&crow)[kRG][4]) {
+  float acc = 0.f;
+#pragma unroll
+  for (int rg = 0; rg < kRG; ++rg) {
+    f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks)
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qop[rg][ks], as_bf16x8(kc[ks]), c, 0, 0, 0);
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = ex2(fmaf(c[i], a.scale_log2, -crow[rg][i]));
+    if (need_mask) {
+      const int4 pr = *reinterpret_cast<const int4*>(&s_pos[rg * 16 + 4 * q4]);
+      p[0] = (key <= pr.x) ? p[0] : 0.f;
+      p[1] = (key <= pr.y) ? p[1] : 0.f;
+      p[2] = (key <= pr.z) ? p[2] : 0.f;
+      p[3] = (key <= pr.w) ? p[3] : 0.f;
+    }
+    acc += (p[0] + p[1]) + (p[2] + p[3]);
+  }
+  return sum_across_rows(acc);
+}
+
+template <int D, int PASS, bool PAGED>
 __global__ __launch_bounds__(256, 2) void std_mfma_kernel(StdArgs a) {
   constexpr int KS = D / 32;
+  using St = Stage<D>;
+  __shared__ __align__(16) unsigned char ring[4 * kNSW * St::BYTES];
   __shared__ __align__(16) int s_pos[kBR];
   __shared__ float s_c[kBR];
   __shared__ float s_m[4][kBR], s_l[4][kBR];
+  __shared__ uint32_t s_row[PAGED ? kMaxChunk : 1];
+  __shared__ float s_out[PASS == 1 ? kMaxChunk : 1];
 
   Block k;
   if (!decode_block(a, k)) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // wave-uniform values live in scalar registers, so the key loop is a plain
+  // scalar loop
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, q4 = lane >> 4;
   stage_positions(a, k, s_pos);
   if (PASS == 1) stage_offsets(a, k, s_c);
+  KeyRows<PAGED> kr;
+  kr.base = ((size_t)k.b * a.Hkv + k.g) * (size_t)a.max_len;
+  kr.row = s_row;
+  kr.k0 = k.k0;
+  if (PAGED) {
+    for (int j = k.k0 + (int)threadIdx.x; j < k.k1; j += blockDim.x)
+      s_row[j - k.k0] = (uint32_t)key_row(a, k.b, k.g, j);
+  }
   bf16x8_t qop[kRG][KS];
   load_q<D>(a, k, r16, q4, qop);
   __syncthreads();
+  wait_vm<0>();                 // the ring's wait counts below start from zero
 
   const int nrow = min(k.rows - k.r0, kBR);
-  const int p_max = s_pos[nrow - 1];
-  const int p_min = (nrow < kBR) ? -1 : s_pos[0];     // -1: padded rows need the mask
+  const int p_max = __builtin_amdgcn_readfirstlane(s_pos[nrow - 1]);
+  const int p_min = (nrow < kBR) ? -1 : __builtin_amdgcn_readfirstlane(s_pos[0]);
   const int kend = min(k.k1, p_max + 1);               // no row sees a key at or past this
+  // (p_min = -1: padded rows need the mask everywhere)
 
+  // Key blocks of this wave: kb = k0 + 16*wave + 64*i < kend.  Stage i%kNSW
+  // of the wave's ring holds block i; kNSW-1 blocks are in flight while one
+  // is computed.  Every loaded row is clamped to key kend-1 (a row that
+  // exists); keys past it are masked by position.
+  const unsigned char* wring = ring + wave * kNSW * St::BYTES;
+  const uint32_t wring_lds = (uint32_t)(size_t)(lds_u8_t*)wring;
+  const int kb0 = k.k0 + 16 * wave;
+  const int nblk = (kend > kb0) ? (kend - kb0 + kKeysPerIter - 1) / kKeysPerIter : 0;
+
+  float m[kRG], l[kRG];
+  int pos[kRG];
+  float crow[kRG][4];
   if (PASS == 0) {
-    int pos[kRG];
-    float m[kRG], l[kRG];
 #pragma unroll
     for (int rg = 0; rg < kRG; ++rg) {
       pos[rg] = s_pos[rg * 16 + r16];
       m[rg] = kNoMax;
       l[rg] = 0.f;
     }
-    int kb = k.k0 + 16 * wave;
-    u32x4_t kc[KS];
-    if (kb < kend) load_k<D>(a, k, kb + r16, q4, kc);
-    for (; kb < kend; kb += kKeysPerIter) {
-      u32x4_t kn[KS];
-      const bool more = kb + kKeysPerIter < kend;
-      if (more) load_k<D>(a, k, kb + kKeysPerIter + r16, q4, kn);
-      const bool need_mask = kb + 15 > p_min;
+  } else {
 #pragma unroll
-      for (int rg = 0; rg < kRG; ++rg) {
-        f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+    for (int rg = 0; rg < kRG; ++rg)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kc[ks]), qop[rg][ks], c, 0, 0, 0);
-        float sv[4];
+      for (int i = 0; i < 4; ++i) crow[rg][i] = s_c[rg * 16 + 4 * q4 + i];
+  }
+
+  if (nblk > 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sv[i] = c[i] * a.scale_log2;
-          if (need_mask) sv[i] = (kb + 4 * q4 + i <= pos[rg]) ? sv[i] : -INFINITY;
-        }
-        const float tmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-        // lazily raised reference: terms stay <= 2^8 and rescales are rare
-        if (tmax > m[rg] + 8.f) {
-          l[rg] *= exp2f(m[rg] - tmax);
-          m[rg] = tmax;
-        }
-        l[rg] += (exp2f(sv[0] - m[rg]) + exp2f(sv[1] - m[rg])) +
-                 (exp2f(sv[2] - m[rg]) + exp2f(sv[3] - m[rg]));
-      }
-      if (more) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kc[ks] = kn[ks];
+    for (int i = 0; i < kNSW - 1; ++i)
+      issue_stage<D, PAGED>(a, kr, kb0 + i * kKeysPerIter, kend,
+                            wring_lds + (uint32_t)(i * St::BYTES), lane);
+    for (int i = 0; i < nblk; ++i) {
+      const int nxt = i + kNSW - 1;                      // always issued, clamped
+      issue_stage<D, PAGED>(a, kr, kb0 + nxt * kKeysPerIter, kend,
+                            wring_lds + (uint32_t)((nxt % kNSW) * St::BYTES), lane);
+      wait_vm<(kNSW - 1) * St::NDMA>();                  // block i has landed
+      const int kb = kb0 + i * kKeysPerIter;
+      u32x4_t kc[KS];
+      read_block<D>(wring + (i % kNSW) * St::BYTES, r16, q4, kc);
+      if (PASS == 0) {
+        tile_rows<D>(a, kc, qop, kb, kb + 15 > p_min, q4, pos, m, l);
+      } else {
+        const float acc = tile_keys<D>(a, kc, qop, kb + r16, kb + 15 > p_min, q4, s_pos, crow);
+        if (q4 == 0) s_out[kb + r16 - k.k0] = acc;
       }
     }
+    wait_vm<0>();                // no DMA into the ring outlives the loop
+  }
+
+  if (PASS == 0) {
     // the four lanes of a row, then the four waves, in a fixed order
 #pragma unroll
     for (int rg = 0; rg < kRG; ++rg) {
@@ -222,50 +371,12 @@ __global__ __launch_bounds__(256, 2) void std_mfma_kernel(StdArgs a) {
       a.ml[((size_t)k.u * a.S + k.s) * a.RBP + k.r0 + r] = make_float2(M, Ls);
     }
   } else {
-    float crow[kRG][4];
-#pragma unroll
-    for (int rg = 0; rg < kRG; ++rg)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) crow[rg][i] = s_c[rg * 16 + 4 * q4 + i];
+    // the split's keys: computed blocks from LDS, keys no row sees as 0
+    __syncthreads();
     float* out = a.colsum + ((size_t)k.u * a.RB + k.rb) * a.max_len;
-    int kb = k.k0 + 16 * wave;
-    u32x4_t kc[KS];
-    if (kb < kend) load_k<D>(a, k, kb + r16, q4, kc);
-    for (; kb < kend; kb += kKeysPerIter) {
-      u32x4_t kn[KS];
-      const bool more = kb + kKeysPerIter < kend;
-      if (more) load_k<D>(a, k, kb + kKeysPerIter + r16, q4, kn);
-      const bool need_mask = kb + 15 > p_min;
-      const int key = kb + r16;
-      float acc = 0.f;
-#pragma unroll
-      for (int rg = 0; rg < kRG; ++rg) {
-        f32x4_t c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qop[rg][ks], as_bf16x8(kc[ks]), c, 0, 0, 0);
-        float p[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) p[i] = exp2f(c[i] * a.scale_log2 - crow[rg][i]);
-        if (need_mask) {
-          const int4 pr = *reinterpret_cast<const int4*>(&s_pos[rg * 16 + 4 * q4]);
-          p[0] = (key <= pr.x) ? p[0] : 0.f;
-          p[1] = (key <= pr.y) ? p[1] : 0.f;
-          p[2] = (key <= pr.z) ? p[2] : 0.f;
-          p[3] = (key <= pr.w) ? p[3] : 0.f;
-        }
-        acc += (p[0] + p[1]) + (p[2] + p[3]);
-      }
-      acc = sum_across_rows(acc);
-      if (q4 == 0 && key < k.k1) out[key] = acc;
-      if (more) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kc[ks] = kn[ks];
-      }
-    }
-    // keys of the split that no row of the block sees
     const int kcov = k.k0 + ((max(kend - k.k0, 0) + 15) / 16) * 16;
-    for (int j = kcov + (int)threadIdx.x; j < k.k1; j += blockDim.x) out[j] = 0.f;
+    for (int j = k.k0 + (int)threadIdx.x; j < k.k1; j += blockDim.x)
+      out[j] = (j < kcov) ? s_out[j - k.k0] : 0.f;
   }
 }
 
@@ -347,10 +458,14 @@ __global__ __launch_bounds__(256) void std_scalar_kernel(StdArgs a) {
 
 template <int D>
 hipError_t launch_passes(const StdArgs& a, int dtype, int grid, hipStream_t stream) {
-  if (dtype == SPEC_BF16) {
-    hipLaunchKernelGGL((std_mfma_kernel<D, 0>), dim3(grid), dim3(256), 0, stream, a);
+  if (dtype == SPEC_BF16 && a.page_shift >= 0) {
+    hipLaunchKernelGGL((std_mfma_kernel<D, 0, true>), dim3(grid), dim3(256), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-    hipLaunchKernelGGL((std_mfma_kernel<D, 1>), dim3(grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((std_mfma_kernel<D, 1, true>), dim3(grid), dim3(256), 0, stream, a);
+  } else if (dtype == SPEC_BF16) {
+    hipLaunchKernelGGL((std_mfma_kernel<D, 0, false>), dim3(grid), dim3(256), 0, stream, a);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    hipLaunchKernelGGL((std_mfma_kernel<D, 1, false>), dim3(grid), dim3(256), 0, stream, a);
   } else {
     hipLaunchKernelGGL((std_scalar_kernel<D, 0>), dim3(grid), dim3(256), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
@@ -373,6 +488,7 @@ StdPlan plan_std(int units, int max_len, int t_max, int G, int top_k) {
   const long smax = (max_len + 255) / 256;
   if (S > smax) S = smax;
   if (S < 1) S = 1;
+  if (S < (max_len + kMaxChunk - 1) / kMaxChunk) S = (max_len + kMaxChunk - 1) / kMaxChunk;
   long chunk = (max_len + S - 1) / S;
   chunk = ((chunk + kKeysPerIter - 1) / kKeysPerIter) * kKeysPerIter;
   p.chunk = (int)chunk;
