@@ -27,6 +27,9 @@ exact (widened) values of the stored inputs:
   text positions (Sparse-to-Dense pt explainer, "Seleção de Cache KV").
 * ``sparse_attention``  -- the sparse draft attention over such a per-head
   list plus the positions written since (same page, "Metodologia").
+* ``commit``            -- the bookkeeping that follows acceptance: keep
+  the accepted rows of the cache, roll back the rest, append the emitted
+  tokens and the new text positions (same page, decoding procedure).
 * ``accept``            -- greedy acceptance: longest prefix of draft tokens that
   match the dense model's argmax, plus one bonus token (Sparse-to-Dense pt
   explainer, "Metodologia", decoding procedure).
@@ -39,10 +42,10 @@ definition rather than the pages; its selection and attention steps are pinned.
 from .attention import (verify_attention, vata_attention, topk_scores, topk_select,
                         topk_attention, paged_rows)
 from .hsr import hsr_fuse, hsr_fuse_loops
-from .accept import accept, argmax_lowest
+from .accept import accept, argmax_lowest, commit
 from .std import sparse_attention, std_keep_list, std_prefill_scores, std_prefill_select
 
 __all__ = ["verify_attention", "vata_attention", "topk_scores", "topk_select",
            "topk_attention", "paged_rows", "hsr_fuse", "hsr_fuse_loops", "accept",
-           "argmax_lowest", "std_prefill_scores", "std_prefill_select", "std_keep_list",
+           "argmax_lowest", "commit", "std_prefill_scores", "std_prefill_select", "std_keep_list",
            "sparse_attention"]
