@@ -10,6 +10,7 @@
  *             selection once, then attention)           spec_sparse_attn
  *   verify:  gamma+1 rows against the full KV cache     spec_verify_attn
  *   accept:  argmax + longest matching prefix           spec_accept
+ *   commit:  keep the accepted rows, append tokens      spec_commit
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -297,6 +298,35 @@ spec_status_t spec_accept(const void* logits, int32_t dtype, int32_t batch, int3
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* spec_status_str(spec_status_t status);
+
+/*
+ * spec_commit -- the bookkeeping that follows acceptance, on the device, so a
+ * whole speculative round needs no host synchronisation (Sparse-to-Dense,
+ * "Metodologia": the accepted tokens and the bonus token join the context).
+ *
+ * Convention: during verification sequence b's cache held kv_len[b]
+ * positions, the last gamma_b + 1 of them the verified rows (the last
+ * committed token at C = kv_len[b] - gamma_b - 1, then the drafts); n =
+ * accept_len[b] and next_tok[b] come from spec_accept.  Rows C..C+n stay
+ * valid and the rest is rolled back (their contents are simply overwritten
+ * later):
+ *   kv_len[b]   <- C + n + 1                       (in/out)
+ *   last_tok[b] <- next_tok[b]   (its K/V is written by the next round)
+ *   tokens[b, tok_len[b] + i] <- draft[b, i] for i < n, then next_tok[b];
+ *                  tok_len[b] += n + 1            (stops at tok_cap)
+ *   text_idx[b, text_len[b] + i] <- C + i for i <= n;
+ *                  text_len[b] += n + 1           (stops at t_max)
+ * draft: [B, n_max-1]; gamma: [B] or NULL (n_max-1), as for spec_accept.
+ * last_tok, tokens (with tok_len) and text_idx (with text_len) may be NULL.
+ * Preconditions: gamma_b + 1 <= kv_len[b]; 0 <= accept_len[b] <= gamma_b.
+ * Paged caches: pages past the new length stay with the caller's allocator.
+ */
+spec_status_t spec_commit(int32_t batch, int32_t n_max, const int32_t* draft,
+                          const int32_t* gamma, const int32_t* accept_len,
+                          const int32_t* next_tok, int32_t* kv_len, int32_t* last_tok,
+                          int32_t* tokens, int32_t* tok_len, int32_t tok_cap,
+                          int32_t* text_idx, int32_t* text_len, int32_t t_max,
+                          hipStream_t stream);
 
 /* SPEC_ABI_VERSION of the loaded library. */
 int32_t spec_abi_version(void);

@@ -4,11 +4,11 @@ Python entry points with the names of the C ABI (include/specattn.h); each
 marshals torch device tensors into one call of libspecattn.so.
 """
 from ._binding import (SPEC_BF16, SPEC_F32, SPEC_WS_SYNC_BYTES, KVCache, SpecError, Workspace, lib, load_library,
-                       spec_abi_version, spec_accept, spec_hsr_fuse, spec_set_debug, spec_sparse_attn,
+                       spec_abi_version, spec_accept, spec_commit, spec_hsr_fuse, spec_set_debug, spec_sparse_attn,
                        spec_status_str, spec_std_select, spec_topk_attn, spec_vata_attn,
                        spec_verify_attn)
 
 __all__ = ["SPEC_BF16", "SPEC_F32", "SPEC_WS_SYNC_BYTES", "KVCache", "SpecError", "Workspace", "lib", "load_library",
-           "spec_abi_version", "spec_accept", "spec_hsr_fuse", "spec_set_debug", "spec_sparse_attn",
+           "spec_abi_version", "spec_accept", "spec_commit", "spec_hsr_fuse", "spec_set_debug", "spec_sparse_attn",
            "spec_status_str", "spec_std_select", "spec_topk_attn", "spec_vata_attn",
            "spec_verify_attn"]

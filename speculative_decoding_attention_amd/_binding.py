@@ -60,6 +60,7 @@ SIGNATURES = {
     "spec_sparse_attn_workspace": (_S, [_KVP, _I, _I, _I, _I, _I]),
     "spec_sparse_attn": (_I, [_KVP, _I, _P, _I, _I, _P, _I, _P, _P, _I, _P, _I, _F, _P, _I, _P,
                               _P, _S, _P]),
+    "spec_commit": (_I, [_I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _I, _P]),
     "spec_abi_version": (_I, []),
     "spec_set_debug": (_I, [_I]),
 }
@@ -412,6 +413,30 @@ def spec_accept(logits: torch.Tensor, draft: torch.Tensor, gamma: Optional[torch
                        _stream(dev))
     _check("spec_accept", st)
     return target_tok, accept_len, next_tok
+
+
+def spec_commit(draft: torch.Tensor, accept_len: torch.Tensor, next_tok: torch.Tensor,
+                kv_len: torch.Tensor, gamma: Optional[torch.Tensor] = None,
+                last_tok: Optional[torch.Tensor] = None, tokens: Optional[torch.Tensor] = None,
+                tok_len: Optional[torch.Tensor] = None, text_idx: Optional[torch.Tensor] = None,
+                text_len: Optional[torch.Tensor] = None) -> None:
+    """Post-acceptance bookkeeping on the device; updates kv_len (and the
+    optional last_tok, tokens/tok_len, text_idx/text_len) in place."""
+    L = lib()
+    _dev(draft, "draft", torch.int32)
+    for t, name in ((accept_len, "accept_len"), (next_tok, "next_tok"), (kv_len, "kv_len")):
+        _dev(t, name, torch.int32)
+    for t, name in ((gamma, "gamma"), (last_tok, "last_tok"), (tokens, "tokens"),
+                    (tok_len, "tok_len"), (text_idx, "text_idx"), (text_len, "text_len")):
+        if t is not None:
+            _dev(t, name, torch.int32)
+    B, g = draft.shape
+    st = L.spec_commit(B, g + 1, _ptr(draft), _ptr(gamma), _ptr(accept_len), _ptr(next_tok),
+                       _ptr(kv_len), _ptr(last_tok), _ptr(tokens), _ptr(tok_len),
+                       int(tokens.shape[1]) if tokens is not None else 0, _ptr(text_idx),
+                       _ptr(text_len), int(text_idx.shape[1]) if text_idx is not None else 0,
+                       _stream(kv_len.device))
+    _check("spec_commit", st)
 
 
 def spec_status_str(status: int) -> str:

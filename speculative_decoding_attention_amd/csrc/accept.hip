@@ -177,7 +177,41 @@ AcceptPlan plan_accept(int batch, int n_max, int vocab, bool bf16) {
   return p;
 }
 
+// One workgroup per sequence.  Thread 0 reads the round's lengths and
+// hands them to the others through LDS before it overwrites them.
+__global__ __launch_bounds__(64) void commit_kernel(CommitArgs a) {
+  __shared__ int s_v[4];
+  const int b = blockIdx.x;
+  if (threadIdx.x == 0) {
+    const int gam = a.gamma ? a.gamma[b] : a.n_max - 1;
+    s_v[0] = a.kv_len[b] - gam - 1;                 // C: the last committed token's row
+    s_v[1] = a.accept_len[b];
+    s_v[2] = a.tokens ? a.tok_len[b] : 0;
+    s_v[3] = a.text_idx ? a.text_len[b] : 0;
+  }
+  __syncthreads();
+  const int C = s_v[0], n = s_v[1], t0 = s_v[2], x0 = s_v[3];
+  const int nxt = a.next_tok[b];
+  for (int i = threadIdx.x; i <= n; i += blockDim.x) {
+    if (a.tokens && t0 + i < a.tok_cap)
+      a.tokens[(size_t)b * a.tok_cap + t0 + i] =
+          (i < n) ? a.draft[(size_t)b * (a.n_max - 1) + i] : nxt;
+    if (a.text_idx && x0 + i < a.t_max) a.text_idx[(size_t)b * a.t_max + x0 + i] = C + i;
+  }
+  if (threadIdx.x == 0) {
+    a.kv_len[b] = C + n + 1;
+    if (a.last_tok) a.last_tok[b] = nxt;
+    if (a.tokens) a.tok_len[b] = min(t0 + n + 1, a.tok_cap);
+    if (a.text_idx) a.text_len[b] = min(x0 + n + 1, a.t_max);
+  }
+}
+
 }  // namespace
+
+spec_status_t launch_commit(const CommitArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(commit_kernel, dim3((unsigned)a.B), dim3(64), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
 
 size_t accept_workspace(int batch, int n_max, int vocab) {
   const AcceptPlan a = plan_accept(batch, n_max, vocab, true);

@@ -338,6 +338,37 @@ spec_status_t spec_sparse_attn(const spec_kv_t* kv, int32_t batch, const void* q
   return launch_attention(a, kv->head_dim, kv->dtype, plan, ws, stream);
 }
 
+// ------------------------------------------------------------- commit ----
+
+spec_status_t spec_commit(int32_t batch, int32_t n_max, const int32_t* draft,
+                          const int32_t* gamma, const int32_t* accept_len,
+                          const int32_t* next_tok, int32_t* kv_len, int32_t* last_tok,
+                          int32_t* tokens, int32_t* tok_len, int32_t tok_cap,
+                          int32_t* text_idx, int32_t* text_len, int32_t t_max,
+                          hipStream_t stream) {
+  if (!accept_len || !next_tok || !kv_len) return SPEC_ERR_NULL;
+  if (n_max > 1 && !draft) return SPEC_ERR_NULL;
+  if ((tokens && !tok_len) || (text_idx && !text_len)) return SPEC_ERR_NULL;
+  if (batch < 1 || n_max < 1 || batch > (1 << 24)) return SPEC_ERR_SHAPE;
+  if ((tokens && tok_cap < 1) || (text_idx && t_max < 1)) return SPEC_ERR_SHAPE;
+  CommitArgs a;
+  a.B = batch;
+  a.n_max = n_max;
+  a.draft = draft;
+  a.gamma = gamma;
+  a.accept_len = accept_len;
+  a.next_tok = next_tok;
+  a.kv_len = kv_len;
+  a.last_tok = last_tok;
+  a.tokens = tokens;
+  a.tok_len = tok_len;
+  a.tok_cap = tok_cap;
+  a.text_idx = text_idx;
+  a.text_len = text_len;
+  a.t_max = t_max;
+  return launch_commit(a, stream);
+}
+
 // ---------------------------------------------------------------- HSR ----
 
 size_t spec_hsr_fuse_workspace(int32_t m, int32_t d_model) {

@@ -140,6 +140,24 @@ spec_status_t launch_accept(const void* logits, int dtype, int batch, int n_max,
                             int32_t* accept_len, int32_t* next_tok, void* ws,
                             hipStream_t stream);
 
+// Bookkeeping after acceptance (spec_commit).
+struct CommitArgs {
+  int32_t B, n_max;
+  const int32_t* draft;        // [B, n_max-1]
+  const int32_t* gamma;        // [B] or null (n_max-1)
+  const int32_t* accept_len;
+  const int32_t* next_tok;
+  int32_t* kv_len;             // in: verification length; out: committed length
+  int32_t* last_tok;           // may be null
+  int32_t* tokens;             // [B, tok_cap] or null
+  int32_t* tok_len;
+  int32_t tok_cap;
+  int32_t* text_idx;           // [B, t_max] or null
+  int32_t* text_len;
+  int32_t t_max;
+};
+spec_status_t launch_commit(const CommitArgs& a, hipStream_t stream);
+
 // Debug-mode checks of device index arrays (see validate.hip).  Null
 // pointers and zero counts skip the corresponding check.
 struct ValidateArgs {

@@ -177,3 +177,18 @@ def test_std_and_sparse_rejections(L):
     assert L.spec_sparse_attn(ctypes.byref(kv), 1, FAKE, 1, 10, None, 28, FAKE, FAKE, 16, None,
                               0, 0.1, FAKE, 1, None, None, 0, None) == 5    # 70 rows > 64
     assert L.spec_sparse_attn_workspace(ctypes.byref(kv), 1, 1, 28, 16, 8) >= 0
+
+
+def test_commit_rejections(L):
+    # spec_commit(B, n_max, draft, gamma, accept_len, next_tok, kv_len, last_tok, tokens,
+    #             tok_len, tok_cap, text_idx, text_len, t_max, stream)
+    assert L.spec_commit(1, 6, FAKE, None, None, FAKE, FAKE, None, None, None, 0, None, None, 0,
+                         None) == 1
+    assert L.spec_commit(1, 6, None, None, FAKE, FAKE, FAKE, None, None, None, 0, None, None, 0,
+                         None) == 1                      # drafts needed when n_max > 1
+    assert L.spec_commit(1, 6, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, None, 4, None, None, 0,
+                         None) == 1                      # tokens without tok_len
+    assert L.spec_commit(0, 6, FAKE, None, FAKE, FAKE, FAKE, None, None, None, 0, None, None, 0,
+                         None) == 2
+    assert L.spec_commit(1, 6, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, FAKE, 0, None, None, 0,
+                         None) == 2                      # tokens with no capacity
