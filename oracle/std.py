@@ -16,7 +16,8 @@ the page is silent:
   text list.  Ties rank by lower index; the kept list is ascending.
 * Decoding then attends to the kept list plus every position written after
   the prefill (``tail_start[b] <= j < kv_len[b]``), under the usual causal
-  mask.
+  mask.  The same call with per-head anchor lists and a sliding window of
+  the last W positions gives the text-anchored window variants.
 """
 from __future__ import annotations
 
@@ -109,13 +110,17 @@ def std_keep_list(sel, text_idx, text_len):
 
 
 def sparse_attention(q, k, v, kv_len, q_len, list_idx, list_len, tail_start, num_kv_heads: int,
-                     scale: float, page_table=None, page_size: int = 0):
+                     scale: float, page_table=None, page_size: int = 0, window: int = 0):
     """Draft attention over a persistent per-head position list plus a dense
     tail of recent positions.
 
-    For (b, g) the attended set is the list ``list_idx[b, g, :list_len[b, g]]``
-    (used as given) followed by ``tail_start[b] <= j < kv_len[b]``
-    (``tail_start=None``: no tail).  Query row i < q_len[b] sits at position
+    The tail of sequence b starts at ``t0 = tail_start[b]``, or, without
+    tail_start, covers the last ``window`` positions (``t0 = kv_len[b] -
+    min(window, kv_len[b])``; window 0: no tail).  For (b, g) the attended set
+    is the union of the list entries below t0,
+    ``list_idx[b, g, :list_len[b, g]]`` (used as given), and the tail
+    ``t0 <= j < kv_len[b]``: entries inside the tail count once, as tail
+    positions.  Query row i < q_len[b] sits at position
     ``P = kv_len[b] - q_len[b] + i`` and sees the members at positions <= P.
     Returns (O ``[B, n_max, Hq, d]``, LSE ``[B, n_max, Hq]``) in float64.
     """
@@ -124,12 +129,15 @@ def sparse_attention(q, k, v, kv_len, q_len, list_idx, list_len, tail_start, num
     lse = np.full((B, n_max, Hq), -np.inf, np.float64)
     for b in range(B):
         L, n = int(kv_len[b]), int(q_len[b])
-        t0 = L if tail_start is None else int(tail_start[b])
+        if tail_start is not None:
+            t0 = int(tail_start[b])
+        else:
+            t0 = L - min(int(window), L)
         kr_all = _kv_rows(k, b, L, page_table, page_size)
         vr_all = _kv_rows(v, b, L, page_table, page_size)
         for g in range(num_kv_heads):
-            members = np.concatenate([np.asarray(list_idx[b, g, :int(list_len[b, g])], np.int64),
-                                      np.arange(t0, L, dtype=np.int64)])
+            lst = np.asarray(list_idx[b, g, :int(list_len[b, g])], np.int64)
+            members = np.concatenate([lst[lst < t0], np.arange(t0, L, dtype=np.int64)])
             if members.size and (members.min() < 0 or members.max() >= L):
                 raise ValueError("attended position outside [0, kv_len)")
             kr, vr = kr_all[g][members], vr_all[g][members]

@@ -195,3 +195,35 @@ def test_sparse_attention_per_head_lists_and_tail():
                                        1, c.scale)
         assert np.array_equal(o[:, :, 2 * g:2 * g + 2], og)
         assert np.array_equal(l[:, :, 2 * g:2 * g + 2], lg)
+
+
+def test_sliding_window_is_attention_over_the_last_positions():
+    """No list, a window of W: text-anchored attention over the last W
+    positions (fewer when the sequence is shorter)."""
+    c = W.small_attn(9, 2, 4, 2, 16, 3, (40, 7), W.F32)
+    q, k, v = c.q.values, c.k.values, c.v.values
+    Wn = 12
+    o1, l1 = oracle.sparse_attention(q, k, v, c.kv_len, c.q_len, np.zeros((2, 2, 1), np.int32),
+                                     np.zeros((2, 2), np.int32), None, 2, c.scale, window=Wn)
+    ti = np.full((2, Wn), 0, np.int32)
+    tl = np.zeros(2, np.int32)
+    for b in range(2):
+        x = np.arange(max(0, c.kv_len[b] - Wn), c.kv_len[b])
+        ti[b, :len(x)] = x
+        tl[b] = len(x)
+    o2, l2 = oracle.vata_attention(q, k, v, c.kv_len, c.q_len, ti, tl, 2, c.scale)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_list_entries_inside_the_tail_count_once():
+    """Anchors that fall inside the window are the window's own positions:
+    the result equals the same call with those anchors removed."""
+    c = W.small_attn(10, 1, 4, 2, 16, 2, (50,), W.F32)
+    q, k, v = c.q.values, c.k.values, c.v.values
+    lst = np.array([[[3, 9, 41, 45, 48], [0, 44, 47, -1, -1]]], np.int32)
+    ln = np.array([[5, 3]], np.int32)
+    a = oracle.sparse_attention(q, k, v, c.kv_len, c.q_len, lst, ln, None, 2, c.scale, window=10)
+    lst2 = np.array([[[3, 9, -1, -1, -1], [0, -1, -1, -1, -1]]], np.int32)
+    b = oracle.sparse_attention(q, k, v, c.kv_len, c.q_len, lst2, np.array([[2, 1]], np.int32),
+                                np.array([40], np.int32), 2, c.scale)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
