@@ -56,7 +56,7 @@
  *   (the pool size is not known to the library); 0 <= gamma <= n_max - 1;
  *   for spec_std_select the text list is strictly ascending; for
  *   spec_sparse_attn 0 <= list_len <= list_max, list entries lie in
- *   [0, tail_start) and kv_len - tail_max <= tail_start <= kv_len.
+ *   [0, kv_len) and kv_len - tail_max <= tail_start <= kv_len.
  *   Debug calls are synchronous and must not be captured into graphs.
  *
  * Sources (the pages this library implements; titles as published):
@@ -234,18 +234,26 @@ spec_status_t spec_std_select(const spec_kv_t* kv, int32_t batch, const void* q_
  * ("Metodologia": the sparse mode of the same model attends only to the
  * selected KV entries; decoding continues with the entries written since).
  *
- * For (b, KV head g) the attended positions are
- *   list_idx[b, g, 0 .. list_len[b, g]-1]        (used as given), then
- *   tail_start[b] .. kv_len[b]-1                  (none if tail_start NULL).
+ * The tail of sequence b starts at t0 = tail_start[b]; without tail_start it
+ * is a sliding window over the last tail_max positions, t0 = kv_len[b] -
+ * min(tail_max, kv_len[b]) (tail_max = 0: no tail).  For (b, KV head g) the
+ * attended positions are the union of
+ *   list_idx[b, g, 0 .. list_len[b, g]-1] below t0  (used as given), and
+ *   t0 .. kv_len[b]-1;
+ * list entries at or past t0 are skipped (the tail already holds them).
  * Query row i < q_len[b] sits at P = kv_len[b] - q_len[b] + i and sees the
  * members at positions <= P; rows past q_len are padding (O = 0,
- * LSE = -inf), as for spec_verify_attn.
- * list_idx: device [B, Hkv, list_max] int32, entries in [0, tail_start[b])
- *           (in [0, kv_len[b]) without a tail); list_len: device [B, Hkv],
- *           0 <= list_len <= list_max.
- * tail_start: device [B] or NULL; kv_len[b] - tail_max <= tail_start[b] <=
- *           kv_len[b].  tail_max: host bound on the tail (sizes the launch;
- *           0 without a tail).
+ * LSE = -inf), as for spec_verify_attn.  Per-head anchor lists with a
+ * window give the text-anchored window variants (Sparrow's explainers name
+ * the window's size and placement as key design choices, without values);
+ * the kept lists of
+ * spec_std_select with tail_start = the prefill length give the
+ * Sparse-to-Dense decode.
+ * list_idx: device [B, Hkv, list_max] int32, entries in [0, kv_len[b]);
+ *           list_len: device [B, Hkv], 0 <= list_len <= list_max.
+ * tail_start: device [B] or NULL; with it kv_len[b] - tail_max <=
+ *           tail_start[b] <= kv_len[b].  tail_max: host bound on the tail
+ *           length (sizes the launch), or the window without tail_start.
  * q, out, lse, scale, dtypes: as spec_verify_attn.
  */
 size_t spec_sparse_attn_workspace(const spec_kv_t* kv, int32_t batch, int32_t n_max,

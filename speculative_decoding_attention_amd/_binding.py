@@ -337,7 +337,8 @@ def spec_sparse_attn(kv: KVCache, q: torch.Tensor, list_idx: torch.Tensor,
                      scale: Optional[float] = None, out_dtype: Optional[torch.dtype] = None,
                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                      want_lse: bool = True, workspace: Optional[Workspace] = None):
-    """Draft attention over per-head kept lists plus a dense tail; returns
+    """Draft attention over per-head lists plus a dense tail (from
+    tail_start, or the last tail_max positions without it); returns
     (out, lse)."""
     L = lib()
     _dev(q, "q", kv.k.dtype)
@@ -355,7 +356,7 @@ def spec_sparse_attn(kv: KVCache, q: torch.Tensor, list_idx: torch.Tensor,
     if lse is None and want_lse:
         lse = torch.empty((B, n_max, Hq), dtype=torch.float32, device=q.device)
     scale = float(d ** -0.5) if scale is None else float(scale)
-    tail_max = int(tail_max) if tail_start is not None else 0
+    tail_max = int(tail_max)
     need = L.spec_sparse_attn_workspace(ctypes.byref(kv.struct), B, n_max, Hq, list_max, tail_max)
     wsp, wsn = _workspace(workspace, q.device).get(need, q.device)
     st = L.spec_sparse_attn(ctypes.byref(kv.struct), B, _ptr(q), _dtype_code(q.dtype), n_max,

@@ -313,7 +313,6 @@ spec_status_t spec_sparse_attn(const spec_kv_t* kv, int32_t batch, const void* q
   if (st != SPEC_OK) return st;
   if (!list_idx || !list_len) return SPEC_ERR_NULL;
   if (list_max < 1 || tail_max < 0) return SPEC_ERR_SHAPE;
-  if (!tail_start) tail_max = 0;
   if ((long long)list_max + tail_max > (1 << 30)) return SPEC_ERR_SHAPE;
   AttnArgs a = make_args(kv, batch, q, n_max, q_len, num_q_heads, scale, out, out_dtype, lse);
   a.mode = 3;
@@ -321,6 +320,7 @@ spec_status_t spec_sparse_attn(const spec_kv_t* kv, int32_t batch, const void* q
   a.slot_len = list_len;
   a.slot_stride = list_max;
   a.tail_start = tail_start;
+  a.tail_window = tail_start ? 0 : tail_max;
   const AttnPlan plan =
       plan_attention(batch * kv->num_kv_heads, list_max + tail_max, a.R, kv->head_dim, true);
   st = check_ws(plan.ws_bytes, ws, ws_bytes);

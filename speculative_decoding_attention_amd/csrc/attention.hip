@@ -57,20 +57,40 @@ struct SlotMap {
   }
 };
 
+// Mode 3: first position of the tail (kv_len without a tail).
+__device__ __forceinline__ int tail_begin(const AttnArgs& a, int b, int L) {
+  return a.tail_start ? a.tail_start[b] : L - min(a.tail_window, L);
+}
+
+// Number of key slots of unit (b, g) (see AttnArgs::mode).
+__device__ __forceinline__ int unit_slots(const AttnArgs& a, int b, int g, int L) {
+  if (a.mode == 0) return L;
+  if (a.mode == 1) return a.slot_len[b];
+  if (a.mode == 2) return min(a.slot_stride, L);
+  return a.slot_len[b * a.Hkv + g] + max(0, L - tail_begin(a, b, L));
+}
+
 // Resolves slots [t_beg, t_end) of (b, g) into LDS: logical position from the
 // slot list (or the slot itself), then the physical row through the page
 // table when the cache is paged.  Rows fit 32 bits for any pool that fits in
 // device memory.
-__device__ __forceinline__ void stage_slots(const AttnArgs& a, int b, int g, int t_beg, int t_end,
-                                            int* pos, uint32_t* row) {
+__device__ __forceinline__ void stage_slots(const AttnArgs& a, int b, int g, int L, int t_beg,
+                                            int t_end, int* pos, uint32_t* row) {
   const size_t u = (size_t)b * a.Hkv + g;
   const int n_list = (a.mode == 3) ? a.slot_len[u] : 0;
+  const int t0 = (a.mode == 3) ? tail_begin(a, b, L) : 0;
   for (int t = t_beg + (int)threadIdx.x; t < t_end; t += blockDim.x) {
     int p;
+    bool skip = false;          // a list entry inside the tail: the tail has it
     if (a.mode == 0) p = t;
     else if (a.mode == 1) p = a.slots[(size_t)b * a.slot_stride + t];
-    else if (a.mode == 2 || t < n_list) p = a.slots[u * a.slot_stride + t];
-    else p = a.tail_start[b] + (t - n_list);
+    else if (a.mode == 2) p = a.slots[u * a.slot_stride + t];
+    else if (t < n_list) {
+      p = a.slots[u * a.slot_stride + t];
+      skip = p >= t0;
+    } else {
+      p = t0 + (t - n_list);
+    }
     uint32_t r;
     if (a.page_shift >= 0) {
       const int page = a.page_table[(size_t)b * a.max_pages + (p >> a.page_shift)];
@@ -79,18 +99,11 @@ __device__ __forceinline__ void stage_slots(const AttnArgs& a, int b, int g, int
     } else {
       r = ((uint32_t)b * (uint32_t)a.Hkv + (uint32_t)g) * (uint32_t)a.max_len + (uint32_t)p;
     }
-    pos[t - t_beg] = p;
+    pos[t - t_beg] = skip ? 0x7fffffff : p;     // never visible; its row is still a real one
     row[t - t_beg] = r;
   }
 }
 
-// Number of key slots of unit (b, g) (see AttnArgs::mode).
-__device__ __forceinline__ int unit_slots(const AttnArgs& a, int b, int g, int L) {
-  if (a.mode == 0) return L;
-  if (a.mode == 1) return a.slot_len[b];
-  if (a.mode == 2) return min(a.slot_stride, L);
-  return a.slot_len[b * a.Hkv + g] + (a.tail_start ? max(0, L - a.tail_start[b]) : 0);
-}
 
 // Shared epilogue: merge the 4 waves' (m, l, l_rnd, acc) in LDS in a fixed
 // order, then write the final output (S == 1) or this split's partial.
@@ -401,7 +414,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
   sm.pos = s_pos;
   sm.row = s_row;
   if (GATHER) {
-    stage_slots(a, b, g, t_beg, t_end, s_pos, s_row);
+    stage_slots(a, b, g, L, t_beg, t_end, s_pos, s_row);
     __syncthreads();
   }
 
@@ -674,7 +687,7 @@ __global__ __launch_bounds__(PipeCfg<NB>::WAVES * 64, 1) void attn_bf16_pipe_ker
   sm.pos = s_pos;
   sm.row = s_row;
   if (GATHER) {
-    stage_slots(a, b, g, t_beg, t_end, s_pos, s_row);
+    stage_slots(a, b, g, L, t_beg, t_end, s_pos, s_row);
     __syncthreads();
   }
 
@@ -855,7 +868,7 @@ __global__ __launch_bounds__(256, 1) void attn_f32_kernel(AttnArgs a) {
   sm.pos = s_pos;
   sm.row = s_row;
   if (GATHER) {
-    stage_slots(a, b, g, t_beg, t_end, s_pos, s_row);
+    stage_slots(a, b, g, L, t_beg, t_end, s_pos, s_row);
     __syncthreads();
   }
 

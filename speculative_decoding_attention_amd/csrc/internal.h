@@ -16,8 +16,8 @@ namespace spec {
 //   0  dense:        position = t,                         T_b = kv_len[b]
 //   1  text list:    position = slots[b*stride + t],       T_b = slot_len[b]
 //   2  top-K list:   position = slots[(b*Hkv+g)*stride+t], T_b = min(stride, kv_len[b])
-//   3  per-head list + tail: slots[(b*Hkv+g)*stride + t] for t < slot_len[b*Hkv+g],
-//                    then tail_start[b] + (t - slot_len[..]) up to kv_len[b]
+//   3  per-head list + tail: slots[(b*Hkv+g)*stride + t] for t < slot_len[b*Hkv+g]
+//                    (entries inside the tail skipped), then the tail positions
 struct AttnArgs {
   const void* q;
   const void* k;
@@ -30,11 +30,13 @@ struct AttnArgs {
   // Key slots of a unit: mode 0 every position below kv_len; mode 1 a list
   // per sequence (slots[b, :slot_len[b]]); mode 2 a list per unit of
   // min(slot_stride, kv_len) entries; mode 3 a list per unit
-  // (slots[u, :slot_len[u]]) followed by positions tail_start[b]..kv_len-1
-  // (no tail when tail_start is null).
+  // (slots[u, :slot_len[u]]) followed by the tail t0..kv_len-1, where t0 =
+  // tail_start[b], or kv_len - min(tail_window, kv_len) without tail_start;
+  // list entries at or past t0 are skipped (the tail holds them).
   const int32_t* slots;
   const int32_t* slot_len;
   const int32_t* tail_start;
+  int32_t tail_window;
   int32_t slot_stride;
   int32_t mode;
   int32_t B, Hq, Hkv, G, n_max, R, max_len;
@@ -175,7 +177,7 @@ struct ValidateArgs {
   const int32_t* gamma = nullptr;
   int32_t gamma_n = 0;              // gamma[b] must be in [0, gamma_n - 1]
   // per-unit lists (spec_sparse_attn): list_idx[b, g, :list_len[b, g]] in
-  // [0, tail_start[b]) (or [0, kv_len[b]) without a tail)
+  // [0, kv_len[b]); tail_start[b] in [kv_len[b] - tail_max, kv_len[b]]
   int32_t Hkv = 0;
   const int32_t* list_idx = nullptr;
   const int32_t* list_len = nullptr;

@@ -24,8 +24,8 @@ __device__ __forceinline__ void flag(bool bad) {
 // (rows <= kv_len without q_len); 0 <= text_len <= t_max and every listed
 // position in [0, kv_len) (strictly ascending when asked); pages needed
 // within max_pages and every used page-table entry >= 0; 0 <= gamma <=
-// gamma_n - 1; per-unit list lengths in [0, list_max] and entries below the
-// tail start, which lies in [kv_len - tail_max, kv_len].
+// gamma_n - 1; per-unit list lengths in [0, list_max], entries in
+// [0, kv_len), and the tail start in [kv_len - tail_max, kv_len].
 __global__ __launch_bounds__(256) void check_kernel(ValidateArgs v) {
   const int b = blockIdx.x;
   const int L = v.kv_len ? v.kv_len[b] : 0;
@@ -64,10 +64,9 @@ __global__ __launch_bounds__(256) void check_kernel(ValidateArgs v) {
     }
   }
   if (v.list_idx && v.kv_len && len_ok) {
-    int end = L;
-    if (v.tail_start) {
-      end = v.tail_start[b];
-      if (threadIdx.x == 0) flag(end < L - v.tail_max || end > L);
+    if (v.tail_start && threadIdx.x == 0) {
+      const int t0 = v.tail_start[b];
+      flag(t0 < L - v.tail_max || t0 > L);
     }
     for (int g = 0; g < v.Hkv; ++g) {
       const size_t u = (size_t)b * v.Hkv + g;
@@ -76,7 +75,7 @@ __global__ __launch_bounds__(256) void check_kernel(ValidateArgs v) {
       const int nn = min(max(n, 0), v.list_max);
       for (int i = threadIdx.x; i < nn; i += blockDim.x) {
         const int pos = v.list_idx[u * v.list_max + i];
-        flag(pos < 0 || pos >= end);
+        flag(pos < 0 || pos >= L);
       }
     }
   }

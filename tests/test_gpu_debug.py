@@ -130,8 +130,8 @@ def test_negative_page_is_rejected(S):
 
 def test_std_and_sparse_lists_are_checked(S):
     """A text list out of order for the prefill selection, and a kept list
-    that reaches into the tail, a list longer than its row, or a tail start
-    before the stated bound.  Reached anyway, each would stay inside the
+    that reaches past the sequence, a list longer than its row, or a tail
+    start before the stated bound.  Reached anyway, each would stay inside the
     arrays: the positions are below kv_len and the lengths within the row."""
     c = W.std_small(13, 2, 8, 2, 128, (600, 500), W.BF16, n_text=(12, 8), top_k=32, n=1)
     kv = kvcache_std(c)
@@ -151,8 +151,13 @@ def test_std_and_sparse_lists_are_checked(S):
     q = dev(c.q)
     S.spec_sparse_attn(kv, q, dev(lst), dev(ln), tail_start=dev(t0), tail_max=20, scale=c.scale)
     torch.cuda.synchronize()
+    inside = lst.copy()
+    inside[1, 1, 3] = t0[1]              # inside the tail: allowed, counted once
+    S.spec_sparse_attn(kv, q, dev(inside), dev(ln), tail_start=dev(t0), tail_max=20,
+                       scale=c.scale)
+    torch.cuda.synchronize()
     bad = lst.copy()
-    bad[1, 1, 3] = t0[1]                 # inside the tail
+    bad[1, 1, 3] = c.kv_len[1]           # past the sequence (row 500 of 600 exists)
     _rejects(lambda: S.spec_sparse_attn(kv, q, dev(bad), dev(ln), tail_start=dev(t0),
                                         tail_max=20, scale=c.scale))
     long = ln.copy()

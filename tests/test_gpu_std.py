@@ -212,6 +212,46 @@ def test_sparse_attn_matches_oracle(case, with_tail):
     assert_attention_close(o, l, ro, rl, c.q_len, dt, tag=str(case))
 
 
+WINDOW = [
+    # seed, B, Hq, Hkv, d, L, n, dtype, page_size, list_max, window
+    (20, 2, 8, 2, 128, (900, 700), 1, W.BF16, 0, 64, 128),
+    (21, 2, 28, 4, 128, (3000, 40), 6, W.BF16, 0, 300, 256),   # window longer than one sequence
+    (22, 2, 4, 2, 64, (500, 333), 3, W.F32, 0, 50, 32),
+    (23, 3, 8, 2, 128, (1200, 900, 64), 2, W.BF16, 16, 200, 100),
+]
+
+
+@pytest.mark.parametrize("case", WINDOW, ids=lambda c: f"s{c[0]}_d{c[4]}_{c[7]}_ps{c[8]}_w{c[10]}")
+@pytest.mark.parametrize("anchors", ["none", "shared", "per_head"])
+def test_window_variants_match_oracle(case, anchors):
+    """Text-anchored window variants: a sliding window of the last W
+    positions alone, with the same anchor list for every head, or with
+    per-head anchor lists; anchors may fall inside the window (counted
+    once)."""
+    import speculative_decoding_attention_amd as S
+    seed, B, Hq, Hkv, d, L, n, dt, ps, list_max, win = case
+    c = W.std_small(seed, B, Hq, Hkv, d, L, dt, n_text=1, page_size=ps, n=n)
+    rng = np.random.default_rng(200 + seed)
+    lst = np.full((B, Hkv, list_max), -1, np.int32)
+    ln = np.zeros((B, Hkv), np.int32)
+    if anchors != "none":
+        for b in range(B):
+            Lb = int(c.kv_len[b])
+            m = min(list_max, Lb)
+            base = np.sort(rng.choice(Lb, size=m, replace=False))
+            for g in range(Hkv):
+                x = base if anchors == "shared" else np.sort(rng.choice(Lb, size=m, replace=False))
+                lst[b, g, :m] = x
+                ln[b, g] = m
+    kv = _kv(c)
+    o, l = S.spec_sparse_attn(kv, dev(c.q), dev(lst), dev(ln), tail_start=None, tail_max=win,
+                              scale=c.scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ro, rl = oracle.sparse_attention(c.q.values, c.k.values, c.v.values, c.kv_len, c.q_len, lst,
+                                     ln, None, Hkv, c.scale, c.page_table, c.page_size, window=win)
+    assert_attention_close(o, l, ro, rl, c.q_len, dt, tag=f"{case} {anchors}")
+
+
 def test_select_then_sparse_decode_end_to_end():
     """Prefill selection followed by a decode step over the kept lists and the
     tokens written since, both on the GPU, against the same two steps of the
