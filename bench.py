@@ -55,6 +55,33 @@ def _parse():
     return ap.parse_args()
 
 
+def expected_tokens(alpha: float, gamma: int) -> float:
+    """Tokens emitted per round when each draft token is accepted
+    independently with probability alpha: the accepted prefix n has
+    P(n = k) = alpha^k (1 - alpha) for k < gamma and P(n = gamma) = alpha^gamma,
+    and every round adds the bonus token, so E = sum_k (k + 1) P(n = k) =
+    (1 - alpha^(gamma+1)) / (1 - alpha)."""
+    if alpha >= 1.0:
+        return float(gamma + 1)
+    return (1.0 - alpha ** (gamma + 1)) / (1.0 - alpha)
+
+
+def io_model(alpha, gamma, draft_us, verify_us, dense_us, draft_bytes, verify_bytes,
+             dense_bytes):
+    """Sparse-to-Dense's I/O argument for the attention of one layer: a round
+    is gamma sparse draft steps plus one dense verification of gamma + 1 rows
+    and yields expected_tokens(alpha, gamma) tokens; plain decoding reads the
+    whole cache once per token.  Returns per-token KV bytes and attention
+    time for both."""
+    e = expected_tokens(alpha, gamma)
+    return {"alpha": alpha, "gamma": gamma, "tokens_per_round": round(e, 3),
+            "kv_bytes_per_token": round((gamma * draft_bytes + verify_bytes) / e),
+            "dense_kv_bytes_per_token": dense_bytes,
+            "attn_us_per_token": round((gamma * draft_us + verify_us) / e, 3),
+            "dense_attn_us_per_token": round(dense_us, 3),
+            "attn_speedup": round(dense_us * e / (gamma * draft_us + verify_us), 3)}
+
+
 def _source_hash(names):
     h = hashlib.sha256()
     for n in names:
@@ -312,6 +339,22 @@ def main():
         sel_flops = 2 * 2 * d * visible
         kept = int(klen_tail.sum().item()) + Hkv * tail
         sparse_bytes = 2 * kept * d * 2 + kept * 4 + 2 * Hq * d * 2 + Hq * 4
+        # dense verification at gamma + 1 rows (and plain one-token decode)
+        ver_us = {}
+        for nr in (1, 4, 6, 9):
+            qn = torch.randn((B, nr, Hq, d), device=dev).to(torch.bfloat16)
+            on = torch.empty((B, nr, Hq, d), dtype=torch.bfloat16, device=dev)
+            ln = torch.empty((B, nr, Hq), dtype=torch.float32, device=dev)
+            for r in range(R):
+                S.spec_verify_attn(kvs[r], qn, scale=scale, out=on, lse=ln, workspace=wsp["verify"])
+            torch.cuda.synchronize()
+            g = capture(lambda: [S.spec_verify_attn(kvs[r], qn, scale=scale, out=on, lse=ln,
+                                                    workspace=wsp["verify"]) for r in range(R)])
+            ver_us[nr] = time_graph(g, args.reps) * 1e3 / R
+        kvb = 2 * L * Hkv * d * 2
+        model = [io_model(al, gm, sparse_us, ver_us[gm + 1], ver_us[1], sparse_bytes,
+                          kvb + 2 * (gm + 1) * Hq * d * 2, kvb + 2 * Hq * d * 2)
+                 for gm in (3, 5, 8) for al in (0.5, 0.7, 0.9)]
         std = {"workload": "std-prefill-select-25k", "select_us": round(select_us, 2),
                "select_tflops": round(sel_flops / (select_us * 1e-6) / 1e12, 1),
                "select_mfma_frac": round(sel_flops / (select_us * 1e-6) / 1e12 /
@@ -320,7 +363,11 @@ def main():
                "sparse_us": round(sparse_us, 3),
                "sparse_gbs": round(sparse_bytes / (sparse_us * 1e-6) / 1e9, 1),
                "sparse_steps_per_s": round(1e6 / sparse_us, 1),
-               "kept_per_head": round(kept / Hkv, 1)}
+               "kept_per_head": round(kept / Hkv, 1),
+               "verify_us_by_rows": {str(k): round(v, 2) for k, v in ver_us.items()},
+               "io_model": {"assumption": "each draft token accepted independently with "
+                                          "probability alpha; attention of one layer only",
+                            "rows": model}}
         del kv_s
 
     # ---- algorithmic bytes (per call)

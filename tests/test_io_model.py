@@ -1,0 +1,33 @@
+"""Pins of the acceptance-rate model used for Sparse-to-Dense's I/O
+argument (bench.py): the closed form of the expected tokens per round
+against an explicit sum over accepted-prefix lengths, its limits, and the
+per-token accounting."""
+import pytest
+
+import bench
+
+
+@pytest.mark.parametrize("gamma", [1, 3, 5, 8])
+@pytest.mark.parametrize("alpha", [0.0, 0.3, 0.7, 0.95])
+def test_expected_tokens_is_the_sum_over_prefix_lengths(alpha, gamma):
+    probs = [alpha ** k * (1 - alpha) for k in range(gamma)] + [alpha ** gamma]
+    assert sum(probs) == pytest.approx(1.0)
+    want = sum((k + 1) * p for k, p in enumerate(probs))
+    assert bench.expected_tokens(alpha, gamma) == pytest.approx(want, rel=1e-12)
+
+
+def test_limits():
+    assert bench.expected_tokens(0.0, 5) == 1.0          # only the bonus token
+    assert bench.expected_tokens(1.0, 5) == 6.0          # every draft accepted
+    assert bench.expected_tokens(0.999999, 5) == pytest.approx(6.0, rel=1e-5)
+
+
+def test_per_token_accounting():
+    r = bench.io_model(0.0, 4, draft_us=2.0, verify_us=10.0, dense_us=8.0, draft_bytes=100,
+                       verify_bytes=1000, dense_bytes=900)
+    # one token per round: 4 drafts + one verification per token
+    assert r["tokens_per_round"] == 1.0
+    assert r["kv_bytes_per_token"] == 1400 and r["attn_us_per_token"] == 18.0
+    assert r["attn_speedup"] == pytest.approx(8.0 / 18.0, abs=1e-3)
+    r = bench.io_model(1.0, 4, 2.0, 10.0, 8.0, 100, 1000, 900)
+    assert r["tokens_per_round"] == 5.0 and r["kv_bytes_per_token"] == 280
