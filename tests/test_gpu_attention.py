@@ -269,3 +269,13 @@ def test_c4_verify_sampled():
         err = np.abs(o[b, :, hs] - ro[b, :, hs]).max()
         assert err <= 1e-2 * np.abs(ro[b, :, hs]).max() and err <= 2e-2
         assert np.abs(l[b, :, hs] - rl[b, :, hs]).max() <= 1e-3
+
+
+def test_verify_and_vata_long_context():
+    """A 300,000-position sequence next to a short one (4 query rows, 4 heads
+    per group): the split plan and the merge at long length."""
+    c = W.small_attn(32, 2, 4, 1, 128, 4, (300000, 700), W.BF16, text_frac=0.01)
+    out, lse, ro, rl = _verify_pair(c)
+    assert_attention_close(out, lse, ro, rl, c.q_len, W.BF16, "long verify")
+    out, lse, ro, rl = _vata_pair(c)
+    assert_attention_close(out, lse, ro, rl, c.q_len, W.BF16, "long vata")

@@ -279,3 +279,17 @@ def test_select_then_sparse_decode_end_to_end():
     ro, rl = oracle.sparse_attention(c.q.values, c.k.values, c.v.values, c.kv_len, c.q_len, rkeep,
                                      rlen, prefill, 2, c.scale)
     assert_attention_close(o, l, ro, rl, c.q_len, W.BF16, tag="e2e")
+
+
+def test_std_select_longer_than_the_selection_bitmask():
+    """140,000 positions (past the ranking kernel's LDS bit mask) with 24 text
+    tokens, K = 1000."""
+    import speculative_decoding_attention_amd as S
+    c = W.std_small(33, 1, 4, 2, 128, (140000,), W.BF16, n_text=(24,), top_k=1000)
+    kv = _kv(c)
+    sel, keep, keep_len, score = S.spec_std_select(kv, dev(c.q_text), dev(c.text_idx),
+                                                   dev(c.text_len), c.top_k, scale=c.scale,
+                                                   want_score=True)
+    torch.cuda.synchronize()
+    _check_selection(c, sel.cpu().numpy(), keep.cpu().numpy(), keep_len.cpu().numpy(),
+                     score.cpu().numpy())

@@ -139,3 +139,13 @@ def test_topk_everything_equals_dense_decode():
     torch.cuda.synchronize()
     assert np.array_equal(sel[0, 0, :700], np.arange(700)) and np.all(sel[0, :, 700:] == -1)
     assert (out - o2).abs().max().item() <= 1e-2 * o2.abs().max().item()
+
+
+def test_topk_longer_than_the_selection_bitmask():
+    """140,000 keys: more than the 131,072 selection bits the ranking kernel
+    keeps in LDS, so the ordered output comes from its score-based path."""
+    c = W.small_attn(31, 1, 4, 1, 128, 1, (140000,), W.BF16)
+    sel, out, lse = _run(c, 512)
+    rs, ro, rl = _ref(c, 512)
+    assert np.array_equal(sel, rs)
+    assert_attention_close(out, lse, ro, rl, np.ones(1, np.int32), W.BF16, "topk long")
