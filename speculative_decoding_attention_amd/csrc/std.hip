@@ -198,55 +198,75 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 // Pass A on one 16-key block: S^T = K Q^T, lane (r16, q4) holds keys
-// kb + 4*q4 + i of row 16*rg + r16; per-lane lazily re-referenced sums.
-template <int D>
+// kb + 4*q4 + i of row 16*rg + r16; per-lane lazily re-referenced sums.  All
+// eight MFMA chains are issued before any result is used, and the code is
+// straight-line (MASK and the rare re-reference are wave-uniform branches),
+// so the matrix and vector pipes overlap.
+template <int D, bool MASK>
 __device__ __forceinline__ void tile_rows(const StdArgs& a, const u32x4_t (&kc)[D / 32],
-                                          const bf16x8_t (&qop)[kRG][D / 32], int kb,
-                                          bool need_mask, int q4, const int (&pos)[kRG],
-                                          float (&m)[kRG], float (&l)[kRG]) {
+                                          const bf16x8_t (&qop)[kRG][D / 32], int kb, int q4,
+                                          const int (&pos)[kRG], float (&m)[kRG],
+                                          float (&l)[kRG]) {
+  f32x4_t c[kRG];
 #pragma unroll
   for (int rg = 0; rg < kRG; ++rg) {
-    f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+    c[rg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks)
-      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kc[ks]), qop[rg][ks], c, 0, 0, 0);
-    float sv[4];
+      c[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kc[ks]), qop[rg][ks], c[rg], 0,
+                                                      0, 0);
+  }
+  float tmax[kRG];
+  bool raise = false;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sv[i] = c[i];
-      if (need_mask) sv[i] = (kb + 4 * q4 + i <= pos[rg]) ? sv[i] : -INFINITY;
+  for (int rg = 0; rg < kRG; ++rg) {
+    if (MASK) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c[rg][i] = (kb + 4 * q4 + i <= pos[rg]) ? c[rg][i] : -INFINITY;
     }
     // the scale is positive, so the maximum can be taken before scaling
-    const float tmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])) * a.scale_log2;
-    // lazily raised reference: terms stay <= 2^8 and rescales are rare
-    if (tmax > m[rg] + 8.f) {
-      l[rg] *= ex2(m[rg] - tmax);
-      m[rg] = tmax;
+    tmax[rg] = fmaxf(fmaxf(c[rg][0], c[rg][1]), fmaxf(c[rg][2], c[rg][3])) * a.scale_log2;
+    raise |= tmax[rg] > m[rg] + 8.f;
+  }
+  // lazily raised reference: terms stay <= 2^8 and raises are rare
+  if (__builtin_amdgcn_ballot_w64(raise)) {
+#pragma unroll
+    for (int rg = 0; rg < kRG; ++rg) {
+      const bool up = tmax[rg] > m[rg] + 8.f;
+      l[rg] = up ? l[rg] * ex2(m[rg] - tmax[rg]) : l[rg];
+      m[rg] = up ? tmax[rg] : m[rg];
     }
+  }
+#pragma unroll
+  for (int rg = 0; rg < kRG; ++rg) {
     const float nm = -m[rg];
-    l[rg] += (ex2(fmaf(sv[0], a.scale_log2, nm)) + ex2(fmaf(sv[1], a.scale_log2, nm))) +
-             (ex2(fmaf(sv[2], a.scale_log2, nm)) + ex2(fmaf(sv[3], a.scale_log2, nm)));
+    l[rg] += (ex2(fmaf(c[rg][0], a.scale_log2, nm)) + ex2(fmaf(c[rg][1], a.scale_log2, nm))) +
+             (ex2(fmaf(c[rg][2], a.scale_log2, nm)) + ex2(fmaf(c[rg][3], a.scale_log2, nm)));
   }
 }
 
 // Pass B on one 16-key block: S = Q K^T, lane (r16, q4) holds rows
 // 16*rg + 4*q4 + i of key kb + r16; returns the key's sum over the 128 rows.
-template <int D>
+template <int D, bool MASK>
 __device__ __forceinline__ float tile_keys(const StdArgs& a, const u32x4_t (&kc)[D / 32],
-                                           const bf16x8_t (&qop)[kRG][D / 32], int key,
-                                           bool need_mask, int q4, const int* s_pos,
-                                           const float (&crow)[kRG][4]) {
+                                           const bf16x8_t (&qop)[kRG][D / 32], int key, int q4,
+                                           const int* s_pos, const float (&crow)[kRG][4]) {
+  f32x4_t c[kRG];
+#pragma unroll
+  for (int rg = 0; rg < kRG; ++rg) {
+    c[rg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks)
+      c[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qop[rg][ks], as_bf16x8(kc[ks]), c[rg], 0,
+                                                      0, 0);
+  }
   float acc = 0.f;
 #pragma unroll
   for (int rg = 0; rg < kRG; ++rg) {
-    f32x4_t c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks)
-      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qop[rg][ks], as_bf16x8(kc[ks]), c, 0, 0, 0);
     float p[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = ex2(fmaf(c[i], a.scale_log2, -crow[rg][i]));
-    if (need_mask) {
+    for (int i = 0; i < 4; ++i) p[i] = ex2(fmaf(c[rg][i], a.scale_log2, -crow[rg][i]));
+    if (MASK) {
       const int4 pr = *reinterpret_cast<const int4*>(&s_pos[rg * 16 + 4 * q4]);
       p[0] = (key <= pr.x) ? p[0] : 0.f;
       p[1] = (key <= pr.y) ? p[1] : 0.f;
@@ -335,10 +355,13 @@ __global__ __launch_bounds__(256, 2) void std_mfma_kernel(StdArgs a) {
       const int kb = kb0 + i * kKeysPerIter;
       u32x4_t kc[KS];
       read_block<D>(wring + (i % kNSW) * St::BYTES, r16, q4, kc);
+      const bool mask = kb + 15 > p_min;   // wave-uniform
       if (PASS == 0) {
-        tile_rows<D>(a, kc, qop, kb, kb + 15 > p_min, q4, pos, m, l);
+        if (mask) tile_rows<D, true>(a, kc, qop, kb, q4, pos, m, l);
+        else tile_rows<D, false>(a, kc, qop, kb, q4, pos, m, l);
       } else {
-        const float acc = tile_keys<D>(a, kc, qop, kb + r16, kb + 15 > p_min, q4, s_pos, crow);
+        const float acc = mask ? tile_keys<D, true>(a, kc, qop, kb + r16, q4, s_pos, crow)
+                               : tile_keys<D, false>(a, kc, qop, kb + r16, q4, s_pos, crow);
         if (q4 == 0) s_out[kb + r16 - k.k0] = acc;
       }
     }
