@@ -368,6 +368,24 @@ def main():
                "io_model": {"assumption": "each draft token accepted independently with "
                                           "probability alpha; attention of one layer only",
                             "rows": model}}
+        sel_tfs = sel_flops / (select_us * 1e-6) / 1e12
+        std["roofline"] = {"bound": "mfma", "achieved": round(sel_tfs, 1),
+                           "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                           "frac": round(sel_tfs / MFMA_BF16_PEAK_TFS, 4), "traffic": None}
+        if not args.no_cpu_baseline and only is None:
+            # the oracle on one of the four KV heads (about 2 s), scaled to the layer
+            import oracle
+            g1 = 2
+            k1 = cs.k.values[:, g1:g1 + 1]
+            q1 = cs.q_text.values[:, :, 7 * g1:7 * g1 + 7]
+            t0 = time.perf_counter()
+            oracle.std_prefill_select(q1, k1, cs.kv_len, cs.text_idx, cs.text_len, 1, cs.top_k,
+                                      scale)
+            one = time.perf_counter() - t0
+            std["cpu_baseline"] = {"value": round(one * Hkv * 1e6, 0), "unit": "us per layer",
+                                   "kind": "oracle",
+                                   "sample": "one of 4 KV heads (512 text rows x 7 heads x "
+                                             "25,512 positions, fp64 numpy), times 4"}
         del kv_s
 
     # ---- algorithmic bytes (per call)
