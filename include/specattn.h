@@ -56,7 +56,9 @@
  *   (the pool size is not known to the library); 0 <= gamma <= n_max - 1;
  *   for spec_std_select the text list is strictly ascending; for
  *   spec_sparse_attn 0 <= list_len <= list_max, list entries lie in
- *   [0, kv_len) and kv_len - tail_max <= tail_start <= kv_len.
+ *   [0, kv_len) and kv_len - tail_max <= tail_start <= kv_len; for
+ *   spec_commit 0 <= accept_len <= gamma <= kv_len - 1, 0 <= tok_len <=
+ *   tok_cap and 0 <= text_len <= t_max.
  *   Debug calls are synchronous and must not be captured into graphs.
  *
  * Sources (the pages this library implements; titles as published):

@@ -178,16 +178,18 @@ AcceptPlan plan_accept(int batch, int n_max, int vocab, bool bf16) {
 }
 
 // One workgroup per sequence.  Thread 0 reads the round's lengths and
-// hands them to the others through LDS before it overwrites them.
+// hands them to the others through LDS before it overwrites them.  Values
+// outside their ranges (a precondition) are clamped so that every access
+// stays inside the arrays.
 __global__ __launch_bounds__(64) void commit_kernel(CommitArgs a) {
   __shared__ int s_v[4];
   const int b = blockIdx.x;
   if (threadIdx.x == 0) {
-    const int gam = a.gamma ? a.gamma[b] : a.n_max - 1;
+    const int gam = min(max(a.gamma ? a.gamma[b] : a.n_max - 1, 0), a.n_max - 1);
     s_v[0] = a.kv_len[b] - gam - 1;                 // C: the last committed token's row
-    s_v[1] = a.accept_len[b];
-    s_v[2] = a.tokens ? a.tok_len[b] : 0;
-    s_v[3] = a.text_idx ? a.text_len[b] : 0;
+    s_v[1] = min(max(a.accept_len[b], 0), gam);
+    s_v[2] = a.tokens ? max(a.tok_len[b], 0) : 0;
+    s_v[3] = a.text_idx ? max(a.text_len[b], 0) : 0;
   }
   __syncthreads();
   const int C = s_v[0], n = s_v[1], t0 = s_v[2], x0 = s_v[3];

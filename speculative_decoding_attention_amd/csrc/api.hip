@@ -351,6 +351,20 @@ spec_status_t spec_commit(int32_t batch, int32_t n_max, const int32_t* draft,
   if ((tokens && !tok_len) || (text_idx && !text_len)) return SPEC_ERR_NULL;
   if (batch < 1 || n_max < 1 || batch > (1 << 24)) return SPEC_ERR_SHAPE;
   if ((tokens && tok_cap < 1) || (text_idx && t_max < 1)) return SPEC_ERR_SHAPE;
+  if (debug_enabled()) {
+    ValidateArgs v;
+    v.B = batch;
+    v.kv_len = kv_len;
+    v.gamma = gamma;
+    v.gamma_n = n_max;
+    v.accept_len = accept_len;
+    v.tok_len = tokens ? tok_len : nullptr;
+    v.tok_cap = tok_cap;
+    v.text_len = text_idx ? text_len : nullptr;
+    v.t_max = t_max;
+    const spec_status_t st = validate(v, stream);
+    if (st != SPEC_OK) return st;
+  }
   CommitArgs a;
   a.B = batch;
   a.n_max = n_max;

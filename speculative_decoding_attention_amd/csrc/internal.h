@@ -176,6 +176,11 @@ struct ValidateArgs {
   bool text_sorted = false;         // text list strictly ascending
   const int32_t* gamma = nullptr;
   int32_t gamma_n = 0;              // gamma[b] must be in [0, gamma_n - 1]
+  // spec_commit: 0 <= accept_len[b] <= gamma_b, gamma_b + 1 <= kv_len[b]
+  // (kv_len without max_len), 0 <= tok_len <= tok_cap, 0 <= text_len <= t_max
+  const int32_t* accept_len = nullptr;
+  const int32_t* tok_len = nullptr;
+  int32_t tok_cap = 0;
   // per-unit lists (spec_sparse_attn): list_idx[b, g, :list_len[b, g]] in
   // [0, kv_len[b]); tail_start[b] in [kv_len[b] - tail_max, kv_len[b]]
   int32_t Hkv = 0;

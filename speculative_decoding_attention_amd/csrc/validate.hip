@@ -29,7 +29,8 @@ __device__ __forceinline__ void flag(bool bad) {
 __global__ __launch_bounds__(256) void check_kernel(ValidateArgs v) {
   const int b = blockIdx.x;
   const int L = v.kv_len ? v.kv_len[b] : 0;
-  const bool len_ok = !v.kv_len || (L >= 1 && L <= v.max_len);
+  // (max_len 0: no upper bound on kv_len, as for spec_commit)
+  const bool len_ok = !v.kv_len || (L >= 1 && (v.max_len == 0 || L <= v.max_len));
   if (threadIdx.x == 0) {
     flag(!len_ok);
     if (v.kv_len && v.rows > 0) {
@@ -47,6 +48,12 @@ __global__ __launch_bounds__(256) void check_kernel(ValidateArgs v) {
     if (v.gamma) {
       const int gm = v.gamma[b];
       flag(gm < 0 || gm > v.gamma_n - 1);
+    }
+    if (v.accept_len) {
+      const int gm = v.gamma ? v.gamma[b] : v.gamma_n - 1;
+      const int n = v.accept_len[b];
+      flag(n < 0 || n > gm || (v.kv_len && L < gm + 1));
+      if (v.tok_len) flag(v.tok_len[b] < 0 || v.tok_len[b] > v.tok_cap);
     }
   }
   if (v.page_table && v.kv_len && len_ok) {

@@ -173,3 +173,22 @@ def test_std_and_sparse_lists_are_checked(S):
 def kvcache_std(c):
     from speculative_decoding_attention_amd import KVCache
     return KVCache(dev(c.k), dev(c.v), dev(c.kv_len.astype(np.int32)), max_len=c.max_len)
+
+
+def test_commit_inputs_are_checked(S):
+    """An accepted prefix longer than gamma, a verification length shorter
+    than the verified rows, or an output length past its capacity.  Reached
+    anyway, the kernel clamps each of them to its range."""
+    draft = dev(np.array([[1, 2, 3], [4, 5, 6]], np.int32))
+    nxt = dev(np.array([7, 8], np.int32))
+    toks = torch.zeros((2, 5), dtype=torch.int32, device="cuda:0")
+
+    def run(acc, kv, tl):
+        S.spec_commit(draft, dev(np.array(acc, np.int32)), nxt, dev(np.array(kv, np.int32)),
+                      tokens=toks, tok_len=dev(np.array(tl, np.int32)))
+
+    run([1, 3], [10, 12], [0, 2])                 # valid
+    torch.cuda.synchronize()
+    _rejects(lambda: run([4, 0], [10, 12], [0, 2]))
+    _rejects(lambda: run([1, 0], [10, 3], [0, 2]))
+    _rejects(lambda: run([1, 0], [10, 12], [0, 6]))
