@@ -81,3 +81,29 @@ def test_hsr_and_accept_in_graphs():
     nxt = torch.empty((3,), dtype=torch.int32, device="cuda:0")
     _check_replays(lambda: S.spec_accept(logits, draft, target_tok=t, accept_len=n_acc,
                                          next_tok=nxt, workspace=ws), [t, n_acc, nxt])
+
+
+def test_std_select_and_sparse_attention_in_graphs():
+    import speculative_decoding_attention_amd as S
+    from speculative_decoding_attention_amd import KVCache
+    c = W.std_small(3, 2, 8, 2, 128, (700, 700), W.BF16, n_text=(30, 12), top_k=64, n=2)
+    kv = KVCache(dev(c.k), dev(c.v), dev(c.kv_len), max_len=c.max_len)
+    ws = S.Workspace()
+    B, Hkv, K, T = 2, 2, 64, c.t_max
+    sel = torch.empty((B, Hkv, K), dtype=torch.int32, device="cuda:0")
+    keep = torch.empty((B, Hkv, K + T), dtype=torch.int32, device="cuda:0")
+    klen = torch.empty((B, Hkv), dtype=torch.int32, device="cuda:0")
+    score = torch.empty((B, Hkv, c.max_len), dtype=torch.float32, device="cuda:0")
+    qt, ti, tl = dev(c.q_text), dev(c.text_idx), dev(c.text_len)
+    _check_replays(lambda: S.spec_std_select(kv, qt, ti, tl, K, scale=c.scale, sel_idx=sel,
+                                             keep_idx=keep, keep_len=klen, score=score,
+                                             workspace=ws), [sel, keep, klen, score])
+    q = dev(c.q)
+    o = torch.empty((B, 2, 8, 128), dtype=torch.float32, device="cuda:0")
+    lse = torch.empty((B, 2, 8), dtype=torch.float32, device="cuda:0")
+    t0 = dev(c.kv_len - 40)
+    _check_replays(lambda: S.spec_sparse_attn(kv, q, keep, klen, tail_start=t0, tail_max=40,
+                                              scale=c.scale, out=o, lse=lse, workspace=ws),
+                   [o, lse])
+    _check_replays(lambda: S.spec_sparse_attn(kv, q, keep, klen, tail_max=32, scale=c.scale,
+                                              out=o, lse=lse, workspace=ws), [o, lse])
