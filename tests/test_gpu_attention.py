@@ -279,3 +279,16 @@ def test_verify_and_vata_long_context():
     assert_attention_close(out, lse, ro, rl, c.q_len, W.BF16, "long verify")
     out, lse, ro, rl = _vata_pair(c)
     assert_attention_close(out, lse, ro, rl, c.q_len, W.BF16, "long vata")
+
+
+@pytest.mark.parametrize("page_size", [1, 2, 256])
+@pytest.mark.parametrize("G", [1, 7])
+def test_page_size_limits_and_group_sizes(page_size, G):
+    """The smallest and largest page sizes, one query head per KV head (plain
+    multi-head attention) and seven; verification and text-anchored attention."""
+    c = W.small_attn(40 + page_size + G, 2, 2 * G, 2, 128, 3, (611, 300), W.BF16,
+                     page_size=page_size)
+    out, lse, ro, rl = _verify_pair(c)
+    assert_attention_close(out, lse, ro, rl, c.q_len, W.BF16, f"verify ps{page_size} G{G}")
+    out, lse, ro, rl = _vata_pair(c)
+    assert_attention_close(out, lse, ro, rl, c.q_len, W.BF16, f"vata ps{page_size} G{G}")
