@@ -59,7 +59,8 @@
  *   [0, kv_len) and kv_len - tail_max <= tail_start <= kv_len; for
  *   spec_commit 0 <= accept_len <= gamma <= kv_len - 1, 0 <= tok_len <=
  *   tok_cap and 0 <= text_len <= t_max.
- *   Debug calls are synchronous and must not be captured into graphs.
+ *   Debug calls are synchronous, must not be captured into graphs, and must
+ *   not run concurrently on one device (their finding word is per device).
  *
  * Sources (the pages this library implements; titles as published):
  * - "Sparrow: Text-Anchored Window Attention with Visual-Semantic Glimpsing

@@ -26,6 +26,8 @@
 // The fp32 variant uses v_mfma_f32_16x16x4_f32, where V needs no transpose.
 #include <math.h>
 
+#include <atomic>
+
 #include "common.h"
 #include "internal.h"
 
@@ -1086,18 +1088,20 @@ spec_status_t launch_zero(void* p, size_t bytes, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 
+// Per-device CU count, queried once per device; calls from several host
+// threads may race to fill an entry, with the same value.
 int device_cu_count() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         n <= 0)
       n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 AttnPlan plan_attention(int units, int t_max, int rows, int d, bool gather, size_t scratch_off) {

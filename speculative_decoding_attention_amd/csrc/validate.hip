@@ -4,8 +4,12 @@
 // an entry point runs one check kernel on its stream, waits for it, and
 // returns SPEC_ERR_SHAPE instead of launching anything if a value is out of
 // range.  The wait makes such calls synchronous, so debug mode is for
-// testing, not for captured graphs.
+// testing, not for captured graphs.  The finding word is one per device,
+// so debug calls on one device must not run concurrently from several host
+// threads.
 #include <stdlib.h>
+
+#include <atomic>
 
 #include "internal.h"
 
@@ -88,21 +92,25 @@ __global__ __launch_bounds__(256) void check_kernel(ValidateArgs v) {
   }
 }
 
-int debug_state = -1;   // -1: not yet read from the environment
+std::atomic<int> debug_state{-1};   // -1: not yet read from the environment
 
 }  // namespace
 
 bool debug_enabled() {
-  if (debug_state < 0) {
+  int s = debug_state.load(std::memory_order_relaxed);
+  if (s < 0) {
     const char* e = getenv("SPEC_DEBUG");
-    debug_state = (e && e[0] && e[0] != '0') ? 1 : 0;
+    s = (e && e[0] && e[0] != '0') ? 1 : 0;
+    int expected = -1;
+    debug_state.compare_exchange_strong(expected, s, std::memory_order_relaxed);
+    s = debug_state.load(std::memory_order_relaxed);
   }
-  return debug_state == 1;
+  return s == 1;
 }
 
 int set_debug(int on) {
   const int prev = debug_enabled() ? 1 : 0;
-  debug_state = on ? 1 : 0;
+  debug_state.store(on ? 1 : 0, std::memory_order_relaxed);
   return prev;
 }
 
