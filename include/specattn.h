@@ -82,7 +82,7 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 2
+#define SPEC_ABI_VERSION 3
 
 /* Bytes at the start of every non-empty workspace that must be zero before
  * its first use (see Workspace above). */

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libspecattn.so")
 
 SPEC_F32 = 0
 SPEC_BF16 = 1
-SPEC_ABI_VERSION = 2
+SPEC_ABI_VERSION = 3
 SPEC_WS_SYNC_BYTES = 1 << 20
 
 STATUS = {

@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.spec_abi_version() == 2
+    assert L.spec_abi_version() == 3
     for code in range(7):
         s = L.spec_status_str(code).decode()
         assert s.startswith("SPEC_")
