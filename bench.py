@@ -50,7 +50,7 @@ def _parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--only", choices=["verify", "vata", "hsr", "topk", "accept", "step", "c5",
-                                       "std"],
+                                       "std", "verify_b16"],
                     default=None, help="time one part only (for counter passes)")
     return ap.parse_args()
 
@@ -388,6 +388,31 @@ def main():
                                              "25,512 positions, fp64 numpy), times 4"}
         del kv_s
 
+    # ---- the same verification kernel on a batch large enough to stream:
+    # 16 sequences x 32,768 positions (1.07 GB of KV), two rotated copies.
+    # Device-side normals of the workload's shapes; context for the
+    # fixed-cost analysis of the 52 MB call above.
+    vb16 = None
+    if only in (None, "verify_b16"):
+        Bb, Lb = 16, 32768
+        kvb = [S.KVCache(torch.randn(Bb, Hkv, Lb, d, device=dev).mul_(0.5).to(torch.bfloat16),
+                         torch.randn(Bb, Hkv, Lb, d, device=dev).mul_(0.5).to(torch.bfloat16),
+                         torch.full((Bb,), Lb, dtype=torch.int32, device=dev)) for _ in range(2)]
+        qb = torch.randn(Bb, n, Hq, d, device=dev).to(torch.bfloat16)
+        ob = torch.empty((Bb, n, Hq, d), dtype=torch.bfloat16, device=dev)
+        lb = torch.empty((Bb, n, Hq), dtype=torch.float32, device=dev)
+        for kv in kvb:
+            S.spec_verify_attn(kv, qb, scale=scale, out=ob, lse=lb, workspace=wsp["verify"])
+        torch.cuda.synchronize()
+        g = capture(lambda: [S.spec_verify_attn(kv, qb, scale=scale, out=ob, lse=lb,
+                                                workspace=wsp["verify"]) for kv in kvb])
+        vb_us = time_graph(g, max(4, args.reps // 4)) * 1e3 / len(kvb)
+        vb_bytes = 2 * Bb * Hkv * Lb * d * 2 + 2 * Bb * n * Hq * d * 2 + Bb * n * Hq * 4
+        vb_gbs = vb_bytes / (vb_us * 1e-6) / 1e9
+        vb16 = {"workload": "verify-16x32768", "us": round(vb_us, 1), "gbs": round(vb_gbs, 1),
+                "frac": round(vb_gbs / HBM_PEAK_GBS, 4)}
+        del kvb
+
     # ---- algorithmic bytes (per call)
     kv_bytes = 2 * L * Hkv * d * 2
     verify_bytes = kv_bytes + 2 * (n * Hq * d * 2) + n * Hq * 4
@@ -475,6 +500,7 @@ def main():
         if "hsr_us" in parts else None,
         "batched_draft": c5,
         "std": std,
+        "verify_batch16": vb16,
         "verify_max_abs_err_vs_oracle": err,
         "roofline": roof,
         "cpu_baseline": cpu,
