@@ -368,7 +368,7 @@ spec_status_t launch_hsr(const void* e, const void* h, const void* w, int m, int
     a.M = m;
     a.D = d_model;
     a.out_bf16 = out_bf16;
-    constexpr int RW = 2, U = 14, WV = 8;
+    constexpr int RW = 1, U = 14, WV = 8;   // one W row per wave (measured best)
     const dim3 grid((d_model + WV * RW - 1) / (WV * RW)), block(WV * 64);
     static_assert(kGemvMaxM == 1, "one X row in LDS");
     hipLaunchKernelGGL((hsr_gemv_kernel<1, RW, U, WV>), grid, block, (size_t)4 * d_model, stream, a);
