@@ -26,7 +26,8 @@ exact (widened) values of the stored inputs:
   visual positions by the mean attention of the text tokens, kept with the
   text positions (Sparse-to-Dense pt explainer, "Seleção de Cache KV").
 * ``sparse_attention``  -- the sparse draft attention over such a per-head
-  list plus the positions written since (same page, "Metodologia").
+  list plus a dense tail: the positions written since, or a sliding window
+  (same page, "Metodologia"; the window variants of Sparrow's text anchors).
 * ``commit``            -- the bookkeeping that follows acceptance: keep
   the accepted rows of the cache, roll back the rest, append the emitted
   tokens and the new text positions (same page, decoding procedure).
@@ -38,6 +39,8 @@ Pins (closed forms, invariants, brute force) live in ``tests/test_oracle_*``.
 One function is "parity unpinned" in part: the aggregation rule of the top-K
 score (sum of the group's queries) is a reading, fixed by the workload
 definition rather than the pages; its selection and attention steps are pinned.
+The prefill selection's granularity (one list per KV head, the group's heads
+averaged) is likewise a reading; its arithmetic is pinned.
 """
 from .attention import (verify_attention, vata_attention, topk_scores, topk_select,
                         topk_attention, paged_rows)
