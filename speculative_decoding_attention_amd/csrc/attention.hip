@@ -72,23 +72,35 @@ __device__ __forceinline__ int unit_slots(const AttnArgs& a, int b, int g, int L
   return a.slot_len[b * a.Hkv + g] + max(0, L - tail_begin(a, b, L));
 }
 
+// The list entry of this thread's first slot, t_beg + threadIdx.x, requested
+// before the lengths that bound the split are known: the index is clamped to
+// the list's extent, so the load is always in bounds, and stage_slots ignores
+// it where the slot turns out to lie past the list.  This takes one global
+// round trip off the path to the first K/V request.
+__device__ __forceinline__ int prefetch_slot(const AttnArgs& a, int b, int g, int t_beg) {
+  if (a.mode == 0 || a.slot_stride <= 0) return 0;
+  const size_t base = (size_t)(a.mode == 1 ? b : b * a.Hkv + g) * a.slot_stride;
+  return a.slots[base + min(t_beg + (int)threadIdx.x, a.slot_stride - 1)];
+}
+
 // Resolves slots [t_beg, t_end) of (b, g) into LDS: logical position from the
 // slot list (or the slot itself), then the physical row through the page
 // table when the cache is paged.  Rows fit 32 bits for any pool that fits in
-// device memory.
+// device memory.  `pre` is prefetch_slot's value for the first slot.
 __device__ __forceinline__ void stage_slots(const AttnArgs& a, int b, int g, int L, int t_beg,
-                                            int t_end, int* pos, uint32_t* row) {
+                                            int t_end, int* pos, uint32_t* row, int pre) {
   const size_t u = (size_t)b * a.Hkv + g;
   const int n_list = (a.mode == 3) ? a.slot_len[u] : 0;
   const int t0 = (a.mode == 3) ? tail_begin(a, b, L) : 0;
-  for (int t = t_beg + (int)threadIdx.x; t < t_end; t += blockDim.x) {
+  const int first = t_beg + (int)threadIdx.x;
+  for (int t = first; t < t_end; t += blockDim.x) {
     int p;
     bool skip = false;          // a list entry inside the tail: the tail has it
     if (a.mode == 0) p = t;
-    else if (a.mode == 1) p = a.slots[(size_t)b * a.slot_stride + t];
-    else if (a.mode == 2) p = a.slots[u * a.slot_stride + t];
+    else if (a.mode == 1) p = (t == first) ? pre : a.slots[(size_t)b * a.slot_stride + t];
+    else if (a.mode == 2) p = (t == first) ? pre : a.slots[u * a.slot_stride + t];
     else if (t < n_list) {
-      p = a.slots[u * a.slot_stride + t];
+      p = (t == first) ? pre : a.slots[u * a.slot_stride + t];
       skip = p >= t0;
     } else {
       p = t0 + (t - n_list);
@@ -404,6 +416,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int u = wg / a.S, s = wg - u * a.S;
   const int b = u / a.Hkv, g = u - b * a.Hkv;
+  const int pre = GATHER ? prefetch_slot(a, b, g, s * a.chunk) : 0;
   const int L = a.kv_len[b];
   const int nq = a.q_len ? a.q_len[b] : a.n_max;
   const int T = unit_slots(a, b, g, L);
@@ -416,7 +429,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
   sm.pos = s_pos;
   sm.row = s_row;
   if (GATHER) {
-    stage_slots(a, b, g, L, t_beg, t_end, s_pos, s_row);
+    stage_slots(a, b, g, L, t_beg, t_end, s_pos, s_row, pre);
     __syncthreads();
   }
 
@@ -673,23 +686,31 @@ __global__ __launch_bounds__(PipeCfg<NB>::WAVES * 64, 1) void attn_bf16_pipe_ker
   lds_u8_t* const ring_l = (lds_u8_t*)ring;        // the ring as an LDS-address-space pointer
   const uint32_t ring_lds = (uint32_t)(size_t)ring_l;
   constexpr uint32_t kQSlot = (uint32_t)((C::NS - 1) * C::TILE_BYTES);
-  // Dense splits: the query block goes out first, so its round trip overlaps
-  // the scalar loads of the lengths and the first K/V tiles.
-  if (!GATHER) pipe_issue_q<NB>(a, b, g, ring_lds + kQSlot, wave, lane);
-  const int L = a.kv_len[b];
-  const int nq = a.q_len ? a.q_len[b] : a.n_max;
-  const int T = unit_slots(a, b, g, L);
   const int t_beg = s * a.chunk;
-  const int t_end = min(T, t_beg + a.chunk);
-  const int n_tiles = t_end > t_beg ? (t_end - t_beg + C::TILE_KEYS - 1) / C::TILE_KEYS : 0;
-
   SlotMap<GATHER> sm;
   sm.t_beg = t_beg;
   sm.base_row = ((uint32_t)b * (uint32_t)a.Hkv + (uint32_t)g) * (uint32_t)a.max_len;
   sm.pos = s_pos;
   sm.row = s_row;
+  // Dense splits: tile 0 and the query block go out before the sequence
+  // length is known, so their round trips overlap the length's.  Tile 0's
+  // slots are clamped to the split's end as planned over the cache capacity,
+  // so every row it names lies inside the cache.  Rows past the sequence's
+  // end may hold anything (a masked key still adds 0 * V), so when the
+  // sequence ends inside tile 0 the tile is requested again below.
+  const int spec_end = min(t_beg + a.chunk, a.max_len);
+  if (!GATHER) {
+    pipe_issue_tile<NB, GATHER>(a, sm, t_beg, spec_end, ring_lds, wave, lane);
+    pipe_issue_q<NB>(a, b, g, ring_lds + kQSlot, wave, lane);
+  }
+  const int pre = GATHER ? prefetch_slot(a, b, g, t_beg) : 0;
+  const int L = a.kv_len[b];
+  const int nq = a.q_len ? a.q_len[b] : a.n_max;
+  const int T = unit_slots(a, b, g, L);
+  const int t_end = min(T, t_beg + a.chunk);
+  const int n_tiles = t_end > t_beg ? (t_end - t_beg + C::TILE_KEYS - 1) / C::TILE_KEYS : 0;
   if (GATHER) {
-    stage_slots(a, b, g, L, t_beg, t_end, s_pos, s_row);
+    stage_slots(a, b, g, L, t_beg, t_end, s_pos, s_row, pre);
     __syncthreads();
   }
 
@@ -708,7 +729,13 @@ __global__ __launch_bounds__(PipeCfg<NB>::WAVES * 64, 1) void attn_bf16_pipe_ker
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) qop[ks] = as_bf16x8(u32x4_t{0, 0, 0, 0});
 
-  for (int j = 0; j < C::NS - 1 && j < n_tiles; ++j)
+  if (!GATHER && n_tiles > 0 && t_end < min(t_beg + C::TILE_KEYS, spec_end)) {
+    // tile 0 named rows past the sequence: every wave's requests land before
+    // any wave re-requests the slot
+    wait_dma_barrier<0>();
+    pipe_issue_tile<NB, GATHER>(a, sm, t_beg, t_end, ring_lds, wave, lane);
+  }
+  for (int j = GATHER ? 0 : 1; j < C::NS - 1 && j < n_tiles; ++j)
     pipe_issue_tile<NB, GATHER>(a, sm, t_beg + j * C::TILE_KEYS, t_end,
                                 ring_lds + (uint32_t)(j * C::TILE_BYTES), wave, lane);
 
@@ -856,6 +883,7 @@ __global__ __launch_bounds__(256, 1) void attn_f32_kernel(AttnArgs a) {
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int u = wg / a.S, s = wg - u * a.S;
   const int b = u / a.Hkv, g = u - b * a.Hkv;
+  const int pre = GATHER ? prefetch_slot(a, b, g, s * a.chunk) : 0;
   const int L = a.kv_len[b];
   const int nq = a.q_len ? a.q_len[b] : a.n_max;
   const int T = unit_slots(a, b, g, L);
@@ -870,7 +898,7 @@ __global__ __launch_bounds__(256, 1) void attn_f32_kernel(AttnArgs a) {
   sm.pos = s_pos;
   sm.row = s_row;
   if (GATHER) {
-    stage_slots(a, b, g, L, t_beg, t_end, s_pos, s_row);
+    stage_slots(a, b, g, L, t_beg, t_end, s_pos, s_row, pre);
     __syncthreads();
   }
 
@@ -967,74 +995,94 @@ __global__ __launch_bounds__(256, 1) void attn_f32_kernel(AttnArgs a) {
 }
 
 // --------------------------------------------------------------- merge ----
-// One workgroup per (unit, row): combine the S partials with the log-sum-exp
-// rule.  Every partial this thread needs is requested before the split
-// weights are known (they only scale the sum), so the kernel waits for one
-// round of loads; wave 0 meanwhile turns the splits' (m, l, l_rnd) into
-// weights in LDS.  Threads form kMergeThreads/D groups over the splits; each group
-// sums its splits in order and the groups are added in a fixed order.
+// One workgroup per (unit, row, slice of kMergeSlice output columns): combine
+// the S partials with the log-sum-exp rule.  Threads form
+// kMergeThreads/kMergeSlice groups over the splits (group k takes splits
+// k, k + NG, ...).  Each thread requests its partials and their splits'
+// (m, l, l_rnd) in one round of loads, merges them against its group's own
+// running maximum, and the groups are then combined in a fixed order against
+// the overall maximum.  One load round trip and one barrier on the critical
+// path; no thread waits for another's weights.
 constexpr int kMaxSplits = 4096;
-constexpr int kMergeThreads = 1024;   // more groups over the splits: more loads in flight
+constexpr int kMergeThreads = 512;   // more groups over the splits: more loads in flight
+constexpr int kMergeSlice = 64;       // output columns per workgroup: one wave per split
+constexpr int kMergeLoads = 4096;     // partial values one workgroup requests per round
 
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
-  constexpr int NG = kMergeThreads / D;
-  constexpr int PB = 8 * 1024 / kMergeThreads;   // partials in flight per thread
-  __shared__ float w_s[kMaxSplits];
-  __shared__ float stat[3];
-  __shared__ float part[NG][D];
+  constexpr int DS = kMergeSlice < D ? kMergeSlice : D;
+  constexpr int NG = kMergeThreads / DS;
+  constexpr int PB = kMergeLoads / kMergeThreads;   // splits per thread per load round
+  static_assert(DS % 64 == 0 && PB >= 1, "merge shape");
+  __shared__ float part[NG][DS];
+  __shared__ float gstat[3][NG];
   const int R = a.R, S = a.S;
-  const int u = blockIdx.x / R, r = blockIdx.x - (blockIdx.x / R) * R;
+  const int row = blockIdx.x / (D / DS), slice = blockIdx.x - row * (D / DS);
+  const int u = row / R, r = row - u * R;
   const int b = u / a.Hkv, g = u - b * a.Hkv;
-  const int nq = a.q_len ? a.q_len[b] : a.n_max;
   const int i = r / a.G, hh = r - i * a.G;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int d = tid % D, grp = tid / D;
-  const float* pm = a.part_ml + (size_t)u * S * 3 * R;
+  const int tid = threadIdx.x, dl = tid % DS, d = slice * DS + dl;
+  // the group index is uniform over a wave (DS is a multiple of 64), so the
+  // per-split statistics below are scalar loads
+  const int grp = __builtin_amdgcn_readfirstlane(tid / DS);
+  const float* pm = a.part_ml + (size_t)u * S * 3 * R + r;
   const float* pa = a.part_acc + (size_t)u * S * R * D + (size_t)r * D + d;
 
-  float v[PB];
+  float M = -INFINITY, o = 0.f, ls = 0.f, lr = 0.f;
+  for (int base = grp; base < S; base += NG * PB) {
+    // clamped indices, loaded unconditionally and masked afterwards: a guarded
+    // load would wait for itself before the next one is issued
+    float v[PB], mv[PB], lv[PB], rv[PB];
 #pragma unroll
-  for (int j = 0; j < PB; ++j) {
-    const int sp = grp + NG * j;
-    v[j] = (sp < S) ? pa[(size_t)sp * R * D] : 0.f;
-  }
-  if (wave == 0) {
-    float mx = -INFINITY;
-    for (int sp = lane; sp < S; sp += 64) mx = fmaxf(mx, pm[sp * 3 * R + r]);
-    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    const float Mu = (mx == -INFINITY) ? 0.f : mx;
-    float ls = 0.f, lr = 0.f;
-    for (int sp = lane; sp < S; sp += 64) {
-      const float w = exp2f(pm[sp * 3 * R + r] - Mu);
-      w_s[sp] = w;
-      ls += pm[sp * 3 * R + R + r] * w;
-      lr += pm[sp * 3 * R + 2 * R + r] * w;
+    for (int j = 0; j < PB; ++j) {
+      const int sp = min(base + NG * j, S - 1);
+      v[j] = pa[(size_t)sp * R * D];
+      mv[j] = pm[(size_t)sp * 3 * R];
+      lv[j] = pm[(size_t)sp * 3 * R + R];
+      rv[j] = pm[(size_t)sp * 3 * R + 2 * R];
     }
-    for (int o = 32; o > 0; o >>= 1) {
-      ls += __shfl_xor(ls, o);
-      lr += __shfl_xor(lr, o);
-    }
-    if (lane == 0) {
-      stat[0] = mx;
-      stat[1] = ls;
-      stat[2] = lr;
-    }
-  }
-  __syncthreads();
-  float o = 0.f;
+    float mr = M;
 #pragma unroll
-  for (int j = 0; j < PB; ++j) {
-    const int sp = grp + NG * j;
-    if (sp < S) o += v[j] * w_s[sp];
+    for (int j = 0; j < PB; ++j) {
+      if (base + NG * j >= S) mv[j] = -INFINITY;   // contributes a zero weight
+      mr = fmaxf(mr, mv[j]);
+    }
+    const float Mu = (mr == -INFINITY) ? 0.f : mr;
+    const float sc = __builtin_amdgcn_exp2f(M - Mu);   // M = -inf: nothing merged yet -> 0
+    o *= sc;
+    ls *= sc;
+    lr *= sc;
+#pragma unroll
+    for (int j = 0; j < PB; ++j) {
+      const float w = __builtin_amdgcn_exp2f(mv[j] - Mu);
+      o = __builtin_fmaf(v[j], w, o);
+      ls = __builtin_fmaf(lv[j], w, ls);
+      lr = __builtin_fmaf(rv[j], w, lr);
+    }
+    M = mr;
   }
-  for (int sp = grp + NG * PB; sp < S; sp += NG) o += pa[(size_t)sp * R * D] * w_s[sp];
-  part[grp][d] = o;
+  part[grp][dl] = o;
+  if (dl == 0) {
+    gstat[0][grp] = M;
+    gstat[1][grp] = ls;
+    gstat[2][grp] = lr;
+  }
   __syncthreads();
   if (grp != 0) return;
-  o = part[0][d];
-  for (int k = 1; k < NG; ++k) o += part[k][d];
-  const float M = stat[0], Ls = stat[1], Lr = stat[2];
+  float Mx = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < NG; ++k) Mx = fmaxf(Mx, gstat[0][k]);
+  const float Mu = (Mx == -INFINITY) ? 0.f : Mx;
+  float Ls = 0.f, Lr = 0.f;
+  o = 0.f;
+#pragma unroll
+  for (int k = 0; k < NG; ++k) {
+    const float f = __builtin_amdgcn_exp2f(gstat[0][k] - Mu);
+    o = __builtin_fmaf(part[k][dl], f, o);
+    Ls = __builtin_fmaf(gstat[1][k], f, Ls);
+    Lr = __builtin_fmaf(gstat[2][k], f, Lr);
+  }
+  const int nq = a.q_len ? a.q_len[b] : a.n_max;
   const bool live = (i < nq) && (Ls > 0.f);
   o = live ? o / Lr : 0.f;
   const size_t oi = (((size_t)b * a.n_max + i) * a.Hq + g * a.G + hh) * D + d;
@@ -1044,7 +1092,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
     reinterpret_cast<float*>(a.out)[oi] = o;
   if (a.lse && d == 0)
     a.lse[((size_t)b * a.n_max + i) * a.Hq + g * a.G + hh] =
-        live ? (M + log2f(Ls)) * 0.69314718055994531f : -INFINITY;
+        live ? (Mx + log2f(Ls)) * 0.69314718055994531f : -INFINITY;
 }
 
 template <int D, int NB, bool GATHER>
@@ -1149,7 +1197,7 @@ spec_status_t launch_attention(AttnArgs a, int d, int dtype, const AttnPlan& pla
                   : launch_d<128, false>(a, dtype, plan.grid, stream);
   if (e != hipSuccess) return SPEC_ERR_HIP;
   if (plan.S > 1) {
-    const int blocks = a.B * a.Hkv * a.R;
+    const int blocks = a.B * a.Hkv * a.R * (d > kMergeSlice ? d / kMergeSlice : 1);
     if (d == 64)
       hipLaunchKernelGGL(attn_merge_kernel<64>, dim3(blocks), dim3(kMergeThreads), 0, stream, a);
     else

@@ -180,10 +180,13 @@ def test_paged_equals_contiguous_on_device():
 
 
 @pytest.mark.parametrize("dt", [W.BF16, W.F32])
-def test_rows_past_the_length_are_never_used(dt):
+@pytest.mark.parametrize("L", [(5000, 3100, 130), (904, 2017, 130)])
+def test_rows_past_the_length_are_never_used(dt, L):
     """Cache capacity beyond kv_len holds NaN keys and infinite values: the
-    output must still match the oracle (which never reads those rows)."""
-    L = (5000, 3100, 130)
+    output must still match the oracle (which never reads those rows).  With
+    256 CUs these shapes plan 288-key splits; 904 and 2017 end 40 keys and
+    1 key into a split's first 64-key tile, which the dense kernel requests
+    before the length is known and must request again."""
     c = W.small_attn(41, 3, 28, 4, 128, 6, L, dt, max_len=5600)
     kb, vb = c.k.bits.copy(), c.v.bits.copy()
     nan, inf = (0x7FC0, 0x7F80) if dt == W.BF16 else (np.nan, np.inf)   # bf16 bits / fp32 values
