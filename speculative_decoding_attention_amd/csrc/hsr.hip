@@ -55,12 +55,11 @@ struct GemmCfg {
 // n0.. into one ring stage.  Instruction j moves 8 rows of 128 bytes; X rows
 // past M repeat row M-1 (their outputs are never stored).
 template <int MT, int NT, int WN>
-__device__ __forceinline__ void gemm_issue(const HsrArgs& a, int m0, int n0, int ks,
-                                           uint32_t stage_lds, int wave, int lane) {
+__device__ __forceinline__ void gemm_src(const HsrArgs& a, int m0, int n0, int ks, int wave,
+                                         int lane, const unsigned char* (&src)[GemmCfg<MT, NT, WN>::PER_WAVE]) {
   using C = GemmCfg<MT, NT, WN>;
   const int k0 = ks * kGemmBK;
   const int sub = lane >> 3, slot = lane & 7;
-  const unsigned char* src[C::PER_WAVE];
 #pragma unroll
   for (int jj = 0; jj < C::PER_WAVE; ++jj) {
     const int j = wave + C::WAVES * jj;
@@ -75,9 +74,25 @@ __device__ __forceinline__ void gemm_issue(const HsrArgs& a, int m0, int n0, int
       src[jj] = reinterpret_cast<const unsigned char*>(a.w + (size_t)(n0 + row) * (2 * a.D) + k);
     }
   }
+}
+
+// Requests instructions [J0, J1) of a step whose addresses gemm_src computed.
+template <int MT, int NT, int WN, int J0, int J1>
+__device__ __forceinline__ void gemm_dma(const unsigned char* const (&src)[GemmCfg<MT, NT, WN>::PER_WAVE],
+                                         uint32_t stage_lds, int wave) {
+  using C = GemmCfg<MT, NT, WN>;
 #pragma unroll
-  for (int jj = 0; jj < C::PER_WAVE; ++jj)
+  for (int jj = J0; jj < J1; ++jj)
     dma16(src[jj], stage_lds + (uint32_t)((wave + C::WAVES * jj) * 1024));
+}
+
+template <int MT, int NT, int WN>
+__device__ __forceinline__ void gemm_issue(const HsrArgs& a, int m0, int n0, int ks,
+                                           uint32_t stage_lds, int wave, int lane) {
+  using C = GemmCfg<MT, NT, WN>;
+  const unsigned char* src[C::PER_WAVE];
+  gemm_src<MT, NT, WN>(a, m0, n0, ks, wave, lane, src);
+  gemm_dma<MT, NT, WN, 0, C::PER_WAVE>(src, stage_lds, wave);
 }
 
 template <int MT, int NT, int WN>
@@ -111,9 +126,14 @@ __global__ __launch_bounds__(128 * WN, 1) void hsr_mfma_kernel(HsrArgs a) {
 
   for (int t = 0; t < nsteps; ++t) {
     wait_tiles_barrier<C::PER_WAVE>(min(C::NS - 2, nsteps - 1 - t));
-    if (t + C::NS - 1 < nsteps)
-      gemm_issue<MT, NT, WN>(a, m0, n0, ks0 + t + C::NS - 1,
-                         ring_lds + (uint32_t)(((t + C::NS - 1) % C::NS) * C::STAGE), wave, lane);
+    // The refill of step t - 1's slot is spread over this step's MFMAs: the
+    // matrix cores keep working while the address unit takes the requests
+    // (one 1 KB request per 16 clocks per CU), instead of every wave
+    // stalling on a burst of requests between the barrier and its MFMAs.
+    const bool refill = t + C::NS - 1 < nsteps;
+    const uint32_t nxt = ring_lds + (uint32_t)(((t + C::NS - 1) % C::NS) * C::STAGE);
+    const unsigned char* src[C::PER_WAVE];
+    gemm_src<MT, NT, WN>(a, m0, n0, refill ? ks0 + t + C::NS - 1 : ks0, wave, lane, src);
     const unsigned char* st = ring + (t % C::NS) * C::STAGE;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {            // two 32-wide k steps of the MFMA
@@ -135,6 +155,10 @@ __global__ __launch_bounds__(128 * WN, 1) void hsr_mfma_kernel(HsrArgs a) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bfr[nt], acc[mt][nt], 0, 0, 0);
+      if (refill) {
+        if (kk == 0) gemm_dma<MT, NT, WN, 0, C::PER_WAVE / 2>(src, nxt, wave);
+        else gemm_dma<MT, NT, WN, C::PER_WAVE / 2, C::PER_WAVE>(src, nxt, wave);
+      }
     }
   }
 

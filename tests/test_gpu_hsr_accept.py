@@ -30,7 +30,9 @@ def _hsr_check(case, y):
 
 
 @pytest.mark.parametrize("m,d", [(1, 256), (2, 128), (5, 128), (16, 64), (17, 192), (40, 256),
-                                 (64, 128), (65, 128), (77, 384), (130, 64), (200, 512)])
+                                 (64, 128), (65, 128), (77, 384), (130, 64), (200, 512),
+                                 # 257..320 rows: one tile spans every row
+                                 (257, 192), (300, 128), (320, 64), (320, 512), (290, 1024)])
 def test_hsr_small(m, d):
     rng = np.random.default_rng(m * 1000 + d)
     case = W.HsrCase("small",
