@@ -50,7 +50,7 @@ def _parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--only", choices=["verify", "vata", "hsr", "topk", "accept", "step", "c5",
-                                       "std", "verify_b16"],
+                                       "std", "verify_b16", "c3", "c4"],
                     default=None, help="time one part only (for counter passes)")
     return ap.parse_args()
 
@@ -413,6 +413,103 @@ def main():
                 "frac": round(vb_gbs / HBM_PEAK_GBS, 4)}
         del kvb
 
+    # ---- ragged paged batch (16 sequences, 16-token pages in a random pool
+    # order, L_b = Lvis_b + Ltxt_b, n_b = gamma_b + 1 rows padded to 8): verify
+    # and text-anchored attention per sequence, and the same batch in a
+    # contiguous cache.  One copy of the pool (565 MB) already exceeds the
+    # 256 MiB cache twice over.  K/V/Q are drawn on the device (same shapes
+    # and scales as the parity cases, which use the host generator).
+    c3 = None
+    if only in (None, "c3"):
+        lay = W.c3_layout(0)
+        B3, n3, ps = len(lay.L), 8, 16
+        L3 = torch.tensor(lay.L, dtype=torch.int32, device=dev)
+        ql3 = torch.tensor(lay.gamma + 1, dtype=torch.int32, device=dev)
+        pt3 = torch.tensor(lay.page_table, dtype=torch.int32, device=dev)
+        kp = torch.randn(lay.pages, Hkv, ps, d, device=dev).mul_(0.5).to(torch.bfloat16)
+        vp = torch.randn(lay.pages, Hkv, ps, d, device=dev).mul_(0.5).to(torch.bfloat16)
+        kv3 = S.KVCache(kp, vp, L3, page_table=pt3, page_size=ps, max_len=int(lay.L.max()))
+        q3 = torch.randn(B3, n3, Hq, d, device=dev).to(torch.bfloat16)
+        o3 = torch.empty((B3, n3, Hq, d), dtype=torch.bfloat16, device=dev)
+        l3 = torch.empty((B3, n3, Hq), dtype=torch.float32, device=dev)
+        tmax3 = int(lay.ltxt.max())
+        ti3 = np.zeros((B3, tmax3), np.int32)
+        for b_ in range(B3):
+            ti3[b_, :lay.ltxt[b_]] = np.arange(lay.lvis[b_], lay.L[b_], dtype=np.int32)
+        ti3 = torch.tensor(ti3, device=dev)
+        tl3 = torch.tensor(lay.ltxt, dtype=torch.int32, device=dev)
+        ws3 = {k_: S.Workspace(dev) for k_ in ("verify", "vata")}
+
+        def c3_verify(kv):
+            S.spec_verify_attn(kv, q3, q_len=ql3, scale=scale, out=o3, lse=l3,
+                               workspace=ws3["verify"])
+
+        def c3_vata(kv):
+            S.spec_vata_attn(kv, q3, ti3, tl3, q_len=ql3, scale=scale, out=o3, lse=l3,
+                             workspace=ws3["vata"])
+
+        reps3 = max(4, args.reps // 4)
+        c3_verify(kv3), c3_vata(kv3)
+        torch.cuda.synchronize()
+        t_ver = time_graph(capture(lambda: c3_verify(kv3)), reps3) * 1e3
+        t_vat = time_graph(capture(lambda: c3_vata(kv3)), reps3) * 1e3
+        del kp, vp, kv3
+        mx = int(lay.L.max())
+        kc = torch.randn(B3, Hkv, mx, d, device=dev).mul_(0.5).to(torch.bfloat16)
+        vc = torch.randn(B3, Hkv, mx, d, device=dev).mul_(0.5).to(torch.bfloat16)
+        kvc3 = S.KVCache(kc, vc, L3)
+        c3_verify(kvc3)
+        torch.cuda.synchronize()
+        t_verc = time_graph(capture(lambda: c3_verify(kvc3)), reps3) * 1e3
+        del kc, vc, kvc3
+        nq3 = int((lay.gamma + 1).sum())
+        ver3_bytes = 2 * int(lay.L.sum()) * Hkv * d * 2 + 2 * nq3 * Hq * d * 2 + nq3 * Hq * 4
+        vat3_bytes = 2 * int(lay.ltxt.sum()) * Hkv * d * 2 + int(lay.ltxt.sum()) * 4 + \
+            2 * nq3 * Hq * d * 2 + nq3 * Hq * 4
+        gbs = lambda by, us: round(by / (us * 1e-6) / 1e9, 1)
+        c3 = {"workload": "ragged-paged-16", "kv_tokens": int(lay.L.sum()),
+              "verify_paged_us": round(t_ver, 1), "verify_paged_gbs": gbs(ver3_bytes, t_ver),
+              "verify_paged_frac": round(ver3_bytes / (t_ver * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+              "verify_contiguous_us": round(t_verc, 1),
+              "verify_contiguous_gbs": gbs(ver3_bytes, t_verc),
+              "vata_paged_us": round(t_vat, 1), "vata_paged_gbs": gbs(vat3_bytes, t_vat)}
+
+    # ---- top-K draft and dense verification, 4 sequences of 32,768 keys
+    # (28,672 visual + 4,096 text), K = 2048: the per-step top-K (score all
+    # keys, select, attend) against the dense verification of gamma + 1 rows.
+    c4 = None
+    if only in (None, "c4"):
+        B4, L4, K4 = 4, 32768, 2048
+        kv4 = [S.KVCache(torch.randn(B4, Hkv, L4, d, device=dev).mul_(0.5).to(torch.bfloat16),
+                         torch.randn(B4, Hkv, L4, d, device=dev).mul_(0.5).to(torch.bfloat16),
+                         torch.full((B4,), L4, dtype=torch.int32, device=dev)) for _ in range(2)]
+        q4 = torch.randn(B4, n, Hq, d, device=dev).to(torch.bfloat16)
+        q4l = q4[:, -1:].contiguous()
+        o4 = torch.empty((B4, n, Hq, d), dtype=torch.bfloat16, device=dev)
+        l4 = torch.empty((B4, n, Hq), dtype=torch.float32, device=dev)
+        s4 = torch.empty((B4, Hkv, K4), dtype=torch.int32, device=dev)
+        o4k = torch.empty((B4, 1, Hq, d), dtype=torch.bfloat16, device=dev)
+        l4k = torch.empty((B4, 1, Hq), dtype=torch.float32, device=dev)
+        ws4 = {k_: S.Workspace(dev) for k_ in ("verify", "topk")}
+        f_ver = lambda: [S.spec_verify_attn(kv, q4, scale=scale, out=o4, lse=l4,
+                                            workspace=ws4["verify"]) for kv in kv4]
+        f_top = lambda: [S.spec_topk_attn(kv, q4l, K4, scale=scale, sel_idx=s4, out=o4k, lse=l4k,
+                                          workspace=ws4["topk"]) for kv in kv4]
+        f_ver(), f_top()
+        torch.cuda.synchronize()
+        reps4 = max(4, args.reps // 4)
+        t4v = time_graph(capture(f_ver), reps4) * 1e3 / len(kv4)
+        t4k = time_graph(capture(f_top), reps4) * 1e3 / len(kv4)
+        del kv4
+        v4_bytes = 2 * B4 * Hkv * L4 * d * 2 + 2 * B4 * n * Hq * d * 2 + B4 * n * Hq * 4
+        k4_bytes = B4 * Hkv * L4 * d * 2 + 2 * B4 * Hkv * K4 * d * 2 + B4 * Hkv * K4 * 4 + \
+            2 * B4 * Hq * d * 2
+        c4 = {"workload": "topk-4x32768", "verify_us": round(t4v, 1),
+              "verify_gbs": round(v4_bytes / (t4v * 1e-6) / 1e9, 1),
+              "verify_frac": round(v4_bytes / (t4v * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+              "topk_us": round(t4k, 1), "topk_gbs": round(k4_bytes / (t4k * 1e-6) / 1e9, 1),
+              "topk_to_dense_bytes": round(k4_bytes / v4_bytes, 3)}
+
     # ---- algorithmic bytes (per call)
     kv_bytes = 2 * L * Hkv * d * 2
     verify_bytes = kv_bytes + 2 * (n * Hq * d * 2) + n * Hq * 4
@@ -501,6 +598,8 @@ def main():
         "batched_draft": c5,
         "std": std,
         "verify_batch16": vb16,
+        "ragged_paged": c3,
+        "topk_batch4": c4,
         "verify_max_abs_err_vs_oracle": err,
         "roofline": roof,
         "cpu_baseline": cpu,

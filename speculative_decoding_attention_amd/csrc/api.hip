@@ -131,7 +131,8 @@ size_t spec_verify_attn_workspace(const spec_kv_t* kv, int32_t batch, int32_t n_
     return 0;
   const int R = n_max * (num_q_heads / kv->num_kv_heads);
   return plan_attention(batch * kv->num_kv_heads, kv->max_len, R, kv->head_dim,
-                        kv->page_size != 0).ws_bytes;
+                        kv->page_size != 0, kSyncBytes,
+                        kv->page_size ? log2_int(kv->page_size) : -1).ws_bytes;
 }
 
 spec_status_t spec_verify_attn(const spec_kv_t* kv, int32_t batch, const void* q,
@@ -144,7 +145,7 @@ spec_status_t spec_verify_attn(const spec_kv_t* kv, int32_t batch, const void* q
   AttnArgs a = make_args(kv, batch, q, n_max, q_len, num_q_heads, scale, out, out_dtype, lse);
   a.mode = 0;
   const AttnPlan plan = plan_attention(batch * kv->num_kv_heads, kv->max_len, a.R, kv->head_dim,
-                                       kv->page_size != 0);
+                                       kv->page_size != 0, kSyncBytes, a.page_shift);
   st = check_ws(plan.ws_bytes, ws, ws_bytes);
   if (st != SPEC_OK) return st;
   if (debug_enabled() && (st = validate(kv_checks(kv, batch, q_len, n_max), stream)) != SPEC_OK)

@@ -50,12 +50,25 @@ struct SlotMap {
   int t_beg;
   uint32_t base_row;      // dense: first row of (b, g)
   const int* pos;         // gather: LDS positions of slots t_beg..
-  const uint32_t* row;    // gather: LDS row indices of slots t_beg..
+  const uint32_t* row;    // gather: LDS row indices of slots t_beg.. (or pages, below)
+  // Dense slots in a paged cache (every position in order): row[] holds the
+  // split's pages instead, from page pg0 on, so a split can span 4096 pages
+  // rather than 4096 slots.  shift = log2(page size), or -1 for a list.
+  int shift, pg0;
+  uint32_t hkv, g;
   __device__ __forceinline__ int position(int slot) const {
-    return GATHER ? pos[slot - t_beg] : slot;
+    return !GATHER ? slot : (shift >= 0 ? slot : pos[slot - t_beg]);
   }
   __device__ __forceinline__ uint32_t rowof(int slot) const {
-    return GATHER ? row[slot - t_beg] : base_row + (uint32_t)slot;
+    if (!GATHER) return base_row + (uint32_t)slot;
+    if (shift < 0) return row[slot - t_beg];
+    return ((row[(slot >> shift) - pg0] * hkv + g) << shift) + (uint32_t)(slot & ((1 << shift) - 1));
+  }
+  __device__ __forceinline__ void set_pages(const AttnArgs& a, int g_) {
+    shift = (a.mode == 0) ? a.page_shift : -1;
+    pg0 = (shift >= 0) ? (t_beg >> shift) : 0;
+    hkv = (uint32_t)a.Hkv;
+    g = (uint32_t)g_;
   }
 };
 
@@ -90,14 +103,20 @@ __device__ __forceinline__ int prefetch_slot(const AttnArgs& a, int b, int g, in
 __device__ __forceinline__ void stage_slots(const AttnArgs& a, int b, int g, int L, int t_beg,
                                             int t_end, int* pos, uint32_t* row, int pre) {
   const size_t u = (size_t)b * a.Hkv + g;
+  if (a.mode == 0) {              // every position of a paged cache: stage the pages
+    if (t_end <= t_beg) return;
+    const int pg0 = t_beg >> a.page_shift, pg1 = (t_end - 1) >> a.page_shift;
+    for (int pg = pg0 + (int)threadIdx.x; pg <= pg1; pg += blockDim.x)
+      row[pg - pg0] = (uint32_t)a.page_table[(size_t)b * a.max_pages + pg];
+    return;
+  }
   const int n_list = (a.mode == 3) ? a.slot_len[u] : 0;
   const int t0 = (a.mode == 3) ? tail_begin(a, b, L) : 0;
   const int first = t_beg + (int)threadIdx.x;
   for (int t = first; t < t_end; t += blockDim.x) {
     int p;
     bool skip = false;          // a list entry inside the tail: the tail has it
-    if (a.mode == 0) p = t;
-    else if (a.mode == 1) p = (t == first) ? pre : a.slots[(size_t)b * a.slot_stride + t];
+    if (a.mode == 1) p = (t == first) ? pre : a.slots[(size_t)b * a.slot_stride + t];
     else if (a.mode == 2) p = (t == first) ? pre : a.slots[u * a.slot_stride + t];
     else if (t < n_list) {
       p = (t == first) ? pre : a.slots[u * a.slot_stride + t];
@@ -428,6 +447,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
   sm.base_row = ((uint32_t)b * (uint32_t)a.Hkv + (uint32_t)g) * (uint32_t)a.max_len;
   sm.pos = s_pos;
   sm.row = s_row;
+  sm.set_pages(a, g);
   if (GATHER) {
     stage_slots(a, b, g, L, t_beg, t_end, s_pos, s_row, pre);
     __syncthreads();
@@ -692,6 +712,7 @@ __global__ __launch_bounds__(PipeCfg<NB>::WAVES * 64, 1) void attn_bf16_pipe_ker
   sm.base_row = ((uint32_t)b * (uint32_t)a.Hkv + (uint32_t)g) * (uint32_t)a.max_len;
   sm.pos = s_pos;
   sm.row = s_row;
+  sm.set_pages(a, g);
   // Dense splits: tile 0 and the query block go out before the sequence
   // length is known, so their round trips overlap the length's.  Tile 0's
   // slots are clamped to the split's end as planned over the cache capacity,
@@ -897,6 +918,7 @@ __global__ __launch_bounds__(256, 1) void attn_f32_kernel(AttnArgs a) {
   sm.base_row = ((uint32_t)b * (uint32_t)a.Hkv + (uint32_t)g) * (uint32_t)a.max_len;
   sm.pos = s_pos;
   sm.row = s_row;
+  sm.set_pages(a, g);
   if (GATHER) {
     stage_slots(a, b, g, L, t_beg, t_end, s_pos, s_row, pre);
     __syncthreads();
@@ -1152,7 +1174,8 @@ int device_cu_count() {
   return n;
 }
 
-AttnPlan plan_attention(int units, int t_max, int rows, int d, bool gather, size_t scratch_off) {
+AttnPlan plan_attention(int units, int t_max, int rows, int d, bool gather, size_t scratch_off,
+                        int dense_page_shift) {
   AttnPlan p;
   const int target = device_cu_count();            // about one workgroup per CU
   const long T = t_max > 0 ? t_max : 1;
@@ -1161,7 +1184,14 @@ AttnPlan plan_attention(int units, int t_max, int rows, int d, bool gather, size
   if (chunk < (T + kMaxSplits - 1) / kMaxSplits) chunk = (T + kMaxSplits - 1) / kMaxSplits;
   chunk = ((chunk + kTK - 1) / kTK) * kTK;
   if (chunk < kTK * kNW) chunk = kTK * kNW;        // every wave gets a tile
-  if (gather && chunk > kMaxChunk) chunk = kMaxChunk;
+  if (gather) {
+    // LDS holds kMaxChunk staged entries: slots, or pages when the split
+    // covers every position of a paged cache
+    const long cap = dense_page_shift >= 0
+                         ? (((long)(kMaxChunk - 1) << dense_page_shift) / kTK) * kTK
+                         : kMaxChunk;
+    if (chunk > cap) chunk = cap;
+  }
   int S = (int)((T + chunk - 1) / chunk);
   if (S < 1) S = 1;
   p.S = S;

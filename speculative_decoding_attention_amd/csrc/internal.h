@@ -69,10 +69,12 @@ int device_cu_count();
 
 // Split plan for U units of at most t_max slots and R rows of width d.
 // `gather`: slot positions come from a list, or rows from a page table.
+// `dense_page_shift` >= 0: every position of a paged cache with pages of
+// 2^shift rows (splits then stage pages, not slots).
 // The partials start at byte `scratch_off` (at least kSyncBytes); ws_bytes is
 // the end of the whole layout, or 0 when a single split needs no workspace.
 AttnPlan plan_attention(int units, int t_max, int rows, int d, bool gather,
-                        size_t scratch_off = kSyncBytes);
+                        size_t scratch_off = kSyncBytes, int dense_page_shift = -1);
 
 spec_status_t launch_attention(AttnArgs a, int d, int dtype, const AttnPlan& plan, void* ws,
                                hipStream_t stream);

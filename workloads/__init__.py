@@ -20,7 +20,7 @@ values are synthetic normals.
 from __future__ import annotations
 
 import dataclasses
-from typing import Optional
+from typing import NamedTuple, Optional
 
 import numpy as np
 
@@ -274,12 +274,17 @@ def c2_sparrow(seed: int = 0, Lvis: int = 25000, with_hsr: bool = True):
     return attn, hsr, acc
 
 
-def c3_ragged_paged(seed: int = 0, batch: int = 16):
-    """Ragged paged batch, bf16: per sequence Lvis ~ U[8000, 25000], Ltxt ~
-    U[256, 1024], gamma ~ U{3..7}; 16-token pages in a random pool order.
-    Text positions are each sequence's trailing Ltxt."""
-    rng = np.random.default_rng(seed)
-    B, Hq, Hkv, d, ps = batch, 28, 4, 128, 16
+class C3Layout(NamedTuple):
+    lvis: np.ndarray
+    ltxt: np.ndarray
+    gamma: np.ndarray
+    L: np.ndarray          # int32 kv lengths
+    pages: int             # pool size
+    page_table: np.ndarray
+
+
+def _c3_layout(rng: np.random.Generator, B: int, ps: int = 16) -> C3Layout:
+    """Lengths, gammas and page table of the ragged batch (the first draws)."""
     lvis = rng.integers(8000, 25001, size=B)
     ltxt = rng.integers(256, 1025, size=B)
     gam = rng.integers(3, 8, size=B)
@@ -287,13 +292,28 @@ def c3_ragged_paged(seed: int = 0, batch: int = 16):
     npg = (L + ps - 1) // ps
     P = int(npg.sum())
     perm = rng.permutation(P).astype(np.int32)
-    n_max = 8                      # gamma <= 7, so blocks are padded to 8 rows
-    max_pages = int(npg.max())
-    page_table = np.zeros((B, max_pages), np.int32)
+    page_table = np.zeros((B, int(npg.max())), np.int32)
     off = 0
     for b in range(B):
         page_table[b, :npg[b]] = perm[off:off + npg[b]]
         off += npg[b]
+    return C3Layout(lvis, ltxt, gam, L, P, page_table)
+
+
+def c3_layout(seed: int = 0, batch: int = 16) -> C3Layout:
+    """The ragged batch's layout alone (no Q/K/V draws)."""
+    return _c3_layout(np.random.default_rng(seed), batch)
+
+
+def c3_ragged_paged(seed: int = 0, batch: int = 16):
+    """Ragged paged batch, bf16: per sequence Lvis ~ U[8000, 25000], Ltxt ~
+    U[256, 1024], gamma ~ U{3..7}; 16-token pages in a random pool order.
+    Text positions are each sequence's trailing Ltxt."""
+    rng = np.random.default_rng(seed)
+    B, Hq, Hkv, d, ps = batch, 28, 4, 128, 16
+    lay = _c3_layout(rng, B, ps)
+    lvis, ltxt, gam, L, P, page_table = lay
+    n_max = 8                      # gamma <= 7, so blocks are padded to 8 rows
     q = _normal(rng, (B, n_max, Hq, d))
     k = _normal(rng, (P, Hkv, ps, d), 0.5)
     v = _normal(rng, (P, Hkv, ps, d), 0.5)
