@@ -574,6 +574,28 @@ __device__ __forceinline__ void pipe_finish(const AttnArgs& a, float* smem, int 
   constexpr int D = 128, RP = NB * 16, DP = D + 4;
   constexpr int KP = PipeCfg<NB>::KP;
   constexpr int PARK = (KP > 1) ? KP - 1 : 1;
+  const int R = a.R;
+  if (a.SP != a.S) {
+    // Few splits (a short list): every wave writes its own partial, split
+    // s * KP + p, and the merge kernel combines them; no LDS merge and no
+    // barrier here.  The wave's running maximum is the partial's reference.
+    const float lt = sum_across_rows(l_run), rt = sum_across_rows(l_rnd);
+    const int r16 = lane & 15, q4 = lane >> 4;
+    const int n = nb * 16 + r16;
+    if (active && n < R) {
+      const size_t sp = (size_t)u * a.SP + (size_t)s * KP + p;
+      float* pa = a.part_acc + sp * R * D + (size_t)n * D;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4_t*>(pa + db * 16 + 4 * q4) = acc[db];
+      if (q4 == 0) {
+        float* pm = a.part_ml + sp * 3 * R;
+        pm[n] = m_run;
+        pm[R + n] = lt;
+        pm[2 * R + n] = rt;
+      }
+    }
+    return;
+  }
   float* macc = smem;                 // [PARK][RP][DP] parked accumulators of phases 1..KP-1
   float* mm = macc + PARK * RP * DP;  // [KP][RP]
   float* ml = mm + KP * RP;
@@ -619,7 +641,6 @@ __device__ __forceinline__ void pipe_finish(const AttnArgs& a, float* smem, int 
       *reinterpret_cast<f32x4_t*>(macc + ((p - 1) * RP + n) * DP + db * 16 + 4 * q4) = acc[db] * f;
   }
   __syncthreads();
-  const int R = a.R;
   if (active && p == 0 && n < R) {
     f32x4_t o[8];
 #pragma unroll
@@ -1026,6 +1047,9 @@ __global__ __launch_bounds__(256, 1) void attn_f32_kernel(AttnArgs a) {
 // the overall maximum.  One load round trip and one barrier on the critical
 // path; no thread waits for another's weights.
 constexpr int kMaxSplits = 4096;
+// Up to this many partials per unit, the pipelined kernel's waves write one
+// each (no LDS merge at the end of a split).
+constexpr int kWavePartials = 64;
 constexpr int kMergeThreads = 512;   // more groups over the splits: more loads in flight
 constexpr int kMergeSlice = 64;       // output columns per workgroup: one wave per split
 constexpr int kMergeLoads = 4096;     // partial values one workgroup requests per round
@@ -1038,7 +1062,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
   static_assert(DS % 64 == 0 && PB >= 1, "merge shape");
   __shared__ float part[NG][DS];
   __shared__ float gstat[3][NG];
-  const int R = a.R, S = a.S;
+  const int R = a.R, S = a.SP;
   const int row = blockIdx.x / (D / DS), slice = blockIdx.x - row * (D / DS);
   const int u = row / R, r = row - u * R;
   const int b = u / a.Hkv, g = u - b * a.Hkv;
@@ -1195,13 +1219,15 @@ AttnPlan plan_attention(int units, int t_max, int rows, int d, bool gather, size
   int S = (int)((T + chunk - 1) / chunk);
   if (S < 1) S = 1;
   p.S = S;
+  p.sp_max = (S > 1 && S * 4 <= kWavePartials) ? S * 4 : S;
   p.chunk = (int)chunk;
   p.grid = units * S;
   p.gather = gather;
   if (S > 1) {
+    const size_t sp = (size_t)units * p.sp_max;
     p.off_acc = align_up(scratch_off, 256);
-    p.off_ml = p.off_acc + align_up((size_t)units * S * rows * d * sizeof(float), 256);
-    p.ws_bytes = p.off_ml + align_up((size_t)units * S * 3 * rows * sizeof(float), 256);
+    p.off_ml = p.off_acc + align_up(sp * rows * d * sizeof(float), 256);
+    p.ws_bytes = p.off_ml + align_up(sp * 3 * rows * sizeof(float), 256);
   }
   return p;
 }
@@ -1209,6 +1235,14 @@ AttnPlan plan_attention(int units, int t_max, int rows, int d, bool gather, size
 spec_status_t launch_attention(AttnArgs a, int d, int dtype, const AttnPlan& plan, void* ws,
                                hipStream_t stream) {
   a.S = plan.S;
+  a.SP = plan.S;
+  if (plan.S > 1 && dtype == SPEC_BF16 && d == 128) {
+    // the pipelined kernel's waves write their own partials when that keeps
+    // the merge small (phases per split as in PipeCfg)
+    const int nb = min(4, (a.R + 15) / 16);
+    const int kp = (nb >= 3) ? 2 : 4 / nb;
+    if (plan.S * kp <= plan.sp_max) a.SP = plan.S * kp;
+  }
   a.chunk = plan.chunk;
   if (plan.S > 1) {
     a.part_acc = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + plan.off_acc);

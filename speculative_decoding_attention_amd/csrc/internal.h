@@ -41,6 +41,7 @@ struct AttnArgs {
   int32_t mode;
   int32_t B, Hq, Hkv, G, n_max, R, max_len;
   int32_t S, chunk;           // splits per unit and slots per split
+  int32_t SP;                 // partials per unit: S, or S * phases when each wave writes its own
   float scale_log2;           // softmax scale * log2(e)
   float* part_acc;            // [U*S, R, D] unnormalised partial outputs
   float* part_ml;             // [U*S, 3, R] partial (max, sum, rounded-weight sum), log2 domain
@@ -57,6 +58,7 @@ constexpr size_t kSyncBytes = SPEC_WS_SYNC_BYTES;
 
 struct AttnPlan {
   int S = 1;
+  int sp_max = 1;             // partials per unit the workspace holds (S, or S * 4)
   int chunk = 0;
   int grid = 0;
   bool gather = false;        // slots resolved through a list or a page table
