@@ -1,29 +1,33 @@
 // Split-K flash-decoding attention for gfx950: the shared engine behind
 // verification attention (dense positions), text-anchored draft attention
-// (positions from a text index list) and top-K sparse draft attention
-// (positions from a per-head selection list).
+// (positions from a text index list), top-K sparse draft attention
+// (positions from a per-head selection list) and the Sparse-to-Dense draft
+// attention (a per-head kept list plus a dense tail).
 //
 // Work decomposition.  A unit is a (sequence b, KV head g) pair; its query
 // block is the n_max * G rows (query position i, head-in-group hh), row
 // r = i*G + hh, padded to NB*16 rows.  The unit's key slots are cut into S
-// splits of `chunk` slots; one 256-thread workgroup (4 waves) owns one split
-// and each wave streams 32-slot tiles of it independently with its own
-// online-softmax state.  The waves merge in LDS; the workgroup writes either
-// the final output (S == 1) or an unnormalised partial that a small merge
-// kernel combines with the log-sum-exp rule.
+// splits of `chunk` slots, about one workgroup per CU in all.  A workgroup
+// writes either the final output (S == 1) or unnormalised partials that
+// attn_merge_kernel combines with the log-sum-exp rule.
 //
-// Per tile and wave (bf16, d = 128):
-//   S^T = K Q^T   on v_mfma_f32_16x16x32_bf16: A = 16 keys x 32 d straight
-//                 from global memory, B = the query block held in registers;
-//                 the key order inside a tile is permuted so that each lane's
-//                 8 scores are 8 consecutive keys of one query row.
-//   online softmax in fp32 (exp2 domain), row maxima across the four 16-lane
-//                 rows of the wave.
-//   O^T += V^T P^T on the same MFMA: the probabilities are already laid out
-//                 as the B operand; V is transposed through LDS as packed
-//                 (key, key+1) bf16 pairs so each lane reads its A operand
-//                 with one 16-byte LDS load.
-// The fp32 variant uses v_mfma_f32_16x16x4_f32, where V needs no transpose.
+// bf16, d = 128 (attn_bf16_pipe_kernel): K/V rows move HBM -> LDS by DMA
+// (global_load_lds_dwordx4) into a 128 KiB ring of tiles, so data in flight
+// costs no registers.  Each wave owns up to 16 query rows (NB row blocks) and
+// one 32-key sub-tile phase of every tile; with NB >= 3 eight waves form two
+// teams on alternate sub-tiles.  Per sub-tile:
+//   S^T = K Q^T   on v_mfma_f32_16x16x32_bf16, K from the swizzled LDS tile,
+//                 Q^T held in registers;
+//   online softmax in fp32 (exp2 domain) against a lazily raised reference;
+//   O^T += V^T P^T with V^T read transposed from LDS (ds_read_b64_tr_b16)
+//                 and P already laid out as the B operand.
+// At the end the phases are merged in LDS, or, when a unit has few splits,
+// every wave writes its own partial.
+//
+// d = 64 bf16 and fp32 (attn_bf16_kernel, attn_f32_kernel): four waves per
+// workgroup stream 32-slot tiles from global memory into registers, each
+// with its own online-softmax state, and merge in LDS; the fp32 variant uses
+// v_mfma_f32_16x16x4_f32, where V needs no transpose.
 #include <math.h>
 
 #include <atomic>
@@ -1050,7 +1054,7 @@ constexpr int kMaxSplits = 4096;
 // Up to this many partials per unit, the pipelined kernel's waves write one
 // each (no LDS merge at the end of a split).
 constexpr int kWavePartials = 64;
-constexpr int kMergeThreads = 512;   // more groups over the splits: more loads in flight
+constexpr int kMergeThreads = 512;   // 8 groups of 64 threads over the splits
 constexpr int kMergeSlice = 64;       // output columns per workgroup: one wave per split
 constexpr int kMergeLoads = 4096;     // partial values one workgroup requests per round
 
