@@ -1145,6 +1145,63 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
         live ? (Mx + log2f(Ls)) * 0.69314718055994531f : -INFINITY;
 }
 
+// Few partials per unit (a batch of short or ragged units): one thread per
+// (row, column), 256 / D rows per workgroup, every partial of the row
+// requested in one round.  The grouped kernel above would spend a 512-thread
+// workgroup on each (row, 64 columns) with most groups idle.
+constexpr int kMergeSmall = 8;
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_merge_small_kernel(AttnArgs a) {
+  constexpr int RPW = 256 / D;
+  const int R = a.R, S = a.SP;
+  const int blocks_per_unit = (R + RPW - 1) / RPW;
+  const int u = blockIdx.x / blocks_per_unit, rb = blockIdx.x - u * blocks_per_unit;
+  // the row is uniform over a wave (D is a multiple of 64): scalar statistics
+  const int r = __builtin_amdgcn_readfirstlane(rb * RPW + (int)threadIdx.x / D);
+  if (r >= R) return;
+  const int d = threadIdx.x % D;
+  const int b = u / a.Hkv, g = u - b * a.Hkv;
+  const int i = r / a.G, hh = r - i * a.G;
+  const float* pm = a.part_ml + (size_t)u * S * 3 * R + r;
+  const float* pa = a.part_acc + (size_t)u * S * R * D + (size_t)r * D + d;
+  float v[kMergeSmall], mv[kMergeSmall], lv[kMergeSmall], rv[kMergeSmall];
+#pragma unroll
+  for (int j = 0; j < kMergeSmall; ++j) {          // clamped, masked after
+    const int sp = min(j, S - 1);
+    v[j] = pa[(size_t)sp * R * D];
+    mv[j] = pm[(size_t)sp * 3 * R];
+    lv[j] = pm[(size_t)sp * 3 * R + R];
+    rv[j] = pm[(size_t)sp * 3 * R + 2 * R];
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kMergeSmall; ++j) {
+    if (j >= S) mv[j] = -INFINITY;
+    M = fmaxf(M, mv[j]);
+  }
+  const float Mu = (M == -INFINITY) ? 0.f : M;
+  float o = 0.f, Ls = 0.f, Lr = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMergeSmall; ++j) {
+    const float w = __builtin_amdgcn_exp2f(mv[j] - Mu);
+    o = __builtin_fmaf(v[j], w, o);
+    Ls = __builtin_fmaf(lv[j], w, Ls);
+    Lr = __builtin_fmaf(rv[j], w, Lr);
+  }
+  const int nq = a.q_len ? a.q_len[b] : a.n_max;
+  const bool live = (i < nq) && (Ls > 0.f);
+  o = live ? o / Lr : 0.f;
+  const size_t oi = (((size_t)b * a.n_max + i) * a.Hq + g * a.G + hh) * D + d;
+  if (a.out_bf16)
+    reinterpret_cast<uint16_t*>(a.out)[oi] = (uint16_t)f32_to_bf16_bits(o);
+  else
+    reinterpret_cast<float*>(a.out)[oi] = o;
+  if (a.lse && d == 0)
+    a.lse[((size_t)b * a.n_max + i) * a.Hq + g * a.G + hh] =
+        live ? (M + log2f(Ls)) * 0.69314718055994531f : -INFINITY;
+}
+
 template <int D, int NB, bool GATHER>
 hipError_t launch_d_nb(const AttnArgs& a, int dtype, int grid, hipStream_t st) {
   if (dtype == SPEC_BF16 && D == 128)
@@ -1265,11 +1322,21 @@ spec_status_t launch_attention(AttnArgs a, int d, int dtype, const AttnPlan& pla
                   : launch_d<128, false>(a, dtype, plan.grid, stream);
   if (e != hipSuccess) return SPEC_ERR_HIP;
   if (plan.S > 1) {
-    const int blocks = a.B * a.Hkv * a.R * (d > kMergeSlice ? d / kMergeSlice : 1);
-    if (d == 64)
-      hipLaunchKernelGGL(attn_merge_kernel<64>, dim3(blocks), dim3(kMergeThreads), 0, stream, a);
-    else
-      hipLaunchKernelGGL(attn_merge_kernel<128>, dim3(blocks), dim3(kMergeThreads), 0, stream, a);
+    const int units = a.B * a.Hkv;
+    if (a.SP <= kMergeSmall) {
+      const int rpw = 256 / d;
+      const int blocks = units * ((a.R + rpw - 1) / rpw);
+      if (d == 64)
+        hipLaunchKernelGGL(attn_merge_small_kernel<64>, dim3(blocks), dim3(256), 0, stream, a);
+      else
+        hipLaunchKernelGGL(attn_merge_small_kernel<128>, dim3(blocks), dim3(256), 0, stream, a);
+    } else {
+      const int blocks = units * a.R * (d > kMergeSlice ? d / kMergeSlice : 1);
+      if (d == 64)
+        hipLaunchKernelGGL(attn_merge_kernel<64>, dim3(blocks), dim3(kMergeThreads), 0, stream, a);
+      else
+        hipLaunchKernelGGL(attn_merge_kernel<128>, dim3(blocks), dim3(kMergeThreads), 0, stream, a);
+    }
     if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
   }
   return SPEC_OK;
