@@ -738,20 +738,27 @@ __global__ __launch_bounds__(PipeCfg<NB>::WAVES * 64, 1) void attn_bf16_pipe_ker
   sm.pos = s_pos;
   sm.row = s_row;
   sm.set_pages(a, g);
-  // Dense splits: tile 0 and the query block go out before the sequence
-  // length is known, so their round trips overlap the length's.  Tile 0's
-  // slots are clamped to the split's end as planned over the cache capacity,
-  // so every row it names lies inside the cache.  Rows past the sequence's
-  // end may hold anything (a masked key still adds 0 * V), so when the
-  // sequence ends inside tile 0 the tile is requested again below.
-  const int spec_end = min(t_beg + a.chunk, a.max_len);
-  if (!GATHER) {
-    pipe_issue_tile<NB, GATHER>(a, sm, t_beg, spec_end, ring_lds, wave, lane);
-    pipe_issue_q<NB>(a, b, g, ring_lds + kQSlot, wave, lane);
-  }
+  // The lengths are requested first (scalar loads, not queued behind the
+  // DMA requests below); their values are waited for only where used.
   const int pre = GATHER ? prefetch_slot(a, b, g, t_beg) : 0;
   const int L = a.kv_len[b];
   const int nq = a.q_len ? a.q_len[b] : a.n_max;
+  // Dense splits: the first NS - 1 tiles and the query block go out before
+  // the sequence length is known, so their round trips overlap the length's.
+  // Their slots are clamped to the split's end as planned over the cache
+  // capacity, so every row they name lies inside the cache.  Rows past the
+  // sequence's end may hold anything (a masked key still adds 0 * V), so
+  // when the sequence ends inside these tiles they are requested again below.
+  const int spec_end = min(t_beg + a.chunk, a.max_len);
+  const int spec_tiles =
+      GATHER ? 0 : min(C::NS - 1, (spec_end - t_beg + C::TILE_KEYS - 1) / C::TILE_KEYS);
+  if (!GATHER) {
+    pipe_issue_tile<NB, GATHER>(a, sm, t_beg, spec_end, ring_lds, wave, lane);
+    pipe_issue_q<NB>(a, b, g, ring_lds + kQSlot, wave, lane);
+    for (int j = 1; j < spec_tiles; ++j)
+      pipe_issue_tile<NB, GATHER>(a, sm, t_beg + j * C::TILE_KEYS, spec_end,
+                                  ring_lds + (uint32_t)(j * C::TILE_BYTES), wave, lane);
+  }
   const int T = unit_slots(a, b, g, L);
   const int t_end = min(T, t_beg + a.chunk);
   const int n_tiles = t_end > t_beg ? (t_end - t_beg + C::TILE_KEYS - 1) / C::TILE_KEYS : 0;
@@ -775,13 +782,17 @@ __global__ __launch_bounds__(PipeCfg<NB>::WAVES * 64, 1) void attn_bf16_pipe_ker
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) qop[ks] = as_bf16x8(u32x4_t{0, 0, 0, 0});
 
-  if (!GATHER && n_tiles > 0 && t_end < min(t_beg + C::TILE_KEYS, spec_end)) {
-    // tile 0 named rows past the sequence: every wave's requests land before
-    // any wave re-requests the slot
+  if (!GATHER && n_tiles > 0 &&
+      t_end < min(t_beg + min(spec_tiles, n_tiles) * C::TILE_KEYS, spec_end)) {
+    // an early tile that is read named rows past the sequence: every wave's
+    // requests land before any wave re-requests those slots (early tiles
+    // past n_tiles are never read, and the loop's waits cover them)
     wait_dma_barrier<0>();
-    pipe_issue_tile<NB, GATHER>(a, sm, t_beg, t_end, ring_lds, wave, lane);
+    for (int j = 0; j < spec_tiles && j < n_tiles; ++j)
+      pipe_issue_tile<NB, GATHER>(a, sm, t_beg + j * C::TILE_KEYS, t_end,
+                                  ring_lds + (uint32_t)(j * C::TILE_BYTES), wave, lane);
   }
-  for (int j = GATHER ? 0 : 1; j < C::NS - 1 && j < n_tiles; ++j)
+  for (int j = GATHER ? 0 : spec_tiles; j < C::NS - 1 && j < n_tiles; ++j)
     pipe_issue_tile<NB, GATHER>(a, sm, t_beg + j * C::TILE_KEYS, t_end,
                                 ring_lds + (uint32_t)(j * C::TILE_BYTES), wave, lane);
 
