@@ -180,13 +180,14 @@ def test_paged_equals_contiguous_on_device():
 
 
 @pytest.mark.parametrize("dt", [W.BF16, W.F32])
-@pytest.mark.parametrize("L", [(5000, 3100, 130), (904, 2017, 130)])
+@pytest.mark.parametrize("L", [(5000, 3100, 130), (904, 2017, 130), (938, 997, 1300)])
 def test_rows_past_the_length_are_never_used(dt, L):
     """Cache capacity beyond kv_len holds NaN keys and infinite values: the
     output must still match the oracle (which never reads those rows).  With
-    256 CUs these shapes plan 288-key splits; 904 and 2017 end 40 keys and
-    1 key into a split's first 64-key tile, which the dense kernel requests
-    before the length is known and must request again."""
+    256 CUs these shapes plan 288-key splits whose first three 64-key tiles
+    the dense kernel requests before the length is known; 904 and 2017 end
+    inside a split's tile 0, 938 inside tile 1, 997 and 1300 inside tile 2,
+    so those tiles are requested again."""
     c = W.small_attn(41, 3, 28, 4, 128, 6, L, dt, max_len=5600)
     kb, vb = c.k.bits.copy(), c.v.bits.copy()
     nan, inf = (0x7FC0, 0x7F80) if dt == W.BF16 else (np.nan, np.inf)   # bf16 bits / fp32 values
