@@ -224,8 +224,12 @@ __device__ __forceinline__ void tile_rows(const StdArgs& a, const u32x4_t (&kc)[
 #pragma unroll
       for (int i = 0; i < 4; ++i) c[rg][i] = (kb + 4 * q4 + i <= pos[rg]) ? c[rg][i] : -INFINITY;
     }
-    // the scale is positive, so the maximum can be taken before scaling
-    tmax[rg] = fmaxf(fmaxf(c[rg][0], c[rg][1]), fmaxf(c[rg][2], c[rg][3])) * a.scale_log2;
+    // the scale is positive, so the maximum can be taken before scaling; the
+    // IEEE maximum (NaN-propagating) needs no canonicalisation of the
+    // matrix-core results, unlike fmaxf
+    tmax[rg] = __builtin_elementwise_maximum(__builtin_elementwise_maximum(c[rg][0], c[rg][1]),
+                                             __builtin_elementwise_maximum(c[rg][2], c[rg][3])) *
+               a.scale_log2;
     raise |= tmax[rg] > m[rg] + 8.f;
   }
   // lazily raised reference: terms stay <= 2^8 and raises are rare
