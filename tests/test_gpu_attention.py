@@ -92,6 +92,20 @@ def test_small_vata(cfg):
     assert_attention_close(out, lse, ro, rl, c.q_len, dt, f"small vata {seed}")
 
 
+@pytest.mark.parametrize("n,page", [(1, 0), (3, 16), (6, 0)])
+def test_many_short_units(n, page):
+    """A batch of 32 short ragged sequences: 128 units of one or two splits,
+    so the split kernel's waves write their own partials and the merge takes
+    the one-thread-per-column path (at most 8 partials per unit)."""
+    rng = np.random.default_rng(50 + n)
+    L = tuple(int(x) for x in rng.integers(max(n, 100), 601, size=32))
+    c = W.small_attn(60 + n, 32, 28, 4, 128, n, L, W.BF16, page_size=page)
+    out, lse, ro, rl = _verify_pair(c)
+    assert_attention_close(out, lse, ro, rl, c.q_len, W.BF16, f"short units verify n={n}")
+    out, lse, ro, rl = _vata_pair(c)
+    assert_attention_close(out, lse, ro, rl, c.q_len, W.BF16, f"short units vata n={n}")
+
+
 def test_padded_query_rows_and_bf16_output():
     c = W.small_attn(11, 3, 8, 2, 128, 6, (900, 450, 1200), W.BF16, q_len=[6, 2, 4])
     out, lse, ro, rl = _verify_pair(c, out_dtype=torch.bfloat16)
