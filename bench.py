@@ -93,8 +93,8 @@ def _source_hash(names):
 def main():
     args = _parse()
     if args.gpus != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(sharding is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path; "
+              "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch

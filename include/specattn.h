@@ -96,7 +96,7 @@ typedef enum {
   SPEC_ERR_SHAPE = 2,       /* a size is out of range or inconsistent         */
   SPEC_ERR_DTYPE = 3,       /* unsupported dtype or dtype combination         */
   SPEC_ERR_WORKSPACE = 4,   /* ws_bytes below the spec_*_workspace() size     */
-  SPEC_ERR_UNSUPPORTED = 5, /* valid request outside what this build supports */
+  SPEC_ERR_UNSUPPORTED = 5, /* valid request outside what the library supports */
   SPEC_ERR_HIP = 6          /* the HIP runtime refused a launch or query      */
 } spec_status_t;
 

@@ -116,7 +116,7 @@ const char* spec_status_str(spec_status_t status) {
     case SPEC_ERR_SHAPE: return "SPEC_ERR_SHAPE: a size is out of range or inconsistent";
     case SPEC_ERR_DTYPE: return "SPEC_ERR_DTYPE: unsupported dtype or dtype combination";
     case SPEC_ERR_WORKSPACE: return "SPEC_ERR_WORKSPACE: workspace smaller than required";
-    case SPEC_ERR_UNSUPPORTED: return "SPEC_ERR_UNSUPPORTED: outside what this build supports";
+    case SPEC_ERR_UNSUPPORTED: return "SPEC_ERR_UNSUPPORTED: outside what the library supports";
     case SPEC_ERR_HIP: return "SPEC_ERR_HIP: the HIP runtime refused a launch or query";
   }
   return "unknown spec_status_t";
