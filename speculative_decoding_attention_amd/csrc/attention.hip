@@ -43,7 +43,9 @@ constexpr int kTK = 32;   // key slots per tile
 constexpr int kNW = 4;    // waves per workgroup
 constexpr int kPV = 20;   // dwords per LDS row of a transposed V tile (16 + 4 pad)
 
-constexpr int kMaxChunk = 4096;  // slots per split whose (position, row) are staged in LDS
+// Slots per split whose (position, row) are staged in LDS; with the 128 KiB
+// ring and the per-32-slot maxima this fills the 160 KiB of LDS.
+constexpr int kMaxChunk = 4032;
 
 // Where the key slots of one split live.  Dense contiguous splits compute
 // position and row arithmetically; every other layout (a text index list, a
@@ -56,8 +58,8 @@ struct SlotMap {
   const int* pos;         // gather: LDS positions of slots t_beg..
   const uint32_t* row;    // gather: LDS row indices of slots t_beg.. (or pages, below)
   // Dense slots in a paged cache (every position in order): row[] holds the
-  // split's pages instead, from page pg0 on, so a split can span 4096 pages
-  // rather than 4096 slots.  shift = log2(page size), or -1 for a list.
+  // split's pages instead, from page pg0 on, so a split can span 4031 pages
+  // rather than 4032 slots.  shift = log2(page size), or -1 for a list.
   int shift, pg0;
   uint32_t hkv, g;
   __device__ __forceinline__ int position(int slot) const {
@@ -105,7 +107,8 @@ __device__ __forceinline__ int prefetch_slot(const AttnArgs& a, int b, int g, in
 // table when the cache is paged.  Rows fit 32 bits for any pool that fits in
 // device memory.  `pre` is prefetch_slot's value for the first slot.
 __device__ __forceinline__ void stage_slots(const AttnArgs& a, int b, int g, int L, int t_beg,
-                                            int t_end, int* pos, uint32_t* row, int pre) {
+                                            int t_end, int* pos, uint32_t* row, int* bmax,
+                                            int pre) {
   const size_t u = (size_t)b * a.Hkv + g;
   if (a.mode == 0) {              // every position of a paged cache: stage the pages
     if (t_end <= t_beg) return;
@@ -117,27 +120,40 @@ __device__ __forceinline__ void stage_slots(const AttnArgs& a, int b, int g, int
   const int n_list = (a.mode == 3) ? a.slot_len[u] : 0;
   const int t0 = (a.mode == 3) ? tail_begin(a, b, L) : 0;
   const int first = t_beg + (int)threadIdx.x;
-  for (int t = first; t < t_end; t += blockDim.x) {
+  // Every thread runs every round (t_beg and blockDim are multiples of 32),
+  // so each 32-lane half of a wave can also reduce the largest position of
+  // its 32 consecutive slots: a sub-tile whose largest position precedes
+  // every query row needs no mask.  List reads past t_end are clamped.
+  for (int r0 = t_beg; r0 < t_end; r0 += blockDim.x) {
+    const int t = r0 + (int)threadIdx.x;
+    const int tc = min(t, t_end - 1);
     int p;
     bool skip = false;          // a list entry inside the tail: the tail has it
-    if (a.mode == 1) p = (t == first) ? pre : a.slots[(size_t)b * a.slot_stride + t];
-    else if (a.mode == 2) p = (t == first) ? pre : a.slots[u * a.slot_stride + t];
-    else if (t < n_list) {
-      p = (t == first) ? pre : a.slots[u * a.slot_stride + t];
+    if (a.mode == 1) p = (t == first) ? pre : a.slots[(size_t)b * a.slot_stride + tc];
+    else if (a.mode == 2) p = (t == first) ? pre : a.slots[u * a.slot_stride + tc];
+    else if (tc < n_list) {
+      p = (t == first) ? pre : a.slots[u * a.slot_stride + tc];
       skip = p >= t0;
     } else {
-      p = t0 + (t - n_list);
+      p = t0 + (tc - n_list);
     }
-    uint32_t r;
-    if (a.page_shift >= 0) {
-      const int page = a.page_table[(size_t)b * a.max_pages + (p >> a.page_shift)];
-      r = (((uint32_t)page * (uint32_t)a.Hkv + (uint32_t)g) << a.page_shift) +
-          (uint32_t)(p & ((1 << a.page_shift) - 1));
-    } else {
-      r = ((uint32_t)b * (uint32_t)a.Hkv + (uint32_t)g) * (uint32_t)a.max_len + (uint32_t)p;
+    const int vis = skip ? 0x7fffffff : p;      // never visible; its row is still a real one
+    if (t < t_end) {
+      uint32_t r;
+      if (a.page_shift >= 0) {
+        const int page = a.page_table[(size_t)b * a.max_pages + (p >> a.page_shift)];
+        r = (((uint32_t)page * (uint32_t)a.Hkv + (uint32_t)g) << a.page_shift) +
+            (uint32_t)(p & ((1 << a.page_shift) - 1));
+      } else {
+        r = ((uint32_t)b * (uint32_t)a.Hkv + (uint32_t)g) * (uint32_t)a.max_len + (uint32_t)p;
+      }
+      pos[t - t_beg] = vis;
+      row[t - t_beg] = r;
     }
-    pos[t - t_beg] = skip ? 0x7fffffff : p;     // never visible; its row is still a real one
-    row[t - t_beg] = r;
+    int mx = (t < t_end) ? vis : 0x7fffffff;
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) mx = max(mx, __shfl_xor(mx, o));
+    if ((threadIdx.x & 31) == 0 && t < t_end) bmax[(t - t_beg) >> 5] = mx;
   }
 }
 
@@ -433,6 +449,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
   __shared__ float smem[(V_DW > M_DW) ? V_DW : M_DW];
   __shared__ int s_pos[GATHER ? kMaxChunk : 1];
   __shared__ uint32_t s_row[GATHER ? kMaxChunk : 1];
+  __shared__ int s_bmax[GATHER ? kMaxChunk / 32 : 1];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, q4 = lane >> 4;
@@ -453,7 +470,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
   sm.row = s_row;
   sm.set_pages(a, g);
   if (GATHER) {
-    stage_slots(a, b, g, L, t_beg, t_end, s_pos, s_row, pre);
+    stage_slots(a, b, g, L, t_beg, t_end, s_pos, s_row, s_bmax, pre);
     __syncthreads();
   }
 
@@ -719,6 +736,7 @@ __global__ __launch_bounds__(PipeCfg<NB>::WAVES * 64, 1) void attn_bf16_pipe_ker
   __shared__ __align__(16) unsigned char ring[C::RING_BYTES];
   __shared__ int s_pos[GATHER ? kMaxChunk : 1];
   __shared__ uint32_t s_row[GATHER ? kMaxChunk : 1];
+  __shared__ int s_bmax[GATHER ? kMaxChunk / 32 : 1];
   static_assert(((C::KP > 1) ? C::KP - 1 : 1) * (NB * 16) * (D + 4) * 4 + 7 * C::KP * NB * 16 * 4 <=
                     C::RING_BYTES,
                 "epilogue fits the ring");
@@ -763,7 +781,7 @@ __global__ __launch_bounds__(PipeCfg<NB>::WAVES * 64, 1) void attn_bf16_pipe_ker
   const int t_end = min(T, t_beg + a.chunk);
   const int n_tiles = t_end > t_beg ? (t_end - t_beg + C::TILE_KEYS - 1) / C::TILE_KEYS : 0;
   if (GATHER) {
-    stage_slots(a, b, g, L, t_beg, t_end, s_pos, s_row, pre);
+    stage_slots(a, b, g, L, t_beg, t_end, s_pos, s_row, s_bmax, pre);
     __syncthreads();
   }
 
@@ -840,7 +858,11 @@ __global__ __launch_bounds__(PipeCfg<NB>::WAVES * 64, 1) void attn_bf16_pipe_ker
     }
     // causal / list / tail mask; a dense tile that lies entirely before the
     // first query row's position and before the split end needs none
-    const bool full = !GATHER && sub0 + 32 <= t_end && sub0 + 31 <= L - nq;
+    // (no short circuit: a guarded LDS read becomes a branch with its own wait)
+    const int smax = GATHER ? ((sm.shift >= 0) ? sub0 + 31
+                                               : s_bmax[min((sub0 - t_beg) >> 5, kMaxChunk / 32 - 1)])
+                            : sub0 + 31;
+    const bool full = (sub0 + 32 <= t_end) & (smax <= L - nq);
     if (!full) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -934,6 +956,7 @@ __global__ __launch_bounds__(256, 1) void attn_f32_kernel(AttnArgs a) {
   __shared__ float smem[M_DW];
   __shared__ int s_pos[GATHER ? kMaxChunk : 1];
   __shared__ uint32_t s_row[GATHER ? kMaxChunk : 1];
+  __shared__ int s_bmax[GATHER ? kMaxChunk / 32 : 1];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, q4 = lane >> 4;
@@ -956,7 +979,7 @@ __global__ __launch_bounds__(256, 1) void attn_f32_kernel(AttnArgs a) {
   sm.row = s_row;
   sm.set_pages(a, g);
   if (GATHER) {
-    stage_slots(a, b, g, L, t_beg, t_end, s_pos, s_row, pre);
+    stage_slots(a, b, g, L, t_beg, t_end, s_pos, s_row, s_bmax, pre);
     __syncthreads();
   }
 
