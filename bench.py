@@ -452,7 +452,9 @@ def main():
         c3_verify(kv3), c3_vata(kv3)
         torch.cuda.synchronize()
         t_ver = time_graph(capture(lambda: c3_verify(kv3)), reps3) * 1e3
-        t_vat = time_graph(capture(lambda: c3_vata(kv3)), reps3) * 1e3
+        # a call this short is timed four to a graph, so that the host's graph
+        # launch is not on the clock
+        t_vat = time_graph(capture(lambda: [c3_vata(kv3) for _ in range(4)]), reps3) * 1e3 / 4
         del kp, vp, kv3
         mx = int(lay.L.max())
         kc = torch.randn(B3, Hkv, mx, d, device=dev).mul_(0.5).to(torch.bfloat16)
