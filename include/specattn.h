@@ -22,7 +22,8 @@
  *   anything is enqueued, so nothing is partially written.
  * - Workspace: scratch memory comes from the caller (`ws`, `ws_bytes`), sized
  *   by the matching spec_*_workspace() query (which depends only on shapes;
- *   a size of 0 means the call needs none and `ws` may be NULL).  Its first
+ *   a size of 0 means the call needs none and `ws` may be NULL; otherwise
+ *   `ws` is 256-byte aligned, as every hipMalloc allocation is).  Its first
  *   SPEC_WS_SYNC_BYTES bytes are a synchronisation region (arrival counters,
  *   packed row maxima, selection histograms): the caller zero-fills a new
  *   workspace once, before its first use, and every call returns the words
@@ -95,7 +96,8 @@ typedef enum {
   SPEC_ERR_NULL = 1,        /* a required pointer is NULL                     */
   SPEC_ERR_SHAPE = 2,       /* a size is out of range or inconsistent         */
   SPEC_ERR_DTYPE = 3,       /* unsupported dtype or dtype combination         */
-  SPEC_ERR_WORKSPACE = 4,   /* ws_bytes below the spec_*_workspace() size     */
+  SPEC_ERR_WORKSPACE = 4,   /* ws_bytes below the spec_*_workspace() size,
+                               or ws not 256-byte aligned                  */
   SPEC_ERR_UNSUPPORTED = 5, /* valid request outside what the library supports */
   SPEC_ERR_HIP = 6          /* the HIP runtime refused a launch or query      */
 } spec_status_t;

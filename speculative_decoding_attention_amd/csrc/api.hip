@@ -98,6 +98,7 @@ spec_status_t check_ws(size_t need, const void* ws, size_t ws_bytes) {
   if (need == 0) return SPEC_OK;
   if (!ws) return SPEC_ERR_NULL;
   if (ws_bytes < need) return SPEC_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) & 255u) return SPEC_ERR_WORKSPACE;   // 256-byte aligned
   return SPEC_OK;
 }
 

@@ -90,6 +90,7 @@ def test_verify_rejects_bad_args(L):
     assert need > 0
     assert _verify(L, kv, ws=None, ws_bytes=0) == 1
     assert _verify(L, kv, ws=FAKE, ws_bytes=need - 1) == 4
+    assert _verify(L, kv, ws=FAKE + 128, ws_bytes=need) == 4   # not 256-byte aligned
 
 
 def test_vata_topk_rejections(L):
