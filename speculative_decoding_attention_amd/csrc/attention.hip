@@ -105,7 +105,8 @@ __device__ __forceinline__ int prefetch_slot(const AttnArgs& a, int b, int g, in
 // Resolves slots [t_beg, t_end) of (b, g) into LDS: logical position from the
 // slot list (or the slot itself), then the physical row through the page
 // table when the cache is paged.  Rows fit 32 bits for any pool that fits in
-// device memory.  `pre` is prefetch_slot's value for the first slot.
+// device memory.  `pre` is prefetch_slot's value for the first slot.  `bmax`
+// (optional) receives the largest visible position of every 32 slots.
 __device__ __forceinline__ void stage_slots(const AttnArgs& a, int b, int g, int L, int t_beg,
                                             int t_end, int* pos, uint32_t* row, int* bmax,
                                             int pre) {
@@ -153,7 +154,7 @@ __device__ __forceinline__ void stage_slots(const AttnArgs& a, int b, int g, int
     int mx = (t < t_end) ? vis : 0x7fffffff;
 #pragma unroll
     for (int o = 16; o > 0; o >>= 1) mx = max(mx, __shfl_xor(mx, o));
-    if ((threadIdx.x & 31) == 0 && t < t_end) bmax[(t - t_beg) >> 5] = mx;
+    if (bmax && (threadIdx.x & 31) == 0 && t < t_end) bmax[(t - t_beg) >> 5] = mx;
   }
 }
 
@@ -449,7 +450,6 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
   __shared__ float smem[(V_DW > M_DW) ? V_DW : M_DW];
   __shared__ int s_pos[GATHER ? kMaxChunk : 1];
   __shared__ uint32_t s_row[GATHER ? kMaxChunk : 1];
-  __shared__ int s_bmax[GATHER ? kMaxChunk / 32 : 1];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, q4 = lane >> 4;
@@ -470,7 +470,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
   sm.row = s_row;
   sm.set_pages(a, g);
   if (GATHER) {
-    stage_slots(a, b, g, L, t_beg, t_end, s_pos, s_row, s_bmax, pre);
+    stage_slots(a, b, g, L, t_beg, t_end, s_pos, s_row, nullptr, pre);
     __syncthreads();
   }
 
@@ -956,7 +956,6 @@ __global__ __launch_bounds__(256, 1) void attn_f32_kernel(AttnArgs a) {
   __shared__ float smem[M_DW];
   __shared__ int s_pos[GATHER ? kMaxChunk : 1];
   __shared__ uint32_t s_row[GATHER ? kMaxChunk : 1];
-  __shared__ int s_bmax[GATHER ? kMaxChunk / 32 : 1];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, q4 = lane >> 4;
@@ -979,7 +978,7 @@ __global__ __launch_bounds__(256, 1) void attn_f32_kernel(AttnArgs a) {
   sm.row = s_row;
   sm.set_pages(a, g);
   if (GATHER) {
-    stage_slots(a, b, g, L, t_beg, t_end, s_pos, s_row, s_bmax, pre);
+    stage_slots(a, b, g, L, t_beg, t_end, s_pos, s_row, nullptr, pre);
     __syncthreads();
   }
 
