@@ -127,6 +127,29 @@ def test_vata_empty_and_partial_lists():
     assert_attention_close(out, lse, ro, rl, c.q_len, W.BF16, "vata partial")
 
 
+
+@pytest.mark.parametrize("n,page", [(1, 0), (6, 0), (6, 16)])
+def test_vata_unordered_list_with_repeats(n, page):
+    """A list in no particular order, with repeated positions: 32-entry
+    blocks whose positions all precede every query row alternate with blocks
+    that hide one of the last n positions (visible to some rows only) at a
+    random place, so whole-block visibility is decided per block."""
+    L = (2400, 1900)
+    c = W.small_attn(21 + n, 2, 28, 4, 128, n, L, W.BF16, page_size=page)
+    rng = np.random.default_rng(77 + n)
+    T = 1200
+    idx = np.zeros((2, T), np.int32)
+    for b, Lb in enumerate(L):
+        early = rng.integers(0, Lb - n, size=T).astype(np.int32)
+        early[5:9] = early[1]                        # repeats
+        for blk in range(1, T // 32, 2):             # every other block hides a late one
+            idx_in = blk * 32 + int(rng.integers(0, 32))
+            early[idx_in] = Lb - 1 - int(rng.integers(0, n))
+        idx[b] = early
+    tlen = np.array([T, T - 45], np.int32)           # a ragged final block
+    out, lse, ro, rl = _vata_pair(c, idx=idx, tlen=tlen)
+    assert_attention_close(out, lse, ro, rl, c.q_len, W.BF16, f"vata unordered n={n}")
+
 # -------------------------------------------------------- invariants ----
 
 def test_values_one_gives_one_and_lse_normalises():
