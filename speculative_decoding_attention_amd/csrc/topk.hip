@@ -229,12 +229,24 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(TopkArgs a) {
 
   const int u = blockIdx.x;
   const int b = u / a.Hkv;
-  const int L = a.kv_len[b];
   const int K = a.top_k;
   const double* sc = a.scores + (size_t)u * a.max_len;
   int32_t* out = a.sel_idx + (size_t)u * K;
   uint32_t* gh = a.hist + (size_t)u * kHistBins;
+  const uint16_t* k16 = a.key16 + (size_t)u * a.max_len;
   const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wave = tid >> 6;
+
+  // Requested together with the length, since neither depends on it: this
+  // thread's histogram bins (descending order) and its first batch of 16-bit
+  // keys (indices clamped to the row's capacity; slots at or past the length
+  // are masked where the keys are used).
+  uint32_t c4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c4[i] = gh[kHistBins - 1 - (tid * 4 + i)];
+  uint32_t kv[kSelBatch];
+#pragma unroll
+  for (int k = 0; k < kSelBatch; ++k) kv[k] = k16[min(k * nt + tid, a.max_len - 1)];
+  const int L = a.kv_len[b];
 
   if (K >= L) {
     for (int j = tid; j < K; j += nt) out[j] = (j < L) ? j : -1;
@@ -249,13 +261,9 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(TopkArgs a) {
     s_bin = 0;
     s_above = 0;
   }
-  uint32_t c4[4];
   uint32_t mine = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    c4[i] = gh[kHistBins - 1 - (tid * 4 + i)];   // descending bin order
-    mine += c4[i];
-  }
+  for (int i = 0; i < 4; ++i) mine += c4[i];
   const uint32_t before = block_exclusive_scan(mine, wsum, &s_total);
   {
     uint32_t run = before;
@@ -277,13 +285,13 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(TopkArgs a) {
   //     workgroup streams them all), kSelBatch per thread in flight: keys
   //     above the boundary bin set their selection bit (a wave's ballot
   //     covers 64 consecutive keys), keys in it join the candidate list
-  const uint16_t* k16 = a.key16 + (size_t)u * a.max_len;
   for (int j0 = 0; j0 < L; j0 += nt * kSelBatch) {
-    uint32_t kv[kSelBatch];
     // unconditional loads from clamped indices: a guarded load would be
     // compiled as a branch with its own wait, one round trip per key
+    if (j0 > 0) {
 #pragma unroll
-    for (int k = 0; k < kSelBatch; ++k) kv[k] = k16[min(j0 + k * nt + tid, L - 1)];
+      for (int k = 0; k < kSelBatch; ++k) kv[k] = k16[min(j0 + k * nt + tid, L - 1)];
+    }
     // ballots first, then one LDS reservation per wave for the whole batch
     uint64_t bcs[kSelBatch];
     uint32_t wtotal = 0;
