@@ -39,6 +39,7 @@ constexpr int kHistBins = 4096;
 constexpr int kScoreKeys = 256;   // keys per score workgroup
 constexpr int kCandMax = 4096;    // candidates sortable in LDS
 constexpr int kSelBatch = 16;     // scores in flight per thread in the selection passes
+constexpr int kSelWords = 4;      // 16-byte words of 16-bit keys in flight per thread
 
 struct TopkArgs {
   const void* q;
@@ -239,13 +240,24 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(TopkArgs a) {
   // Requested together with the length, since neither depends on it: this
   // thread's histogram bins (descending order) and its first batch of 16-bit
   // keys (indices clamped to the row's capacity; slots at or past the length
-  // are masked where the keys are used).
+  // are masked where the keys are used).  Rows of a multiple of 8 keys start
+  // on 16-byte boundaries (the workspace is 256-byte aligned) and are read as
+  // 16-byte words of 8 keys, kSelWords per thread per round; other rows are
+  // read key by key, kSelBatch per thread per round.
+  const bool vec = (a.max_len & 7) == 0;
   uint32_t c4[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) c4[i] = gh[kHistBins - 1 - (tid * 4 + i)];
+  const u32x4_t* w16 = reinterpret_cast<const u32x4_t*>(k16);
+  u32x4_t kw[kSelWords];
   uint32_t kv[kSelBatch];
+  if (vec) {
 #pragma unroll
-  for (int k = 0; k < kSelBatch; ++k) kv[k] = k16[min(k * nt + tid, a.max_len - 1)];
+    for (int k = 0; k < kSelWords; ++k) kw[k] = w16[min(k * nt + tid, (a.max_len >> 3) - 1)];
+  } else {
+#pragma unroll
+    for (int k = 0; k < kSelBatch; ++k) kv[k] = k16[min(k * nt + tid, a.max_len - 1)];
+  }
   const int L = a.kv_len[b];
 
   if (K >= L) {
@@ -282,10 +294,64 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(TopkArgs a) {
   int need = K - (int)s_above;                           // 1..count(bstar)
 
   // (b) one pass over the 16-bit keys (a quarter of the score bytes; one
-  //     workgroup streams them all), kSelBatch per thread in flight: keys
-  //     above the boundary bin set their selection bit (a wave's ballot
-  //     covers 64 consecutive keys), keys in it join the candidate list
-  for (int j0 = 0; j0 < L; j0 += nt * kSelBatch) {
+  //     workgroup streams them all): keys above the boundary bin set their
+  //     selection bit, keys in it join the candidate list
+  if (vec) {
+    // thread: 8 consecutive keys per word, whose selection bits are one byte
+    // of the mask; every byte of the mask words below L is written (zero
+    // past L).  A wave scan of the per-thread candidate counts places them.
+    const int nw = (L + 7) >> 3;
+    const int nwm = use_mask ? ((L + 31) >> 5) * 4 : nw;
+    uint8_t* selb = reinterpret_cast<uint8_t*>(selmask);
+    for (int c0 = 0; c0 < nwm; c0 += nt * kSelWords) {
+      if (c0 > 0) {
+#pragma unroll
+        for (int k = 0; k < kSelWords; ++k) kw[k] = w16[min(c0 + k * nt + tid, nw - 1)];
+      }
+      uint32_t cmask[kSelWords];
+      uint32_t cnt = 0;
+#pragma unroll
+      for (int k = 0; k < kSelWords; ++k) {
+        const int c = c0 + k * nt + tid;
+        const uint32_t wd[4] = {kw[k][0], kw[k][1], kw[k][2], kw[k][3]};
+        uint32_t am = 0, cm = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = c * 8 + e;
+          const uint32_t cb = ((wd[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) >> 4;
+          am |= (uint32_t)(j < L && cb > bstar) << e;
+          cm |= (uint32_t)(j < L && cb == bstar) << e;
+        }
+        if (use_mask && c < nwm) selb[c] = (uint8_t)am;
+        cmask[k] = cm;
+        cnt += (uint32_t)__popc(cm);
+      }
+      uint32_t incl = cnt;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+      }
+      const uint32_t wtot = __shfl(incl, 63);
+      if (wtot) {
+        uint32_t wbase = 0;
+        if (lane == 0) wbase = atomicAdd(&s_ncand, wtot);
+        uint32_t pos = __shfl(wbase, 0) + incl - cnt;
+#pragma unroll
+        for (int k = 0; k < kSelWords; ++k) {
+          uint32_t cm = cmask[k];
+          const int c = c0 + k * nt + tid;
+          while (cm) {
+            const int e = __ffs(cm) - 1;
+            cm &= cm - 1;
+            if (pos < (uint32_t)kCandMax) cidx[pos] = c * 8 + e;
+            ++pos;
+          }
+        }
+      }
+    }
+  }
+  for (int j0 = 0; !vec && j0 < L; j0 += nt * kSelBatch) {
     // unconditional loads from clamped indices: a guarded load would be
     // compiled as a branch with its own wait, one round trip per key
     if (j0 > 0) {
