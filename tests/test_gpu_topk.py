@@ -32,6 +32,8 @@ def _ref(c, top_k):
     (3, 2, 4, 1, 64, (999, 300), W.F32, 0, 37),
     (4, 1, 28, 4, 128, (500,), W.BF16, 0, 1),
     (5, 2, 8, 2, 128, (120, 900), W.BF16, 0, 200),      # top_k > L for sequence 0
+    (6, 2, 8, 2, 128, (1024, 640), W.BF16, 0, 600),     # K near L: the cut sits in the low tail
+    (7, 3, 8, 2, 128, (4096, 33, 2051), W.BF16, 16, 32),  # 16-byte key rows, ragged lengths, paged
 ], ids=lambda c: f"s{c[0]}")
 def test_small_topk(cfg):
     seed, B, Hq, Hkv, d, L, dt, page, K = cfg
