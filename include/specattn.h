@@ -43,8 +43,9 @@
  *   i >= q_len[b] are padding and are written as O = 0, LSE = -inf.
  * - LSE is the natural-log log-sum-exp of the scaled scores, fp32
  *   [B, n_max, Hq]; pass NULL to skip it.
- * - Scores use the caller's `scale` (normally 1/sqrt(d)); Q and K are
- *   post-rotary.  Accumulation is fp32 for every input dtype.
+ * - Scores use the caller's `scale` (normally 1/sqrt(d)), which must be
+ *   finite and > 0 (else SPEC_ERR_SHAPE); Q and K are post-rotary.
+ *   Accumulation is fp32 for every input dtype.
  * - Contents of device index arrays (kv_len, q_len, text_idx, text_len,
  *   page_table, gamma) are preconditions: values outside the stated ranges
  *   are undefined behaviour, unless debug mode is on (spec_set_debug, or

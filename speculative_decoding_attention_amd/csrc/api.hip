@@ -42,7 +42,9 @@ spec_status_t check_common(const spec_kv_t* kv, int32_t batch, const void* q, in
   if (num_q_heads % kv->num_kv_heads != 0) return SPEC_ERR_SHAPE;
   if (q_dtype != kv->dtype) return SPEC_ERR_DTYPE;
   if (out_dtype != SPEC_F32 && out_dtype != SPEC_BF16) return SPEC_ERR_DTYPE;
-  if (!isfinite(scale)) return SPEC_ERR_SHAPE;
+  // the kernels take the masked keys' -inf and the running maxima as the
+  // small and large ends of the scaled scores, which holds for scale > 0 only
+  if (!(scale > 0.f) || !isfinite(scale)) return SPEC_ERR_SHAPE;
   if ((long long)n_max * (num_q_heads / kv->num_kv_heads) > 64) return SPEC_ERR_UNSUPPORTED;
   if ((long long)batch * kv->num_kv_heads > (1 << 24)) return SPEC_ERR_SHAPE;
   // contiguous caches address rows with 32-bit indices
@@ -252,7 +254,7 @@ spec_status_t spec_std_select(const spec_kv_t* kv, int32_t batch, const void* q_
   if (keep_idx && !keep_len) return SPEC_ERR_NULL;
   if (batch < 1 || num_q_heads < 1 || num_q_heads % kv->num_kv_heads) return SPEC_ERR_SHAPE;
   if (q_dtype != kv->dtype) return SPEC_ERR_DTYPE;
-  if (!isfinite(scale) || t_max < 1 || top_k < 1) return SPEC_ERR_SHAPE;
+  if (!(scale > 0.f) || !isfinite(scale) || t_max < 1 || top_k < 1) return SPEC_ERR_SHAPE;
   const int G = num_q_heads / kv->num_kv_heads;
   if ((long long)t_max * G > (1 << 20)) return SPEC_ERR_UNSUPPORTED;
   if ((long long)batch * kv->num_kv_heads * kv->max_len > (1LL << 31)) return SPEC_ERR_SHAPE;

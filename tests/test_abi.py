@@ -86,6 +86,9 @@ def test_verify_rejects_bad_args(L):
     assert _verify(L, kv, out_dtype=5) == 3
     assert _verify(L, kv, n_max=10) == 5              # 10 * 7 rows > 64
     assert _verify(L, kv, scale=float("nan")) == 2
+    assert _verify(L, kv, scale=float("inf")) == 2
+    assert _verify(L, kv, scale=0.0) == 2             # the kernels need scale > 0
+    assert _verify(L, kv, scale=-1.0) == 2
     need = L.spec_verify_attn_workspace(ctypes.byref(kv), 1, 6, 28)
     assert need > 0
     assert _verify(L, kv, ws=None, ws_bytes=0) == 1
@@ -159,6 +162,15 @@ def test_std_and_sparse_rejections(L):
                              None, None, None, None, 0, None) == 3      # q dtype != kv dtype
     assert L.spec_std_select(ctypes.byref(kv), 1, FAKE, 1, 28, FAKE, FAKE, 0, 4, 0.1, FAKE,
                              None, None, None, None, 0, None) == 2
+    for bad in (0.0, -1.0):                             # scale must be > 0
+        assert L.spec_std_select(ctypes.byref(kv), 1, FAKE, 1, 28, FAKE, FAKE, 8, 4, bad, FAKE,
+                                 None, None, None, None, 0, None) == 2
+        assert L.spec_vata_attn(ctypes.byref(kv), 1, FAKE, 1, 1, None, 28, FAKE, FAKE, 512, bad,
+                                FAKE, 1, None, None, 0, None) == 2
+        assert L.spec_topk_attn(ctypes.byref(kv), 1, FAKE, 1, 28, 16, bad, FAKE, FAKE, 1, None,
+                                None, 0, None) == 2
+        assert L.spec_sparse_attn(ctypes.byref(kv), 1, FAKE, 1, 1, None, 28, FAKE, FAKE, 16,
+                                  None, 0, bad, FAKE, 1, None, None, 0, None) == 2
     assert L.spec_std_select(ctypes.byref(kv), 1, FAKE, 1, 28, FAKE, FAKE, 8, 0, 0.1, FAKE,
                              None, None, None, None, 0, None) == 2
     assert L.spec_std_select(ctypes.byref(kv), 1, FAKE, 1, 27, FAKE, FAKE, 8, 4, 0.1, FAKE,
