@@ -50,7 +50,7 @@ def _parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--only", choices=["verify", "vata", "hsr", "topk", "accept", "step", "c5",
-                                       "std", "verify_b16", "c3", "c4"],
+                                       "std", "verify_b16", "c3", "c4", "lvis"],
                     default=None, help="time one part only (for counter passes)")
     return ap.parse_args()
 
@@ -80,6 +80,68 @@ def io_model(alpha, gamma, draft_us, verify_us, dense_us, draft_bytes, verify_by
             "attn_us_per_token": round((gamma * draft_us + verify_us) / e, 3),
             "dense_attn_us_per_token": round(dense_us, 3),
             "attn_speedup": round(dense_us * e / (gamma * draft_us + verify_us), 3)}
+
+
+def cpu_verify_baseline(oracle, attn, Hkv, scale, call_bytes, seconds):
+    """Times the oracle on whole verification calls for about `seconds`: the
+    (sequence, KV head) units of several calls at once go to a thread pool as
+    wide as the CPUs this process may use, with BLAS pinned to one thread per
+    worker (numpy releases the GIL inside its kernels).  Returns the
+    cpu_baseline object (throughput over every call finished)."""
+    import concurrent.futures as cf
+    host = len(os.sched_getaffinity(0))
+    units = [(b, g) for b in range(attn.q.shape[0]) for g in range(Hkv)]
+    per_round = max(1, host // len(units))          # calls in flight together
+    threads = min(host, per_round * len(units))
+    try:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(limits=1)
+    except Exception:
+        limit = None
+
+    q, k, v = attn.q.values, attn.k.values, attn.v.values     # inputs widened once
+
+    def one(u):
+        oracle.verify_attention(q, k, v, attn.kv_len, attn.q_len, Hkv, scale, units=[u])
+
+    t_start = time.perf_counter()
+    calls = 0
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        while True:
+            list(ex.map(one, units * per_round))
+            calls += per_round
+            if time.perf_counter() - t_start >= seconds:
+                break
+    secs = (time.perf_counter() - t_start) / calls
+    if limit is not None:
+        limit.restore_original_limits()
+    return {"value": round(call_bytes / secs / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "host_cores": host, "blas_threads_per_worker": 1, "kind": "oracle",
+            "sample": f"{calls} full verification calls of this workload ({len(units)} "
+                      f"(sequence, KV head) units x 42 rows x 25,512 keys each, fp64 numpy), "
+                      f"{per_round} in flight at a time on {threads} pool threads; "
+                      f"{secs:.3f} s per call"}
+
+
+def break_even_alpha(gamma, draft_us, verify_us, dense_us):
+    """Smallest acceptance rate at which a round of gamma draft steps and one
+    verification costs no more attention time per token than plain decoding:
+    dense_us * expected_tokens(alpha, gamma) = gamma * draft_us + verify_us.
+    expected_tokens rises from 1 (alpha = 0) to gamma + 1 (alpha = 1), so the
+    root is found by bisection; None when even alpha = 1 does not pay."""
+    need = (gamma * draft_us + verify_us) / dense_us
+    if need <= 1.0:
+        return 0.0
+    if need > gamma + 1:
+        return None
+    lo, hi = 0.0, 1.0
+    for _ in range(60):
+        mid = 0.5 * (lo + hi)
+        if expected_tokens(mid, gamma) < need:
+            lo = mid
+        else:
+            hi = mid
+    return round(hi, 4)
 
 
 def _source_hash(names):
@@ -289,6 +351,49 @@ def main():
               "accept_us": round(acc_c5_us, 2),
               "accept_gbs": round(acc_c5_bytes / (acc_c5_us * 1e-6) / 1e9, 1)}
 
+    # ---- the draft step as the video grows: text-anchored attention (one
+    # row, 512 text positions in the same layout) and the draft step (HSR row
+    # + VATA) at 500, 5,000 and 25,000 visual tokens, against dense one-row
+    # decoding over the whole cache, the cost the text anchoring avoids.
+    # Enough cache copies rotate that 520 MB stream per pass over them.
+    sweep = None
+    if only in (None, "lvis"):
+        sweep = []
+        for lv in (500, 5000, 25000):
+            Lw = lv + 512
+            copy_bytes = 2 * Hkv * Lw * d * 2
+            Rw = max(R, -(-520_000_000 // copy_bytes))
+            lw_len = torch.full((1,), Lw, dtype=torch.int32, device=dev)
+            kvw = [S.KVCache(torch.randn(1, Hkv, Lw, d, device=dev).mul_(0.5).to(torch.bfloat16),
+                             torch.randn(1, Hkv, Lw, d, device=dev).mul_(0.5).to(torch.bfloat16),
+                             lw_len) for _ in range(Rw)]
+            tiw = torch.tensor(W.c2_text_layout(lv, 512)[None, :], dtype=torch.int32,
+                               device=dev)
+            tlw = torch.full((1,), 512, dtype=torch.int32, device=dev)
+            ow = torch.empty((1, 1, Hq, d), dtype=torch.bfloat16, device=dev)
+            lw = torch.empty((1, 1, Hq), dtype=torch.float32, device=dev)
+            ws_w = {k_: S.Workspace(dev) for k_ in ("vata", "dense")}
+
+            def vata_w(j):
+                S.spec_vata_attn(kvw[j], y_hsr[:1].view(1, 1, Hq, d), tiw, tlw, scale=scale,
+                                 out=ow, lse=lw, workspace=ws_w["vata"])
+
+            def dense_w(j):
+                S.spec_verify_attn(kvw[j], q_last, scale=scale, out=ow, lse=lw,
+                                   workspace=ws_w["dense"])
+            for j in range(Rw):
+                vata_w(j), dense_w(j)
+            torch.cuda.synchronize()
+            t_v = time_graph(capture(lambda: [vata_w(j) for j in range(Rw)]), 4) * 1e3 / Rw
+            t_s = time_graph(capture(lambda: [(call_hsr(j % R, 0), vata_w(j))
+                                              for j in range(Rw)]), 4) * 1e3 / Rw
+            t_d = time_graph(capture(lambda: [dense_w(j) for j in range(Rw)]), 4) * 1e3 / Rw
+            sweep.append({"visual_tokens": lv, "kv_len": Lw, "copies": Rw,
+                          "vata_us": round(t_v, 3), "draft_step_us": round(t_s, 3),
+                          "draft_steps_per_s": round(1e6 / t_s, 1),
+                          "dense_decode_us": round(t_d, 3)})
+            del kvw
+
     # ---- Sparse-to-Dense at the same shape: the prefill selection of one
     # layer (512 text queries x 28 heads over 25,512 positions, K = 2048) and
     # the sparse draft step over the kept lists plus 64 decoded positions.
@@ -299,46 +404,55 @@ def main():
         qt = to_dev(cs.q_text)
         ti_s = torch.tensor(cs.text_idx, dtype=torch.int32, device=dev)
         tl_s = torch.tensor(cs.text_len, dtype=torch.int32, device=dev)
-        sel_s = torch.empty((B, Hkv, cs.top_k), dtype=torch.int32, device=dev)
-        keep_s = torch.empty((B, Hkv, cs.top_k + cs.t_max), dtype=torch.int32, device=dev)
-        klen_s = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
         ws_std = S.Workspace(dev)
-
-        def call_select():
-            S.spec_std_select(kv_s, qt, ti_s, tl_s, cs.top_k, scale=scale, sel_idx=sel_s,
-                              keep_idx=keep_s, keep_len=klen_s, workspace=ws_std)
-        call_select()
-        torch.cuda.synchronize()
-        g = capture(call_select)
-        select_us = time_graph(g, max(4, args.reps // 4)) * 1e3
-        tail = 64
-        t0_s = torch.full((B,), L - tail, dtype=torch.int32, device=dev)
-        keep_tail = keep_s.clone()
-        # the kept positions at or past the tail start are the tail's own
-        keep_tail[keep_tail >= L - tail] = -1
-        klen_tail = (keep_tail >= 0).sum(dim=2).to(torch.int32)
-        keep_tail = torch.sort(torch.where(keep_tail < 0, torch.full_like(keep_tail, 1 << 30),
-                                           keep_tail), dim=2).values
-        keep_tail = torch.where(keep_tail == (1 << 30), torch.full_like(keep_tail, -1),
-                                keep_tail).contiguous()
+        ws_sp = S.Workspace(dev)
         o_sp = torch.empty((B, 1, Hq, d), dtype=torch.bfloat16, device=dev)
         l_sp = torch.empty((B, 1, Hq), dtype=torch.float32, device=dev)
-        ws_sp = S.Workspace(dev)
+        tail = 64
+        t0_s = torch.full((B,), L - tail, dtype=torch.int32, device=dev)
 
-        def call_sparse(r):
-            S.spec_sparse_attn(kvs[r], q_last, keep_tail, klen_tail, tail_start=t0_s,
-                               tail_max=tail, scale=scale, out=o_sp, lse=l_sp, workspace=ws_sp)
-        for r in range(R):
-            call_sparse(r)
-        torch.cuda.synchronize()
-        g = capture(lambda: [call_sparse(r) for r in range(R)])
-        sparse_us = time_graph(g, args.reps) * 1e3 / R
+        def select_and_sparse(kk):
+            """Prefill selection with K = kk, then the sparse draft step over
+            the kept lists plus the last `tail` positions; returns the two
+            times (us), the kept positions per KV head and the step's bytes."""
+            sel_s = torch.empty((B, Hkv, kk), dtype=torch.int32, device=dev)
+            keep_s = torch.empty((B, Hkv, kk + cs.t_max), dtype=torch.int32, device=dev)
+            klen_s = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+
+            def call_select():
+                S.spec_std_select(kv_s, qt, ti_s, tl_s, kk, scale=scale, sel_idx=sel_s,
+                                  keep_idx=keep_s, keep_len=klen_s, workspace=ws_std)
+            call_select()
+            torch.cuda.synchronize()
+            sel_t = time_graph(capture(call_select), max(4, args.reps // 4)) * 1e3
+            keep_tail = keep_s.clone()
+            # the kept positions at or past the tail start are the tail's own
+            keep_tail[keep_tail >= L - tail] = -1
+            klen_tail = (keep_tail >= 0).sum(dim=2).to(torch.int32)
+            keep_tail = torch.sort(torch.where(keep_tail < 0, torch.full_like(keep_tail, 1 << 30),
+                                               keep_tail), dim=2).values
+            keep_tail = torch.where(keep_tail == (1 << 30), torch.full_like(keep_tail, -1),
+                                    keep_tail).contiguous()
+
+            def call_sparse(r):
+                S.spec_sparse_attn(kvs[r], q_last, keep_tail, klen_tail, tail_start=t0_s,
+                                   tail_max=tail, scale=scale, out=o_sp, lse=l_sp,
+                                   workspace=ws_sp)
+            for r in range(R):
+                call_sparse(r)
+            torch.cuda.synchronize()
+            sp_t = time_graph(capture(lambda: [call_sparse(r) for r in range(R)]),
+                              args.reps) * 1e3 / R
+            kept_ = int(klen_tail.sum().item()) + Hkv * tail
+            bytes_ = 2 * kept_ * d * 2 + kept_ * 4 + 2 * Hq * d * 2 + Hq * 4
+            return sel_t, sp_t, kept_, bytes_
+
+        per_k = {kk: select_and_sparse(kk) for kk in (512, 1024, 2048, 4096)}
+        select_us, sparse_us, kept, sparse_bytes = per_k[cs.top_k]
         # work of the selection: both passes form every visible score
         pos = cs.text_idx[0, :cs.text_len[0]].astype(np.int64)
         visible = int((pos + 1).sum()) * Hq          # (row, key) pairs over all heads
         sel_flops = 2 * 2 * d * visible
-        kept = int(klen_tail.sum().item()) + Hkv * tail
-        sparse_bytes = 2 * kept * d * 2 + kept * 4 + 2 * Hq * d * 2 + Hq * 4
         # dense verification at gamma + 1 rows (and plain one-token decode)
         ver_us = {}
         for nr in (1, 4, 6, 9):
@@ -355,6 +469,25 @@ def main():
         model = [io_model(al, gm, sparse_us, ver_us[gm + 1], ver_us[1], sparse_bytes,
                           kvb + 2 * (gm + 1) * Hq * d * 2, kvb + 2 * Hq * d * 2)
                  for gm in (3, 5, 8) for al in (0.5, 0.7, 0.9)]
+        # the same model as the retained fraction K/L changes: measured
+        # selection and sparse-step times per K, the per-token attention time
+        # at gamma = 5, and the acceptance rate at which a round breaks even
+        # with plain decoding (time, and KV bytes read)
+        kl_rows = []
+        for kk, (st_, sp_, kept_, by_) in per_k.items():
+            be_t = {str(gm): break_even_alpha(gm, sp_, ver_us[gm + 1], ver_us[1])
+                    for gm in (3, 5, 8)}
+            be_b = {str(gm): break_even_alpha(gm, by_, kvb + 2 * (gm + 1) * Hq * d * 2,
+                                              kvb + 2 * Hq * d * 2) for gm in (3, 5, 8)}
+            kl_rows.append({
+                "top_k": kk, "kept_per_head": round(kept_ / Hkv, 1),
+                "kept_fraction": round(kept_ / (Hkv * L), 4),
+                "select_us": round(st_, 2), "sparse_us": round(sp_, 3),
+                "sparse_bytes": by_,
+                "break_even_alpha_time": be_t, "break_even_alpha_bytes": be_b,
+                "gamma5": [io_model(al, 5, sp_, ver_us[6], ver_us[1], by_,
+                                    kvb + 2 * 6 * Hq * d * 2, kvb + 2 * Hq * d * 2)
+                           for al in (0.5, 0.7, 0.9)]})
         std = {"workload": "std-prefill-select-25k", "select_us": round(select_us, 2),
                "select_tflops": round(sel_flops / (select_us * 1e-6) / 1e12, 1),
                "select_mfma_frac": round(sel_flops / (select_us * 1e-6) / 1e12 /
@@ -367,7 +500,8 @@ def main():
                "verify_us_by_rows": {str(k): round(v, 2) for k, v in ver_us.items()},
                "io_model": {"assumption": "each draft token accepted independently with "
                                           "probability alpha; attention of one layer only",
-                            "rows": model}}
+                            "rows": model},
+               "io_model_by_top_k": kl_rows}
         sel_tfs = sel_flops / (select_us * 1e-6) / 1e12
         std["roofline"] = {"bound": "mfma", "achieved": round(sel_tfs, 1),
                            "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
@@ -522,38 +656,34 @@ def main():
     topk_bytes = L * Hkv * d * 2 + 2 * top_k * Hkv * d * 2 + Hq * d * 4 + Hkv * top_k * 4
     accept_bytes = n * V * 2 + gamma * 4 + (n + 2) * 4
 
-    # ---- parity of the timed outputs (sampled units of the verification)
+    # ---- parity of the timed outputs: every (sequence, KV head) unit of the
+    # verification call against the oracle, with the tests' bf16 bounds
     import oracle
     torch.cuda.synchronize()
     call_verify(0)
     torch.cuda.synchronize()
     ro, rl = oracle.verify_attention(attn.q.values, attn.k.values, attn.v.values, attn.kv_len,
-                                     attn.q_len, Hkv, scale, units=[(0, 0), (0, 3)])
+                                     attn.q_len, Hkv, scale)
     o = o_ver.float().cpu().numpy()
-    err = float(max(np.abs(o[0, :, g * 7:(g + 1) * 7] - ro[0, :, g * 7:(g + 1) * 7]).max()
-                    for g in (0, 3)))
+    lo = l_ver.cpu().numpy()
+    err = float(np.abs(o - ro).max())
+    G = Hq // Hkv
+    for g in range(Hkv):
+        hs = slice(g * G, (g + 1) * G)
+        eg = float(np.abs(o[:, :, hs] - ro[:, :, hs]).max())
+        if eg > 2e-2 or eg > 1e-2 * float(np.abs(ro[:, :, hs]).max()) + 1e-7 or \
+                float(np.abs(lo[:, :, hs] - rl[:, :, hs]).max()) > 1e-3:
+            print(f"bench: verification output of KV head {g} differs from the oracle "
+                  f"(max abs err {eg})", file=sys.stderr)
+            sys.exit(1)
 
-    # ---- CPU baseline: the oracle as it stands, on the host cores
+    # ---- CPU baseline: the oracle as it stands, on the host cores.  The
+    # call's (sequence, KV head) units run on a thread pool as wide as the
+    # CPUs this process may use, with BLAS pinned to one thread per worker
+    # (numpy releases the GIL inside its kernels).
     cpu = None
     if not args.no_cpu_baseline and only is None:
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
-        except Exception:
-            threads = 1
-        t_start = time.perf_counter()
-        calls = 0
-        while True:
-            oracle.verify_attention(attn.q.values, attn.k.values, attn.v.values, attn.kv_len,
-                                    attn.q_len, Hkv, scale)
-            calls += 1
-            if time.perf_counter() - t_start >= args.cpu_seconds:
-                break
-        secs = (time.perf_counter() - t_start) / calls
-        cpu = {"value": round(verify_bytes / secs / 1e9, 4), "unit": "GB/s", "cores": threads,
-               "kind": "oracle",
-               "sample": f"{calls} full verification call(s) of this workload (4 KV heads x 42 "
-                         f"rows x 25,512 keys, fp64 numpy), {secs:.2f} s each"}
+        cpu = cpu_verify_baseline(oracle, attn, Hkv, scale, verify_bytes, args.cpu_seconds)
 
     traffic = None
     src_hash = _source_hash(KERNEL_SOURCES)
@@ -598,6 +728,7 @@ def main():
         "hsr_tflops": round(hsr_flops / (parts["hsr_us"] * 1e-6) / 1e12, 2)
         if "hsr_us" in parts else None,
         "batched_draft": c5,
+        "draft_by_visual_tokens": sweep,
         "std": std,
         "verify_batch16": vb16,
         "ragged_paged": c3,

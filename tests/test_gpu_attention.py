@@ -197,6 +197,28 @@ def test_first_verify_row_equals_decode_on_device():
     assert (l[:, 0] - ld[:, 0]).abs().max().item() < 1e-4
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_every_verify_row_equals_decode_fp32(d):
+    """fp32 inputs: verification row i equals a one-row decode over the
+    prefix it sees (kv_len = L - n + i + 1) within 1e-5, for every row i.
+    fp32 probabilities are not rounded, so the two tilings differ only in
+    summation order."""
+    S = _lib()
+    from speculative_decoding_attention_amd import KVCache
+    n = 6
+    c = W.small_attn(18 + d, 2, 8, 2, d, n, (2222, 1111), W.F32)
+    kv = kvcache(c)
+    q = dev(c.q)
+    o, l = S.spec_verify_attn(kv, q, scale=c.scale, out_dtype=torch.float32)
+    for i in range(n):
+        kvd = KVCache(kv.k, kv.v, dev((c.kv_len - n + i + 1).astype(np.int32)))
+        od, ld = S.spec_verify_attn(kvd, q[:, i:i + 1].contiguous(), scale=c.scale,
+                                    out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert (o[:, i] - od[:, 0]).abs().max().item() <= 1e-5, f"row {i}"
+        assert (l[:, i] - ld[:, 0]).abs().max().item() <= 1e-5, f"row {i} lse"
+
+
 def test_paged_equals_contiguous_on_device():
     S = _lib()
     c = W.small_attn(16, 2, 28, 4, 128, 6, (1700, 2600), W.BF16, page_size=16)
@@ -292,24 +314,12 @@ def test_c3_vata_full(c3):
     assert_attention_close(out, lse, ro, rl, c3.q_len, W.BF16, "c3 vata")
 
 
-def test_c4_verify_sampled():
-    """Dense verification at L = 32768, B = 4: every output of two sampled
+def test_c4_verify_full():
+    """Dense verification at L = 32768, B = 4: every output of all 16
     (sequence, KV head) units against the oracle."""
-    S = _lib()
     c = W.c4_topk(0)
-    out, lse = S.spec_verify_attn(kvcache(c), dev(c.q), q_len=dev(c.q_len), scale=c.scale,
-                                  out_dtype=torch.float32)
-    torch.cuda.synchronize()
-    units = [(0, 0), (3, 2)]
-    ro, rl = oracle.verify_attention(c.q.values, c.k.values, c.v.values, c.kv_len, c.q_len, 4,
-                                     c.scale, units=units)
-    o = out.cpu().numpy()
-    l = lse.cpu().numpy()
-    for b, g in units:
-        hs = slice(g * 7, g * 7 + 7)
-        err = np.abs(o[b, :, hs] - ro[b, :, hs]).max()
-        assert err <= 1e-2 * np.abs(ro[b, :, hs]).max() and err <= 2e-2
-        assert np.abs(l[b, :, hs] - rl[b, :, hs]).max() <= 1e-3
+    out, lse, ro, rl = _verify_pair(c)
+    assert_attention_close(out, lse, ro, rl, c.q_len, W.BF16, "c4 verify")
 
 
 def test_verify_and_vata_long_context():

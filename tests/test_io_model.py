@@ -31,3 +31,24 @@ def test_per_token_accounting():
     assert r["attn_speedup"] == pytest.approx(8.0 / 18.0, abs=1e-3)
     r = bench.io_model(1.0, 4, 2.0, 10.0, 8.0, 100, 1000, 900)
     assert r["tokens_per_round"] == 5.0 and r["kv_bytes_per_token"] == 280
+
+
+@pytest.mark.parametrize("gamma", [1, 3, 5, 8])
+def test_break_even_alpha_balances_the_round(gamma):
+    draft_us, verify_us, dense_us = 3.0, 12.0, 10.0
+    a = bench.break_even_alpha(gamma, draft_us, verify_us, dense_us)
+    need = (gamma * draft_us + verify_us) / dense_us
+    if need > gamma + 1:
+        assert a is None
+        return
+    assert dense_us * bench.expected_tokens(a, gamma) == pytest.approx(gamma * draft_us + verify_us,
+                                                                       rel=1e-3)
+    r = bench.io_model(a, gamma, draft_us, verify_us, dense_us, 1, 1, 1)
+    assert r["attn_speedup"] == pytest.approx(1.0, abs=2e-3)
+
+
+def test_break_even_alpha_limits():
+    assert bench.break_even_alpha(4, 1.0, 5.0, 20.0) == 0.0      # pays even with no acceptance
+    assert bench.break_even_alpha(2, 10.0, 10.0, 5.0) is None    # 30 us > 3 tokens x 5 us
+    # cheaper drafts (a smaller kept fraction) break even at a lower rate
+    assert bench.break_even_alpha(5, 2.0, 20.0, 19.0) < bench.break_even_alpha(5, 6.0, 20.0, 19.0)
