@@ -151,6 +151,30 @@ spec_status_t spec_verify_attn(const spec_kv_t* kv, int32_t batch, const void* q
                                float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * spec_verify_attn_noalloc -- spec_verify_attn for callers that cannot
+ * allocate device memory (code under HIP graph capture that may not call
+ * hipMalloc, tight serving loops, harnesses that forbid allocation).
+ *
+ * Same arguments, limits, results and errors as spec_verify_attn, without
+ * the workspace: the split partials live in the library's own scratch
+ * array, SPEC_NOALLOC_SCRATCH_BYTES per device, held from the library's
+ * load until the process ends.  The call allocates nothing (no hipMalloc,
+ * no allocating library routine); its first call on a device looks the
+ * array up once.  Returns SPEC_ERR_WORKSPACE, with nothing enqueued, when
+ * the shapes need more scratch than that (spec_verify_attn_workspace()
+ * reports the need; the 25k-visual-token step needs about 6.5 MB, 16
+ * sequences of 32,768 positions about 23 MB).
+ * Every call on one device shares that device's array: calls that may
+ * overlap on one device (different streams, or host threads without
+ * ordering) race and must be serialised by the caller.
+ */
+#define SPEC_NOALLOC_SCRATCH_BYTES (32u << 20)
+spec_status_t spec_verify_attn_noalloc(const spec_kv_t* kv, int32_t batch, const void* q,
+                                       int32_t q_dtype, int32_t n_max, const int32_t* q_len,
+                                       int32_t num_q_heads, float scale, void* out,
+                                       int32_t out_dtype, float* lse, hipStream_t stream);
+
+/*
  * spec_vata_attn -- text-anchored draft attention (Sparrow, technical summary
  * 3.1 / 3.A: the draft drops the visual KV cache and attends only to
  * text-anchored positions, so its cost scales with the text length).

@@ -19,6 +19,7 @@ SPEC_F32 = 0
 SPEC_BF16 = 1
 SPEC_ABI_VERSION = 3
 SPEC_WS_SYNC_BYTES = 1 << 20
+SPEC_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 STATUS = {
     0: "SPEC_OK", 1: "SPEC_ERR_NULL", 2: "SPEC_ERR_SHAPE", 3: "SPEC_ERR_DTYPE",
@@ -45,6 +46,7 @@ _KVP = ctypes.POINTER(SpecKV)
 SIGNATURES = {
     "spec_verify_attn_workspace": (_S, [_KVP, _I, _I, _I]),
     "spec_verify_attn": (_I, [_KVP, _I, _P, _I, _I, _P, _I, _F, _P, _I, _P, _P, _S, _P]),
+    "spec_verify_attn_noalloc": (_I, [_KVP, _I, _P, _I, _I, _P, _I, _F, _P, _I, _P, _P]),
     "spec_vata_attn_workspace": (_S, [_KVP, _I, _I, _I, _I]),
     "spec_vata_attn": (_I, [_KVP, _I, _P, _I, _I, _P, _I, _P, _P, _I, _F, _P, _I, _P, _P, _S, _P]),
     "spec_topk_attn_workspace": (_S, [_KVP, _I, _I, _I]),
@@ -235,6 +237,33 @@ def spec_verify_attn(kv: KVCache, q: torch.Tensor, q_len: Optional[torch.Tensor]
                             _ptr(q_len), Hq, scale, _ptr(out), _dtype_code(out.dtype), _ptr(lse),
                             wsp, wsn, _stream(q.device))
     _check("spec_verify_attn", st)
+    return out, lse
+
+
+def spec_verify_attn_noalloc(kv: KVCache, q: torch.Tensor, out: torch.Tensor,
+                             lse: Optional[torch.Tensor] = None,
+                             q_len: Optional[torch.Tensor] = None,
+                             scale: Optional[float] = None):
+    """Dense verification attention into caller-provided `out` (and `lse`)
+    with no device allocation: the library's own scratch holds the split
+    partials.  Returns (out, lse)."""
+    L = lib()
+    _dev(q, "q", kv.k.dtype)
+    _dev(out, "out")
+    B, n_max, Hq, d = q.shape
+    if tuple(out.shape) != (B, n_max, Hq, d):
+        raise ValueError("out must have the shape of q")
+    if lse is not None:
+        _dev(lse, "lse", torch.float32)
+        if tuple(lse.shape) != (B, n_max, Hq):
+            raise ValueError("lse must be [B, n_max, Hq]")
+    if q_len is not None:
+        _dev(q_len, "q_len", torch.int32)
+    scale = float(d ** -0.5) if scale is None else float(scale)
+    st = L.spec_verify_attn_noalloc(ctypes.byref(kv.struct), B, _ptr(q), _dtype_code(q.dtype),
+                                    n_max, _ptr(q_len), Hq, scale, _ptr(out),
+                                    _dtype_code(out.dtype), _ptr(lse), _stream(q.device))
+    _check("spec_verify_attn_noalloc", st)
     return out, lse
 
 

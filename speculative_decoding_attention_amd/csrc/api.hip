@@ -4,11 +4,38 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "internal.h"
 
 using namespace spec;
 
+// Scratch of spec_verify_attn_noalloc: the split partials of callers that
+// cannot allocate device memory.  One copy per device, held from module load
+// until the process ends; every call on a device reuses it.  No word of it
+// needs to start at zero (each partial is written before it is read), so
+// nothing is cleared.  In host code the name stands for a host-side shadow,
+// never a device address: host code reaches the memory only through the
+// per-device pointer that noalloc_scratch() obtains.
+static __device__ __align__(256) unsigned char scratch[SPEC_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+// This device's copy of `scratch`, looked up once per device (with that
+// device current) under a lock; nullptr if the runtime cannot resolve it.
+void* noalloc_scratch() {
+  static std::mutex mu;
+  static void* ptr[64] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    ptr[dev] = p;
+  }
+  return ptr[dev];
+}
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
@@ -151,6 +178,25 @@ spec_status_t spec_verify_attn(const spec_kv_t* kv, int32_t batch, const void* q
                                        kv->page_size != 0, kSyncBytes, a.page_shift);
   st = check_ws(plan.ws_bytes, ws, ws_bytes);
   if (st != SPEC_OK) return st;
+  if (debug_enabled() && (st = validate(kv_checks(kv, batch, q_len, n_max), stream)) != SPEC_OK)
+    return st;
+  return launch_attention(a, kv->head_dim, kv->dtype, plan, ws, stream);
+}
+
+spec_status_t spec_verify_attn_noalloc(const spec_kv_t* kv, int32_t batch, const void* q,
+                                       int32_t q_dtype, int32_t n_max, const int32_t* q_len,
+                                       int32_t num_q_heads, float scale, void* out,
+                                       int32_t out_dtype, float* lse, hipStream_t stream) {
+  spec_status_t st =
+      check_common(kv, batch, q, q_dtype, n_max, num_q_heads, scale, out, out_dtype);
+  if (st != SPEC_OK) return st;
+  AttnArgs a = make_args(kv, batch, q, n_max, q_len, num_q_heads, scale, out, out_dtype, lse);
+  a.mode = 0;
+  const AttnPlan plan = plan_attention(batch * kv->num_kv_heads, kv->max_len, a.R, kv->head_dim,
+                                       kv->page_size != 0, kSyncBytes, a.page_shift);
+  if (plan.ws_bytes > SPEC_NOALLOC_SCRATCH_BYTES) return SPEC_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (plan.ws_bytes > 0 && !(ws = noalloc_scratch())) return SPEC_ERR_HIP;
   if (debug_enabled() && (st = validate(kv_checks(kv, batch, q_len, n_max), stream)) != SPEC_OK)
     return st;
   return launch_attention(a, kv->head_dim, kv->dtype, plan, ws, stream);

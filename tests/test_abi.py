@@ -96,6 +96,28 @@ def test_verify_rejects_bad_args(L):
     assert _verify(L, kv, ws=FAKE + 128, ws_bytes=need) == 4   # not 256-byte aligned
 
 
+def test_verify_noalloc_rejects_before_touching_the_device(L):
+    """The allocation-free verification checks its arguments as spec_verify_attn
+    does, and refuses shapes whose split partials exceed its fixed scratch
+    (SPEC_ERR_WORKSPACE), all before any device call."""
+    from speculative_decoding_attention_amd import _binding
+    kv = _kv()
+    call = lambda kv_, B=1, n_max=6, Hq=28, scale=0.088, q=FAKE: L.spec_verify_attn_noalloc(
+        ctypes.byref(kv_), B, q, 1, n_max, None, Hq, scale, FAKE, 1, None, None)
+    assert call(kv, q=None) == 1
+    assert call(kv, Hq=30) == 2
+    assert call(kv, scale=0.0) == 2
+    assert call(_kv(head_dim=96)) == 5
+    # 16 sequences x 32,768 positions with 64 rows per KV head need 33.75 MiB
+    big = _kv(max_len=32768)
+    need = L.spec_verify_attn_workspace(ctypes.byref(big), 16, 16, 16)
+    assert need > _binding.SPEC_NOALLOC_SCRATCH_BYTES
+    assert call(big, B=16, n_max=16, Hq=16) == 4
+    # the 25k-visual-token step fits
+    assert L.spec_verify_attn_workspace(ctypes.byref(_kv(max_len=25512)), 1, 6, 28) < \
+        _binding.SPEC_NOALLOC_SCRATCH_BYTES
+
+
 def test_vata_topk_rejections(L):
     kv = _kv()
     assert L.spec_vata_attn(ctypes.byref(kv), 1, FAKE, 1, 1, None, 28, None, FAKE, 512, 0.1, FAKE,
