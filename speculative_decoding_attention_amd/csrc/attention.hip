@@ -80,15 +80,15 @@ struct SlotMap {
 
 // Mode 3: first position of the tail (kv_len without a tail).
 __device__ __forceinline__ int tail_begin(const AttnArgs& a, int b, int L) {
-  return a.tail_start ? a.tail_start[b] : L - min(a.tail_window, L);
+  return a.tail_start ? ld_uniform(a.tail_start, b) : L - min(a.tail_window, L);
 }
 
 // Number of key slots of unit (b, g) (see AttnArgs::mode).
 __device__ __forceinline__ int unit_slots(const AttnArgs& a, int b, int g, int L) {
   if (a.mode == 0) return L;
-  if (a.mode == 1) return a.slot_len[b];
+  if (a.mode == 1) return ld_uniform(a.slot_len, b);
   if (a.mode == 2) return min(a.slot_stride, L);
-  return a.slot_len[b * a.Hkv + g] + max(0, L - tail_begin(a, b, L));
+  return ld_uniform(a.slot_len, b * a.Hkv + g) + max(0, L - tail_begin(a, b, L));
 }
 
 // The list entry of this thread's first slot, t_beg + threadIdx.x, requested
@@ -118,7 +118,7 @@ __device__ __forceinline__ void stage_slots(const AttnArgs& a, int b, int g, int
       row[pg - pg0] = (uint32_t)a.page_table[(size_t)b * a.max_pages + pg];
     return;
   }
-  const int n_list = (a.mode == 3) ? a.slot_len[u] : 0;
+  const int n_list = (a.mode == 3) ? ld_uniform(a.slot_len, (int)u) : 0;
   const int t0 = (a.mode == 3) ? tail_begin(a, b, L) : 0;
   const int first = t_beg + (int)threadIdx.x;
   // Every thread runs every round (t_beg and blockDim are multiples of 32),
@@ -457,8 +457,8 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
   const int u = wg / a.S, s = wg - u * a.S;
   const int b = u / a.Hkv, g = u - b * a.Hkv;
   const int pre = GATHER ? prefetch_slot(a, b, g, s * a.chunk) : 0;
-  const int L = a.kv_len[b];
-  const int nq = a.q_len ? a.q_len[b] : a.n_max;
+  const int L = ld_uniform(a.kv_len, b);
+  const int nq = a.q_len ? ld_uniform(a.q_len, b) : a.n_max;
   const int T = unit_slots(a, b, g, L);
   const int t_beg = s * a.chunk;
   const int t_end = min(T, t_beg + a.chunk);
@@ -537,7 +537,7 @@ __device__ __forceinline__ uint32_t swz(uint32_t r) { return ((r & 7u) << 1) ^ (
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 
-template <int NB>
+template <int NB, bool GATHER = false>
 struct PipeCfg {
   // NB >= 3: 8 waves in two teams; each team's waves own one 16-row block and
   // the teams take alternate 32-key sub-tiles, so every SIMD runs two waves.
@@ -548,19 +548,21 @@ struct PipeCfg {
   static constexpr int TILE_KEYS = 32 * KP;
   static constexpr int SUB_BYTES = 32 * 256;               // one sub-tile of K (or V)
   static constexpr int TILE_BYTES = KP * 2 * SUB_BYTES;
+  // 128 KiB of ring; gathered splits need the other 32 KiB for their slot
+  // tables.  (A five-stage 160 KiB ring for dense splits measured slower:
+  // the deeper first burst delays every split's first tile.)
   static constexpr int RING_BYTES = 128 * 1024;
   static constexpr int NS = RING_BYTES / TILE_BYTES;       // 4 or 2 stages
   static constexpr int INSTR = TILE_BYTES / 1024;          // 1 KB DMA instructions per tile
   static constexpr int PER_WAVE = INSTR / WAVES;
-  static_assert(NS >= 2 && NS - 2 <= 6, "ring depth");
-  static_assert(PER_WAVE * (NS - 2) <= 63, "vmcnt range");
+  static_assert(NS >= 2, "ring depth");
 };
 
 template <int NB, bool GATHER>
 __device__ __forceinline__ void pipe_issue_tile(const AttnArgs& a, const SlotMap<GATHER>& sm,
                                                 int tile_start, int t_end, uint32_t slot_lds,
                                                 int wave, int lane) {
-  using C = PipeCfg<NB>;
+  using C = PipeCfg<NB, GATHER>;
   const unsigned char* kg = reinterpret_cast<const unsigned char*>(a.k);
   const unsigned char* vg = reinterpret_cast<const unsigned char*>(a.v);
   // All source addresses first: a gathered row comes from LDS, and each DMA
@@ -731,12 +733,21 @@ __device__ __forceinline__ void pipe_issue_q(const AttnArgs& a, int b, int g, ui
 
 template <int NB, bool GATHER>
 __global__ __launch_bounds__(PipeCfg<NB>::WAVES * 64, 1) void attn_bf16_pipe_kernel(AttnArgs a) {
-  using C = PipeCfg<NB>;
+  using C = PipeCfg<NB, GATHER>;
   constexpr int D = 128;
   __shared__ __align__(16) unsigned char ring[C::RING_BYTES];
-  __shared__ int s_pos[GATHER ? kMaxChunk : 1];
-  __shared__ uint32_t s_row[GATHER ? kMaxChunk : 1];
-  __shared__ int s_bmax[GATHER ? kMaxChunk / 32 : 1];
+  // slot tables of gathered splits (a dense split has no LDS beside the ring)
+  int* s_pos = nullptr;
+  uint32_t* s_row = nullptr;
+  int* s_bmax = nullptr;
+  if constexpr (GATHER) {
+    __shared__ int g_pos[kMaxChunk];
+    __shared__ uint32_t g_row[kMaxChunk];
+    __shared__ int g_bmax[kMaxChunk / 32];
+    s_pos = g_pos;
+    s_row = g_row;
+    s_bmax = g_bmax;
+  }
   static_assert(((C::KP > 1) ? C::KP - 1 : 1) * (NB * 16) * (D + 4) * 4 + 7 * C::KP * NB * 16 * 4 <=
                     C::RING_BYTES,
                 "epilogue fits the ring");
@@ -759,8 +770,8 @@ __global__ __launch_bounds__(PipeCfg<NB>::WAVES * 64, 1) void attn_bf16_pipe_ker
   // The lengths are requested first (scalar loads, not queued behind the
   // DMA requests below); their values are waited for only where used.
   const int pre = GATHER ? prefetch_slot(a, b, g, t_beg) : 0;
-  const int L = a.kv_len[b];
-  const int nq = a.q_len ? a.q_len[b] : a.n_max;
+  const int L = ld_uniform(a.kv_len, b);
+  const int nq = a.q_len ? ld_uniform(a.q_len, b) : a.n_max;
   // Dense splits: the first NS - 1 tiles and the query block go out before
   // the sequence length is known, so their round trips overlap the length's.
   // Their slots are clamped to the split's end as planned over the cache
@@ -777,7 +788,7 @@ __global__ __launch_bounds__(PipeCfg<NB>::WAVES * 64, 1) void attn_bf16_pipe_ker
       pipe_issue_tile<NB, GATHER>(a, sm, t_beg + j * C::TILE_KEYS, spec_end,
                                   ring_lds + (uint32_t)(j * C::TILE_BYTES), wave, lane);
   }
-  const int T = unit_slots(a, b, g, L);
+  const int T = GATHER ? unit_slots(a, b, g, L) : L;   // a dense split is mode 0
   const int t_end = min(T, t_beg + a.chunk);
   const int n_tiles = t_end > t_beg ? (t_end - t_beg + C::TILE_KEYS - 1) / C::TILE_KEYS : 0;
   if (GATHER) {
@@ -820,9 +831,8 @@ __global__ __launch_bounds__(PipeCfg<NB>::WAVES * 64, 1) void attn_bf16_pipe_ker
   for (int db = 0; db < 8; ++db) acc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   for (int t = 0; t < n_tiles; ++t) {
-    const int later = min(C::NS - 2, n_tiles - 1 - t);
-    wait_tiles_barrier<C::PER_WAVE>(later);
     if (t == 0) {
+      wait_tiles_barrier<C::PER_WAVE, C::NS - 2>(n_tiles - 1);
       // the query block landed with (before) tile 0; every wave copies its
       // rows out before tile NS-1 reuses the slot
       if (valid) {
@@ -832,28 +842,62 @@ __global__ __launch_bounds__(PipeCfg<NB>::WAVES * 64, 1) void attn_bf16_pipe_ker
               ring + kQSlot + n * 256 + 16 * q4 + 64 * ks));
       }
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (C::NS - 1 < n_tiles)
+        pipe_issue_tile<NB, GATHER>(a, sm, t_beg + (C::NS - 1) * C::TILE_KEYS, t_end,
+                                    ring_lds + (uint32_t)((C::NS - 1) * C::TILE_BYTES), wave,
+                                    lane);
+    } else {
+      // Every wave is done with tile t-1, so its slot is refilled at once,
+      // before tile t is waited for: NS-1 tiles stay in flight while this
+      // tile is computed, whenever its data arrives.
+      asm volatile("s_barrier" ::: "memory");
+      if (t + C::NS - 1 < n_tiles)
+        pipe_issue_tile<NB, GATHER>(a, sm, t_beg + (t + C::NS - 1) * C::TILE_KEYS, t_end,
+                                    ring_lds +
+                                        (uint32_t)(((t + C::NS - 1) % C::NS) * C::TILE_BYTES),
+                                    wave, lane);
+      wait_tiles_barrier<C::PER_WAVE, C::NS - 1>(n_tiles - 1 - t);
     }
-    if (t + C::NS - 1 < n_tiles)
-      pipe_issue_tile<NB, GATHER>(a, sm, t_beg + (t + C::NS - 1) * C::TILE_KEYS, t_end,
-                                  ring_lds + (uint32_t)(((t + C::NS - 1) % C::NS) * C::TILE_BYTES),
-                                  wave, lane);
     if (!active) continue;
     const uint32_t kofs = (uint32_t)((t % C::NS) * C::TILE_BYTES + (2 * p) * C::SUB_BYTES);
     const uint32_t vofs = kofs + C::SUB_BYTES;
     const int sub0 = t_beg + t * C::TILE_KEYS + 32 * p;
 
+    // Every LDS read of the sub-tile is requested at once, so their latency
+    // is paid once per tile: the K fragments, then the transposed V
+    // fragments (they do not depend on the scores).  The V^T operand of lane
+    // (i, q4) for output block db is V[keys 4q4.. and 16+4q4..][d = 16*db+i].
+    u32x4_t kfr[2][4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const uint32_t row = 16 * kb + r16;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const uint32_t chunk = (uint32_t)(4 * ks + q4) ^ swz(row);
+        kfr[kb][ks] = *reinterpret_cast<const u32x4_t*>(ring + kofs + row * 256 + chunk * 16);
+      }
+    }
+    short4_t vlo[8], vhi[8];
+    {
+      const int sl = lane & 15;
+      const uint32_t r0 = (uint32_t)(4 * q4 + (sl >> 2)), r1 = r0 + 16;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const uint32_t chunk = (uint32_t)(2 * db + ((sl & 3) >> 1));
+        const uint32_t o0 = vofs + r0 * 256 + ((chunk ^ swz(r0)) * 16) + 8 * (sl & 1);
+        const uint32_t o1 = vofs + r1 * 256 + ((chunk ^ swz(r1)) * 16) + 8 * (sl & 1);
+        vlo[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(ring_l + o0));
+        vhi[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(ring_l + o1));
+      }
+    }
     // S^T = K Q^T for keys 16*kb + m of the sub-tile (unscaled scores)
     f32x4_t sc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const uint32_t row = 16 * kb + r16;
       f32x4_t c4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const uint32_t chunk = (uint32_t)(4 * ks + q4) ^ swz(row);
-        const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(ring + kofs + row * 256 + chunk * 16);
-        c4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv), qop[ks], c4, 0, 0, 0);
-      }
+      for (int ks = 0; ks < 4; ++ks)
+        c4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kfr[kb][ks]), qop[ks], c4, 0, 0, 0);
       sc[kb] = c4;
     }
     // causal / list / tail mask; a dense tile that lies entirely before the
@@ -916,17 +960,10 @@ __global__ __launch_bounds__(PipeCfg<NB>::WAVES * 64, 1) void attn_bf16_pipe_ker
     l_rnd += lr;
     const bf16x8_t pop = as_bf16x8(pk);
 
-    // O^T += V^T P^T: the V^T operand of lane (i, q4) is V[keys 4q4.. and
-    // 16+4q4..][d = 16*db + i], read transposed from LDS
-    const int sl = lane & 15;
-    const uint32_t r0 = (uint32_t)(4 * q4 + (sl >> 2)), r1 = r0 + 16;
+    // O^T += V^T P^T with the V^T fragments requested above
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      const uint32_t chunk = (uint32_t)(2 * db + ((sl & 3) >> 1));
-      const uint32_t o0 = vofs + r0 * 256 + ((chunk ^ swz(r0)) * 16) + 8 * (sl & 1);
-      const uint32_t o1 = vofs + r1 * 256 + ((chunk ^ swz(r1)) * 16) + 8 * (sl & 1);
-      const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(ring_l + o0));
-      const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(ring_l + o1));
+      const short4_t lo = vlo[db], hi = vhi[db];
       u32x4_t va;
       va[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
       va[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
@@ -963,8 +1000,8 @@ __global__ __launch_bounds__(256, 1) void attn_f32_kernel(AttnArgs a) {
   const int u = wg / a.S, s = wg - u * a.S;
   const int b = u / a.Hkv, g = u - b * a.Hkv;
   const int pre = GATHER ? prefetch_slot(a, b, g, s * a.chunk) : 0;
-  const int L = a.kv_len[b];
-  const int nq = a.q_len ? a.q_len[b] : a.n_max;
+  const int L = ld_uniform(a.kv_len, b);
+  const int nq = a.q_len ? ld_uniform(a.q_len, b) : a.n_max;
   const int T = unit_slots(a, b, g, L);
   const int t_beg = s * a.chunk;
   const int t_end = min(T, t_beg + a.chunk);
@@ -1165,7 +1202,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
     Ls = __builtin_fmaf(gstat[1][k], f, Ls);
     Lr = __builtin_fmaf(gstat[2][k], f, Lr);
   }
-  const int nq = a.q_len ? a.q_len[b] : a.n_max;
+  const int nq = a.q_len ? ld_uniform(a.q_len, b) : a.n_max;
   const bool live = (i < nq) && (Ls > 0.f);
   o = live ? o / Lr : 0.f;
   const size_t oi = (((size_t)b * a.n_max + i) * a.Hq + g * a.G + hh) * D + d;
@@ -1222,7 +1259,7 @@ __global__ __launch_bounds__(256) void attn_merge_small_kernel(AttnArgs a) {
     Ls = __builtin_fmaf(lv[j], w, Ls);
     Lr = __builtin_fmaf(rv[j], w, Lr);
   }
-  const int nq = a.q_len ? a.q_len[b] : a.n_max;
+  const int nq = a.q_len ? ld_uniform(a.q_len, b) : a.n_max;
   const bool live = (i < nq) && (Ls > 0.f);
   o = live ? o / Lr : 0.f;
   const size_t oi = (((size_t)b * a.n_max + i) * a.Hq + g * a.G + hh) * D + d;

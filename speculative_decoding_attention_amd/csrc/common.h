@@ -38,6 +38,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
+// A wave-uniform load through the scalar unit (s_load, waited on with
+// lgkmcnt).  A vector load's wait (vmcnt) retires in order, so waiting for a
+// length loaded after DMA requests would also wait for all of those; a
+// scalar load never does.  Only for data no kernel of the same launch writes
+// (lengths, list sizes).  The index must be uniform across the wave.
+__device__ __forceinline__ int ld_uniform(const int32_t* p, int i) {
+  typedef const int32_t __attribute__((address_space(4)))* cptr_t;
+  return ((cptr_t)p)[__builtin_amdgcn_readfirstlane(i)];
+}
+
 // 16-byte global load / store helpers.
 __device__ __forceinline__ u32x4_t ld16(const void* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
@@ -60,30 +70,6 @@ __device__ __forceinline__ float sum_across_rows(float x) {
   return x;
 }
 
-// Device-wide hand-off between workgroups without cache flushes.  Each XCD
-// has its own L2, so plain stores can sit in one XCD's L2 where another XCD
-// cannot see them, and a release fence writes back that whole L2 (costly:
-// tens of microseconds when every workgroup of a grid does it).  Instead the
-// data handed off is stored and loaded at agent scope: such stores write
-// through to the device-coherent level and complete (vmcnt) only once they
-// are visible there, and such loads bypass the non-coherent caches.  The
-// producer's waves wait for their own stores, meet at a workgroup barrier,
-// and only then does thread 0 signal with an agent-scope atomic; the
-// consumer reads the data only after it has seen the signal.
-__device__ __forceinline__ void st_agent(float* p, float v) {
-  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_agent(const float* p) {
-  return __uint_as_float(__hip_atomic_load(const_cast<uint32_t*>(reinterpret_cast<const uint32_t*>(p)),
-                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-}
-// Every wave's agent-scope stores have completed when this returns.
-__device__ __forceinline__ void block_stores_done() {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-}
-
 // ---------------------------------------------------------- LDS DMA ----
 typedef __attribute__((address_space(3))) unsigned char lds_u8_t;
 
@@ -103,16 +89,19 @@ __device__ __forceinline__ void wait_dma_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" :: "n"(N) : "memory");
 }
 
-template <int PER_WAVE>
+// Waits until at most `later` tile groups of PER_WAVE DMA loads each are
+// still outstanding for this wave (later clamped to [0, MAXL], so every
+// vmcnt immediate is known at compile time), then a workgroup barrier.
+template <int PER_WAVE, int MAXL>
 __device__ __forceinline__ void wait_tiles_barrier(int later_tiles) {
-  switch (later_tiles) {
-    case 0: wait_dma_barrier<0>(); break;
-    case 1: wait_dma_barrier<PER_WAVE * 1>(); break;
-    case 2: wait_dma_barrier<PER_WAVE * 2>(); break;
-    case 3: wait_dma_barrier<PER_WAVE * 3>(); break;
-    case 4: wait_dma_barrier<PER_WAVE * 4>(); break;
-    case 5: wait_dma_barrier<PER_WAVE * 5>(); break;
-    default: wait_dma_barrier<PER_WAVE * 6>(); break;
+  static_assert(PER_WAVE * MAXL <= 63, "vmcnt range");
+  if constexpr (MAXL <= 0) {
+    wait_dma_barrier<0>();
+  } else {
+    if (later_tiles >= MAXL)
+      wait_dma_barrier<PER_WAVE * MAXL>();
+    else
+      wait_tiles_barrier<PER_WAVE, MAXL - 1>(later_tiles);
   }
 }
 

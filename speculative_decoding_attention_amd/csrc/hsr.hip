@@ -125,7 +125,7 @@ __global__ __launch_bounds__(128 * WN, 1) void hsr_mfma_kernel(HsrArgs a) {
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   for (int t = 0; t < nsteps; ++t) {
-    wait_tiles_barrier<C::PER_WAVE>(min(C::NS - 2, nsteps - 1 - t));
+    wait_tiles_barrier<C::PER_WAVE, C::NS - 2>(nsteps - 1 - t);
     // The refill of step t - 1's slot is spread over this step's MFMAs: the
     // matrix cores keep working while the address unit takes the requests
     // (one 1 KB request per 16 clocks per CU), instead of every wave

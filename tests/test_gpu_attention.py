@@ -239,14 +239,16 @@ def test_paged_equals_contiguous_on_device():
 
 
 @pytest.mark.parametrize("dt", [W.BF16, W.F32])
-@pytest.mark.parametrize("L", [(5000, 3100, 130), (904, 2017, 130), (938, 997, 1300)])
+@pytest.mark.parametrize("L", [(5000, 3100, 130), (904, 2017, 130), (938, 997, 1300),
+                               (1064, 1131, 2400)])
 def test_rows_past_the_length_are_never_used(dt, L):
     """Cache capacity beyond kv_len holds NaN keys and infinite values: the
     output must still match the oracle (which never reads those rows).  With
-    256 CUs these shapes plan 288-key splits whose first three 64-key tiles
-    the dense kernel requests before the length is known; 904 and 2017 end
-    inside a split's tile 0, 938 inside tile 1, 997 and 1300 inside tile 2,
-    so those tiles are requested again."""
+    256 CUs these shapes plan 288-key splits whose first four 64-key tiles
+    the dense bf16 kernel requests before the length is known; 904 and 2017
+    end inside a split's tile 0, 938 inside tile 1, 997 and 1300 inside tile
+    2, 1064 inside tile 3, so those tiles are requested again; 1131 ends in
+    tile 4, which is requested only after the length is known."""
     c = W.small_attn(41, 3, 28, 4, 128, 6, L, dt, max_len=5600)
     kb, vb = c.k.bits.copy(), c.v.bits.copy()
     nan, inf = (0x7FC0, 0x7F80) if dt == W.BF16 else (np.nan, np.inf)   # bf16 bits / fp32 values
