@@ -3,14 +3,14 @@
 //
 // accept_scan_kernel: the vocabulary of every row is cut into chunks so that
 // every CU streams logits; a workgroup reduces its chunk to one packed
-// 64-bit key
-//   (order-preserving bits of the value) << 32 | (0xFFFFFFFF - index)
-// whose maximum is "largest value, then lowest index" in any reduction
-// order, and stores it to its own slot (no atomics: device-scope atomics on
-// shared words serialise and cost tens of microseconds at batch 64).
+// 64-bit key (see below) and stores it to its own slot (no atomics:
+// device-scope atomics on shared words serialise and cost tens of
+// microseconds at batch 64).
 // accept_finish_kernel: one workgroup per sequence takes the maximum over
 // each row's slots, turns it into the target token and counts the matching
 // prefix.
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 
@@ -19,7 +19,6 @@ namespace spec {
 namespace {
 
 constexpr int kAcceptThreads = 256;
-constexpr int kAccLoads = 4;      // 16-byte loads in flight per thread
 
 struct AcceptArgs {
   const void* logits;
@@ -48,45 +47,59 @@ __device__ __forceinline__ unsigned long long shfl_xor64(unsigned long long v, i
          (uint32_t)__shfl_xor((int)(uint32_t)v, o);
 }
 
-template <bool BF16>
+// Running maximum of one thread: elements arrive in increasing index order,
+// and only a strictly larger value replaces the current one, so the kept
+// index is the lowest of the maximum (IEEE compare: -0 does not replace +0,
+// nor +0 -0).
+__device__ __forceinline__ void take(float x, int v, bool ok, float& m, int& mi) {
+  const bool gt = ok & (x > m);
+  m = gt ? x : m;
+  mi = gt ? v : mi;
+}
+
+// Chunk maximum of one row: every thread requests its NL 16-byte loads at
+// once (rows past gamma are scanned too, so no load waits for gamma), keeps
+// a (value, index) pair, and packs it into the 64-bit key
+//   (order-preserving bits of the value) << 32 | (0xFFFFFFFF - index)
+// only once, for the workgroup reduction: the key's maximum is "largest
+// value, then lowest index" in any reduction order.
+template <bool BF16, int NL>
 __global__ __launch_bounds__(kAcceptThreads) void accept_scan_kernel(AcceptArgs a) {
   constexpr int EPV = BF16 ? 8 : 4;                 // elements per 16-byte load
-  constexpr int SCALAR = kAccLoads * EPV;           // scalar loads per thread (ragged vocab)
+  constexpr int SCALAR = NL * EPV;                  // scalar loads per thread (ragged vocab)
   __shared__ unsigned long long red[kAcceptThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = blockIdx.x / a.chunks;              // b * n_max + i
   const int ch = blockIdx.x - row * a.chunks;
   const int v0 = ch * a.chunk, v1 = min(a.V, v0 + a.chunk);
-  // Every row is scanned (rows past gamma are ignored at the end), so the
-  // loads do not wait for gamma; all of a thread's loads are in flight at once.
-  unsigned long long best = 0;
+  float m = -INFINITY;
+  int mi = -1;
   if (a.vec) {
     const unsigned char* p = reinterpret_cast<const unsigned char*>(a.logits) +
                              (size_t)row * a.V * (BF16 ? 2 : 4);
-    u32x4_t w[kAccLoads];
+    // clamped, unconditional loads (a guarded load waits for itself before
+    // the next is issued); elements past the chunk are masked below
+    u32x4_t w[NL];
 #pragma unroll
-    for (int k = 0; k < kAccLoads; ++k) {
-      const int v = v0 + (k * kAcceptThreads + tid) * EPV;
-      w[k] = (v < v1) ? ld16(p + (size_t)v * (BF16 ? 2 : 4)) : u32x4_t{0, 0, 0, 0};
+    for (int k = 0; k < NL; ++k) {
+      const int v = min(v0 + (k * kAcceptThreads + tid) * EPV, v1 - EPV);
+      w[k] = ld16(p + (size_t)v * (BF16 ? 2 : 4));
     }
 #pragma unroll
-    for (int k = 0; k < kAccLoads; ++k) {
+    for (int k = 0; k < NL; ++k) {
       const int v = v0 + (k * kAcceptThreads + tid) * EPV;
-      if (v < v1) {
+      const bool ok = v < v1;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (BF16) {
-            best = umax64(best, pack_key(__uint_as_float(w[k][j] << 16), v + 2 * j));
-            best = umax64(best, pack_key(__uint_as_float(w[k][j] & 0xFFFF0000u), v + 2 * j + 1));
-          } else {
-            best = umax64(best, pack_key(__uint_as_float(w[k][j]), v + j));
-          }
+      for (int j = 0; j < 4; ++j) {
+        if (BF16) {
+          take(__uint_as_float(w[k][j] << 16), v + 2 * j, ok, m, mi);
+          take(__uint_as_float(w[k][j] & 0xFFFF0000u), v + 2 * j + 1, ok, m, mi);
+        } else {
+          take(__uint_as_float(w[k][j]), v + j, ok, m, mi);
         }
       }
     }
   } else {
-    // unconditional loads from clamped indices (a guarded load becomes a
-    // branch with its own wait); out-of-range lanes are masked below
     float x[SCALAR];
 #pragma unroll
     for (int k = 0; k < SCALAR; ++k) {
@@ -97,16 +110,17 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_scan_kernel(AcceptArgs 
 #pragma unroll
     for (int k = 0; k < SCALAR; ++k) {
       const int v = v0 + k * kAcceptThreads + tid;
-      if (v < v1) best = umax64(best, pack_key(x[k], v));
+      take(x[k], v, v < v1, m, mi);
     }
   }
+  unsigned long long best = (mi >= 0) ? pack_key(m, (uint32_t)mi) : 0ull;
   for (int o = 32; o > 0; o >>= 1) best = umax64(best, shfl_xor64(best, o));
   if (lane == 0) red[wave] = best;
   __syncthreads();
   if (tid == 0) {
-    unsigned long long m = red[0];
-    for (int w = 1; w < kAcceptThreads / 64; ++w) m = umax64(m, red[w]);
-    a.best[(size_t)row * a.chunks + ch] = m;
+    unsigned long long mm = red[0];
+    for (int w = 1; w < kAcceptThreads / 64; ++w) mm = umax64(mm, red[w]);
+    a.best[(size_t)row * a.chunks + ch] = mm;
   }
 }
 
@@ -160,14 +174,20 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_finish_kernel(AcceptArg
 }
 
 struct AcceptPlan {
-  int chunk, chunks, vec;
+  int loads, chunk, chunks, vec;
   size_t ws_bytes;
 };
 
+// Chunks of 256 threads x `loads` 16-byte loads: 8 loads (128 bytes in
+// flight per thread) when that still gives every CU two workgroups, else 2,
+// so that a few rows (one sequence) spread over the chip.
 AcceptPlan plan_accept(int batch, int n_max, int vocab, bool bf16) {
   AcceptPlan p;
   const int vw = bf16 ? 8 : 4;
-  p.chunk = kAcceptThreads * kAccLoads * vw;        // 64 B of logits per thread
+  const long rows = (long)batch * n_max;
+  const int big = kAcceptThreads * 8 * vw;
+  p.loads = (rows * ((vocab + big - 1) / big) >= 2L * device_cu_count()) ? 8 : 2;
+  p.chunk = kAcceptThreads * p.loads * vw;
   p.vec = (vocab % vw == 0) ? 1 : 0;
   if (p.chunk > vocab) p.chunk = ((vocab + vw - 1) / vw) * vw;
   p.chunks = (vocab + p.chunk - 1) / p.chunk;
@@ -216,9 +236,15 @@ spec_status_t launch_commit(const CommitArgs& a, hipStream_t stream) {
 }
 
 size_t accept_workspace(int batch, int n_max, int vocab) {
-  const AcceptPlan a = plan_accept(batch, n_max, vocab, true);
-  const AcceptPlan b = plan_accept(batch, n_max, vocab, false);
-  return a.ws_bytes > b.ws_bytes ? a.ws_bytes : b.ws_bytes;
+  // the largest of the plans any dtype and CU count can choose
+  size_t need = 0;
+  for (int vw : {4, 8}) {
+    const int chunk = std::min(kAcceptThreads * 2 * vw, ((vocab + vw - 1) / vw) * vw);
+    const size_t chunks = (size_t)((vocab + chunk - 1) / chunk);
+    need = std::max(need, kSyncBytes + align_up((size_t)batch * n_max * chunks *
+                                                    sizeof(unsigned long long), 256));
+  }
+  return need;
 }
 
 spec_status_t launch_accept(const void* logits, int dtype, int batch, int n_max, int vocab,
@@ -242,10 +268,14 @@ spec_status_t launch_accept(const void* logits, int dtype, int batch, int n_max,
   a.chunks = p.chunks;
   a.vec = p.vec;
   const dim3 grid((unsigned)batch * n_max * p.chunks), block(kAcceptThreads);
-  if (bf16)
-    hipLaunchKernelGGL(accept_scan_kernel<true>, grid, block, 0, stream, a);
+  if (bf16 && p.loads == 8)
+    hipLaunchKernelGGL((accept_scan_kernel<true, 8>), grid, block, 0, stream, a);
+  else if (bf16)
+    hipLaunchKernelGGL((accept_scan_kernel<true, 2>), grid, block, 0, stream, a);
+  else if (p.loads == 8)
+    hipLaunchKernelGGL((accept_scan_kernel<false, 8>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL(accept_scan_kernel<false>, grid, block, 0, stream, a);
+    hipLaunchKernelGGL((accept_scan_kernel<false, 2>), grid, block, 0, stream, a);
   if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
   hipLaunchKernelGGL(accept_finish_kernel, dim3((unsigned)batch), dim3(kAcceptThreads), 0, stream,
                      a);
