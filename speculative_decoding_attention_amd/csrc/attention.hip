@@ -91,6 +91,92 @@ __device__ __forceinline__ int unit_slots(const AttnArgs& a, int b, int g, int L
   return ld_uniform(a.slot_len, b * a.Hkv + g) + max(0, L - tail_begin(a, b, L));
 }
 
+// Balanced split plan from the device lengths.  One lane per sequence (at
+// most 64) loads its slot count T_b (modes 0-2: the same for each of its KV
+// heads); every unit of sequence b gets S_b = max(1, ceil(T_b / ch)) splits
+// of ch slots, where ch is the smallest multiple of 32 (at least 128) with
+// at most `dyn_groups` splits in all -- found by bisection between the
+// total over dyn_groups and the capacity plan's split length, which always
+// fits.  So every split fits the capacity plan's LDS staging and the grid
+// (one workgroup per CU), and the longest split is as short as the whole
+// tiles allow.  Splits are numbered unit by unit (b, then g, then s); split
+// w's partial is slot w.  Each wave computes the plan itself (one vector
+// load, then shuffles).
+struct DynSplit {
+  int b, g, s;      // unit (b, g) and split index within it
+  int ch;           // slots per split
+  int S;            // splits of the unit
+  int first;        // slot of the unit's first partial
+  int w;            // split index (= partial slot)
+  bool valid;       // false: this workgroup has no split
+};
+
+__device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// by_unit: `key` is a unit index (the merge's query).  Otherwise `key` is
+// the workgroup index: workgroups below the number of splits take one each,
+// through the XCD-aware order over exactly that many (the hardware deals
+// workgroup i to XCD i mod 8, so the splits spread evenly over the XCDs and
+// neighbouring splits share one), the rest have nothing to do.
+__device__ __forceinline__ DynSplit dyn_split(const AttnArgs& a, int key, bool by_unit) {
+  const int lane = threadIdx.x & 63;
+  const int bb = min(lane, a.B - 1);
+  int t = (a.mode == 1) ? a.slot_len[bb] : a.kv_len[bb];
+  if (a.mode == 2) t = min(t, a.slot_stride);
+  const int T = (lane < a.B) ? max(t, 0) : 0;
+  long tot = T;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o);
+  tot *= a.Hkv;
+  long lo = (tot + a.dyn_groups - 1) / a.dyn_groups;
+  lo = max(((lo + kTK - 1) / kTK) * kTK, (long)(kTK * kNW));
+  long hi = max((long)a.chunk, lo);                  // the capacity plan's length fits
+  while (lo < hi) {                                  // multiples of kTK: smallest that fits
+    const long mid = ((lo + hi) / 2 / kTK) * kTK;
+    const long c = max(mid, lo);
+    long n = (lane < a.B) ? max(1L, ((long)T + c - 1) / c) : 0;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) n += __shfl_xor(n, o);
+    if (n * a.Hkv <= a.dyn_groups) hi = c;
+    else lo = c + kTK;
+  }
+  const int ch = (int)hi;
+  const int Sb = (lane < a.B) ? max(1, (T + ch - 1) / ch) : 0;
+  const int cnt = Sb * a.Hkv;
+  const int incl = wave_inclusive_scan(cnt, lane);
+  DynSplit d;
+  d.ch = ch;
+  if (by_unit) {
+    d.b = key / a.Hkv;
+    d.g = key - d.b * a.Hkv;
+    d.s = 0;
+    d.S = __shfl(Sb, d.b);
+    d.first = __shfl(incl - cnt, d.b) + d.g * d.S;
+    d.w = d.first;
+    d.valid = true;
+    return d;
+  }
+  const int total = __shfl(incl, 63);                // lanes past B add nothing
+  d.valid = key < total;
+  key = d.valid ? xcd_remap(key, total) : 0;
+  d.w = key;
+  const uint64_t m = __builtin_amdgcn_ballot_w64(lane < a.B && key < incl);
+  d.b = d.valid ? __ffsll((long long)m) - 1 : 0;
+  d.S = max(1, __shfl(Sb, d.b));
+  const int off = key - __shfl(incl - cnt, d.b);
+  d.g = off / d.S;
+  d.s = off - d.g * d.S;
+  d.first = key - d.s;
+  return d;
+}
+
 // The list entry of this thread's first slot, t_beg + threadIdx.x, requested
 // before the lengths that bound the split are known: the index is clamped to
 // the list's extent, so the load is always in bounds, and stage_slots ignores
@@ -592,8 +678,8 @@ __device__ __forceinline__ void pipe_issue_tile(const AttnArgs& a, const SlotMap
 template <int NB>
 __device__ __forceinline__ void pipe_finish(const AttnArgs& a, float* smem, int wave, int lane,
                                             bool active, int nb, int p, int u, int s, int b,
-                                            int g, int nq, float m_run, float l_run, float l_rnd,
-                                            f32x4_t (&acc)[8]) {
+                                            int g, int nq, int S_unit, size_t pidx, float m_run,
+                                            float l_run, float l_rnd, f32x4_t (&acc)[8]) {
   constexpr int D = 128, RP = NB * 16, DP = D + 4;
   constexpr int KP = PipeCfg<NB>::KP;
   constexpr int PARK = (KP > 1) ? KP - 1 : 1;
@@ -673,7 +759,7 @@ __device__ __forceinline__ void pipe_finish(const AttnArgs& a, float* smem, int 
       for (int k = 1; k < KP; ++k)
         o[db] += *reinterpret_cast<const f32x4_t*>(macc + ((k - 1) * RP + n) * DP + db * 16 + 4 * q4);
     }
-    if (a.S == 1) {
+    if (S_unit == 1) {
       const int i = n / a.G, hh = n - i * a.G;
       const float Ls = mrow[RP + n], Lr = mrow[2 * RP + n];
       const bool live = (i < nq) && (Ls > 0.f);
@@ -696,14 +782,14 @@ __device__ __forceinline__ void pipe_finish(const AttnArgs& a, float* smem, int 
         a.lse[((size_t)b * a.n_max + i) * a.Hq + g * a.G + hh] =
             live ? (mrow[n] + log2f(Ls)) * 0.69314718055994531f : -INFINITY;
     } else {
-      float* pa = a.part_acc + ((size_t)u * a.S + s) * R * D + (size_t)n * D;
+      float* pa = a.part_acc + pidx * R * D + (size_t)n * D;
 #pragma unroll
       for (int db = 0; db < 8; ++db)
         *reinterpret_cast<f32x4_t*>(pa + db * 16 + 4 * q4) = o[db];
     }
   }
-  if (a.S > 1) {
-    float* pm = a.part_ml + ((size_t)u * a.S + s) * 3 * R;
+  if (S_unit > 1) {
+    float* pm = a.part_ml + pidx * 3 * R;
     for (int r = threadIdx.x; r < R; r += blockDim.x) {
       pm[r] = mrow[r];
       pm[R + r] = mrow[RP + r];
@@ -755,12 +841,33 @@ __global__ __launch_bounds__(PipeCfg<NB>::WAVES * 64, 1) void attn_bf16_pipe_ker
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, q4 = lane >> 4;
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
-  const int u = wg / a.S, s = wg - u * a.S;
-  const int b = u / a.Hkv, g = u - b * a.Hkv;
+  int u, s, b, g, chunk, S_unit;
+  size_t pidx;
+  if (a.dyn) {
+    // the split comes from the device lengths; a workgroup past the last
+    // split has nothing to do (it has touched neither LDS nor the ring)
+    const DynSplit d = dyn_split(a, blockIdx.x, false);
+    if (!d.valid) return;
+    b = d.b;
+    g = d.g;
+    s = d.s;
+    chunk = d.ch;
+    S_unit = d.S;
+    pidx = (size_t)d.w;
+  } else {
+    u = wg / a.S;
+    s = wg - u * a.S;
+    b = u / a.Hkv;
+    g = u - b * a.Hkv;
+    chunk = a.chunk;
+    S_unit = a.S;
+    pidx = (size_t)u * a.S + s;
+  }
+  u = b * a.Hkv + g;
   lds_u8_t* const ring_l = (lds_u8_t*)ring;        // the ring as an LDS-address-space pointer
   const uint32_t ring_lds = (uint32_t)(size_t)ring_l;
   constexpr uint32_t kQSlot = (uint32_t)((C::NS - 1) * C::TILE_BYTES);
-  const int t_beg = s * a.chunk;
+  const int t_beg = s * chunk;
   SlotMap<GATHER> sm;
   sm.t_beg = t_beg;
   sm.base_row = ((uint32_t)b * (uint32_t)a.Hkv + (uint32_t)g) * (uint32_t)a.max_len;
@@ -772,16 +879,18 @@ __global__ __launch_bounds__(PipeCfg<NB>::WAVES * 64, 1) void attn_bf16_pipe_ker
   const int pre = GATHER ? prefetch_slot(a, b, g, t_beg) : 0;
   const int L = ld_uniform(a.kv_len, b);
   const int nq = a.q_len ? ld_uniform(a.q_len, b) : a.n_max;
-  // Dense splits: the first NS - 1 tiles and the query block go out before
-  // the sequence length is known, so their round trips overlap the length's.
-  // Their slots are clamped to the split's end as planned over the cache
-  // capacity, so every row they name lies inside the cache.  Rows past the
-  // sequence's end may hold anything (a masked key still adds 0 * V), so
-  // when the sequence ends inside these tiles they are requested again below.
-  const int spec_end = min(t_beg + a.chunk, a.max_len);
+  // Dense splits of the capacity plan: the first NS - 1 tiles and the query
+  // block go out before the sequence length is known, so their round trips
+  // overlap the length's.  Their slots are clamped to the split's end as
+  // planned over the cache capacity, so every row they name lies inside the
+  // cache.  Rows past the sequence's end may hold anything (a masked key
+  // still adds 0 * V), so when the sequence ends inside these tiles they are
+  // requested again below.  (A balanced split already knows its lengths.)
+  const bool spec = !GATHER && !a.dyn;
+  const int spec_end = min(t_beg + chunk, a.max_len);
   const int spec_tiles =
-      GATHER ? 0 : min(C::NS - 1, (spec_end - t_beg + C::TILE_KEYS - 1) / C::TILE_KEYS);
-  if (!GATHER) {
+      spec ? min(C::NS - 1, (spec_end - t_beg + C::TILE_KEYS - 1) / C::TILE_KEYS) : 0;
+  if (spec) {
     pipe_issue_tile<NB, GATHER>(a, sm, t_beg, spec_end, ring_lds, wave, lane);
     pipe_issue_q<NB>(a, b, g, ring_lds + kQSlot, wave, lane);
     for (int j = 1; j < spec_tiles; ++j)
@@ -789,7 +898,7 @@ __global__ __launch_bounds__(PipeCfg<NB>::WAVES * 64, 1) void attn_bf16_pipe_ker
                                   ring_lds + (uint32_t)(j * C::TILE_BYTES), wave, lane);
   }
   const int T = GATHER ? unit_slots(a, b, g, L) : L;   // a dense split is mode 0
-  const int t_end = min(T, t_beg + a.chunk);
+  const int t_end = min(T, t_beg + chunk);
   const int n_tiles = t_end > t_beg ? (t_end - t_beg + C::TILE_KEYS - 1) / C::TILE_KEYS : 0;
   if (GATHER) {
     stage_slots(a, b, g, L, t_beg, t_end, s_pos, s_row, s_bmax, pre);
@@ -804,14 +913,14 @@ __global__ __launch_bounds__(PipeCfg<NB>::WAVES * 64, 1) void attn_bf16_pipe_ker
   const bool valid = active && n < nq * a.G;
   const int qi = n / a.G;
   const int rowP = valid ? L - nq + qi : 0x7fffffff;
-  // Gathered splits resolve their slots first (plain loads the compiler
-  // waits for), then send the query block ahead of the first tiles.
-  if (GATHER) pipe_issue_q<NB>(a, b, g, ring_lds + kQSlot, wave, lane);
+  // Gathered and balanced splits resolve their slots first (plain loads the
+  // compiler waits for), then send the query block ahead of the first tiles.
+  if (!spec) pipe_issue_q<NB>(a, b, g, ring_lds + kQSlot, wave, lane);
   bf16x8_t qop[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) qop[ks] = as_bf16x8(u32x4_t{0, 0, 0, 0});
 
-  if (!GATHER && n_tiles > 0 &&
+  if (spec && n_tiles > 0 &&
       t_end < min(t_beg + min(spec_tiles, n_tiles) * C::TILE_KEYS, spec_end)) {
     // an early tile that is read named rows past the sequence: every wave's
     // requests land before any wave re-requests those slots (early tiles
@@ -821,7 +930,7 @@ __global__ __launch_bounds__(PipeCfg<NB>::WAVES * 64, 1) void attn_bf16_pipe_ker
       pipe_issue_tile<NB, GATHER>(a, sm, t_beg + j * C::TILE_KEYS, t_end,
                                   ring_lds + (uint32_t)(j * C::TILE_BYTES), wave, lane);
   }
-  for (int j = GATHER ? 0 : spec_tiles; j < C::NS - 1 && j < n_tiles; ++j)
+  for (int j = spec_tiles; j < C::NS - 1 && j < n_tiles; ++j)
     pipe_issue_tile<NB, GATHER>(a, sm, t_beg + j * C::TILE_KEYS, t_end,
                                 ring_lds + (uint32_t)(j * C::TILE_BYTES), wave, lane);
 
@@ -974,7 +1083,7 @@ __global__ __launch_bounds__(PipeCfg<NB>::WAVES * 64, 1) void attn_bf16_pipe_ker
   }
   if (n_tiles == 0) wait_dma_barrier<0>();   // the query DMA still targets the ring
   pipe_finish<NB>(a, reinterpret_cast<float*>(ring), wave, lane, active, nb, p, u, s, b, g, nq,
-                  m_run, l_run, l_rnd, acc);
+                  S_unit, pidx, m_run, l_run, l_rnd, acc);
 }
 
 // ---------------------------------------------------------------- fp32 ----
@@ -1136,17 +1245,27 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
   static_assert(DS % 64 == 0 && PB >= 1, "merge shape");
   __shared__ float part[NG][DS];
   __shared__ float gstat[3][NG];
-  const int R = a.R, S = a.SP;
+  const int R = a.R;
   const int row = blockIdx.x / (D / DS), slice = blockIdx.x - row * (D / DS);
   const int u = row / R, r = row - u * R;
   const int b = u / a.Hkv, g = u - b * a.Hkv;
   const int i = r / a.G, hh = r - i * a.G;
   const int tid = threadIdx.x, dl = tid % DS, d = slice * DS + dl;
+  // the unit's partials: S per unit in the capacity plan, or the balanced
+  // plan's (a unit with one split wrote its output itself)
+  int S = a.SP;
+  size_t first = (size_t)u * a.SP;
+  if (a.dyn) {
+    const DynSplit ds = dyn_split(a, u, true);
+    if (ds.S == 1) return;
+    S = ds.S;
+    first = (size_t)ds.first;
+  }
   // the group index is uniform over a wave (DS is a multiple of 64), so the
   // per-split statistics below are scalar loads
   const int grp = __builtin_amdgcn_readfirstlane(tid / DS);
-  const float* pm = a.part_ml + (size_t)u * S * 3 * R + r;
-  const float* pa = a.part_acc + (size_t)u * S * R * D + (size_t)r * D + d;
+  const float* pm = a.part_ml + first * 3 * R + r;
+  const float* pa = a.part_acc + first * R * D + (size_t)r * D + d;
 
   float M = -INFINITY, o = 0.f, ls = 0.f, lr = 0.f;
   for (int base = grp; base < S; base += NG * PB) {
@@ -1216,48 +1335,65 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
 }
 
 // Few partials per unit (a batch of short or ragged units): one thread per
-// (row, column), 256 / D rows per workgroup, every partial of the row
-// requested in one round.  The grouped kernel above would spend a 512-thread
+// (row, column), 256 / D rows per workgroup, the row's partials requested
+// kMergeSmall at a time (one round for the capacity plan's few partials;
+// the balanced plan's units may have more, merged round by round against a
+// running maximum).  The grouped kernel above would spend a 512-thread
 // workgroup on each (row, 64 columns) with most groups idle.
 constexpr int kMergeSmall = 8;
 
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_small_kernel(AttnArgs a) {
   constexpr int RPW = 256 / D;
-  const int R = a.R, S = a.SP;
+  const int R = a.R;
   const int blocks_per_unit = (R + RPW - 1) / RPW;
   const int u = blockIdx.x / blocks_per_unit, rb = blockIdx.x - u * blocks_per_unit;
+  int S = a.SP;
+  size_t first = (size_t)u * a.SP;
+  if (a.dyn) {
+    const DynSplit ds = dyn_split(a, u, true);
+    if (ds.S == 1) return;                 // the split wrote the output itself
+    S = ds.S;
+    first = (size_t)ds.first;
+  }
   // the row is uniform over a wave (D is a multiple of 64): scalar statistics
   const int r = __builtin_amdgcn_readfirstlane(rb * RPW + (int)threadIdx.x / D);
   if (r >= R) return;
   const int d = threadIdx.x % D;
   const int b = u / a.Hkv, g = u - b * a.Hkv;
   const int i = r / a.G, hh = r - i * a.G;
-  const float* pm = a.part_ml + (size_t)u * S * 3 * R + r;
-  const float* pa = a.part_acc + (size_t)u * S * R * D + (size_t)r * D + d;
-  float v[kMergeSmall], mv[kMergeSmall], lv[kMergeSmall], rv[kMergeSmall];
+  const float* pm = a.part_ml + first * 3 * R + r;
+  const float* pa = a.part_acc + first * R * D + (size_t)r * D + d;
+  float M = -INFINITY, o = 0.f, Ls = 0.f, Lr = 0.f;
+  for (int base = 0; base < S; base += kMergeSmall) {
+    float v[kMergeSmall], mv[kMergeSmall], lv[kMergeSmall], rv[kMergeSmall];
 #pragma unroll
-  for (int j = 0; j < kMergeSmall; ++j) {          // clamped, masked after
-    const int sp = min(j, S - 1);
-    v[j] = pa[(size_t)sp * R * D];
-    mv[j] = pm[(size_t)sp * 3 * R];
-    lv[j] = pm[(size_t)sp * 3 * R + R];
-    rv[j] = pm[(size_t)sp * 3 * R + 2 * R];
-  }
-  float M = -INFINITY;
+    for (int j = 0; j < kMergeSmall; ++j) {          // clamped, masked after
+      const int sp = min(base + j, S - 1);
+      v[j] = pa[(size_t)sp * R * D];
+      mv[j] = pm[(size_t)sp * 3 * R];
+      lv[j] = pm[(size_t)sp * 3 * R + R];
+      rv[j] = pm[(size_t)sp * 3 * R + 2 * R];
+    }
+    float mr = M;
 #pragma unroll
-  for (int j = 0; j < kMergeSmall; ++j) {
-    if (j >= S) mv[j] = -INFINITY;
-    M = fmaxf(M, mv[j]);
-  }
-  const float Mu = (M == -INFINITY) ? 0.f : M;
-  float o = 0.f, Ls = 0.f, Lr = 0.f;
+    for (int j = 0; j < kMergeSmall; ++j) {
+      if (base + j >= S) mv[j] = -INFINITY;
+      mr = fmaxf(mr, mv[j]);
+    }
+    const float Mu = (mr == -INFINITY) ? 0.f : mr;
+    const float sc = __builtin_amdgcn_exp2f(M - Mu);   // M = -inf: nothing merged yet -> 0
+    o *= sc;
+    Ls *= sc;
+    Lr *= sc;
 #pragma unroll
-  for (int j = 0; j < kMergeSmall; ++j) {
-    const float w = __builtin_amdgcn_exp2f(mv[j] - Mu);
-    o = __builtin_fmaf(v[j], w, o);
-    Ls = __builtin_fmaf(lv[j], w, Ls);
-    Lr = __builtin_fmaf(rv[j], w, Lr);
+    for (int j = 0; j < kMergeSmall; ++j) {
+      const float w = __builtin_amdgcn_exp2f(mv[j] - Mu);
+      o = __builtin_fmaf(v[j], w, o);
+      Ls = __builtin_fmaf(lv[j], w, Ls);
+      Lr = __builtin_fmaf(rv[j], w, Lr);
+    }
+    M = mr;
   }
   const int nq = a.q_len ? ld_uniform(a.q_len, b) : a.n_max;
   const bool live = (i < nq) && (Ls > 0.f);
@@ -1350,7 +1486,9 @@ AttnPlan plan_attention(int units, int t_max, int rows, int d, bool gather, size
   int S = (int)((T + chunk - 1) / chunk);
   if (S < 1) S = 1;
   p.S = S;
-  p.sp_max = (S > 1 && S * 4 <= kWavePartials) ? S * 4 : S;
+  // partials per unit: one per wave of every split when few, and room for
+  // the balanced plan's (at most grid + units splits)
+  p.sp_max = (S > 1 && S * 4 <= kWavePartials) ? S * 4 : S + 1;
   p.chunk = (int)chunk;
   p.grid = units * S;
   p.gather = gather;
@@ -1367,7 +1505,18 @@ spec_status_t launch_attention(AttnArgs a, int d, int dtype, const AttnPlan& pla
                                hipStream_t stream) {
   a.S = plan.S;
   a.SP = plan.S;
-  if (plan.S > 1 && dtype == SPEC_BF16 && d == 128) {
+  a.dyn = 0;
+  a.dyn_groups = plan.grid;
+  int grid = plan.grid;
+  const int units = a.B * a.Hkv;
+  if (plan.S > 1 && dtype == SPEC_BF16 && d == 128 && a.mode == 0 && a.B >= 2 && a.B <= 64) {
+    // several sequences: split what the lengths hold rather than the
+    // capacity, so short sequences leave no empty workgroups and every
+    // split is about as long (the partials are numbered split by split).
+    // Text and top-K lists are short: there the extra round trip for the
+    // lengths before the list is read costs more than the balance saves.
+    a.dyn = 1;
+  } else if (plan.S > 1 && dtype == SPEC_BF16 && d == 128) {
     // the pipelined kernel's waves write their own partials when that keeps
     // the merge small (phases per split as in PipeCfg)
     const int nb = min(4, (a.R + 15) / 16);
@@ -1382,18 +1531,19 @@ spec_status_t launch_attention(AttnArgs a, int d, int dtype, const AttnPlan& pla
     a.part_acc = nullptr;
     a.part_ml = nullptr;
   }
-  if (plan.grid == 0) return SPEC_OK;
+  if (grid == 0) return SPEC_OK;
   hipError_t e;
   if (plan.gather)
-    e = (d == 64) ? launch_d<64, true>(a, dtype, plan.grid, stream)
-                  : launch_d<128, true>(a, dtype, plan.grid, stream);
+    e = (d == 64) ? launch_d<64, true>(a, dtype, grid, stream)
+                  : launch_d<128, true>(a, dtype, grid, stream);
   else
-    e = (d == 64) ? launch_d<64, false>(a, dtype, plan.grid, stream)
-                  : launch_d<128, false>(a, dtype, plan.grid, stream);
+    e = (d == 64) ? launch_d<64, false>(a, dtype, grid, stream)
+                  : launch_d<128, false>(a, dtype, grid, stream);
   if (e != hipSuccess) return SPEC_ERR_HIP;
   if (plan.S > 1) {
-    const int units = a.B * a.Hkv;
-    if (a.SP <= kMergeSmall) {
+    // balanced plans merge few partials per unit when the capacity plan has
+    // few splits (a unit's balanced split count is about its share of them)
+    if (a.dyn ? plan.S <= 2 * kMergeSmall : a.SP <= kMergeSmall) {
       const int rpw = 256 / d;
       const int blocks = units * ((a.R + rpw - 1) / rpw);
       if (d == 64)

@@ -45,6 +45,12 @@ struct AttnArgs {
   float scale_log2;           // softmax scale * log2(e)
   float* part_acc;            // [U*S, R, D] unnormalised partial outputs
   float* part_ml;             // [U*S, 3, R] partial (max, sum, rounded-weight sum), log2 domain
+  // Balanced splits from the device lengths (bf16, d = 128, dense
+  // verification of 2..64 sequences): the slots actually present are spread over
+  // dyn_groups workgroups; partials are numbered split by split, unit by
+  // unit (see dyn_split in attention.hip).
+  int32_t dyn;
+  int32_t dyn_groups;
   void* out;
   int32_t out_bf16;
   float* lse;
@@ -58,7 +64,7 @@ constexpr size_t kSyncBytes = SPEC_WS_SYNC_BYTES;
 
 struct AttnPlan {
   int S = 1;
-  int sp_max = 1;             // partials per unit the workspace holds (S, or S * 4)
+  int sp_max = 1;             // partials per unit the workspace holds (S + 1, or S * 4)
   int chunk = 0;
   int grid = 0;
   bool gather = false;        // slots resolved through a list or a page table

@@ -66,9 +66,9 @@ __device__ __forceinline__ bool decode_block(const StdArgs& a, Block& k) {
   k.u = us / a.S;
   k.b = k.u / a.Hkv;
   k.g = k.u - k.b * a.Hkv;
-  k.rows = a.text_len[k.b] * a.G;
+  k.rows = ld_uniform(a.text_len, k.b) * a.G;
   k.r0 = k.rb * kBR;
-  k.L = a.kv_len[k.b];
+  k.L = ld_uniform(a.kv_len, k.b);
   k.k0 = k.s * a.chunk;
   k.k1 = min(k.L, k.k0 + a.chunk);
   return k.r0 < k.rows;

@@ -97,19 +97,40 @@ __global__ __launch_bounds__(256) void topk_score_kernel(TopkArgs a) {
   const int tiles = (a.max_len + kScoreKeys - 1) / kScoreKeys;
   const int u = blockIdx.x / tiles, tile = blockIdx.x - (blockIdx.x / tiles) * tiles;
   const int b = u / a.Hkv, g = u - b * a.Hkv;
-  const int L = a.kv_len[b];
+  const int L = ld_uniform(a.kv_len, b);
   const int j0 = tile * kScoreKeys;
+  // The group's query values are requested in batches of 8 heads (clamped,
+  // unconditional loads: all in flight at once) before anything waits,
+  // then summed in head order.
+  constexpr int QB = 8;
+  float qv[QB];
+  const int c = min((int)threadIdx.x, D - 1);
+#pragma unroll
+  for (int k = 0; k < QB; ++k) {
+    const size_t qi = ((size_t)b * a.Hq + g * a.G + min(k, a.G - 1)) * D + c;   // q: [B, 1, Hq, D]
+    qv[k] = BF16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(a.q)[qi])
+                 : reinterpret_cast<const float*>(a.q)[qi];
+  }
   if (j0 >= L) return;
   const int nk = min(kScoreKeys, L - j0);
 
   for (int i = threadIdx.x; i < kHistBins / 2; i += blockDim.x) hist[i] = 0;
   if (threadIdx.x < D) {
     double s = 0.0;
-    for (int h = g * a.G; h < (g + 1) * a.G; ++h) {
-      const size_t qi = ((size_t)b * a.Hq + h) * D + threadIdx.x;   // q is [B, 1, Hq, D]
-      const double qv = BF16 ? (double)bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(a.q)[qi])
-                             : (double)reinterpret_cast<const float*>(a.q)[qi];
-      s = __dadd_rn(s, qv);
+#pragma unroll
+    for (int k = 0; k < QB; ++k)
+      if (k < a.G) s = __dadd_rn(s, (double)qv[k]);
+    for (int h0 = QB; h0 < a.G; h0 += QB) {   // groups of more than 8 heads
+      float qw[QB];
+#pragma unroll
+      for (int k = 0; k < QB; ++k) {
+        const size_t qi = ((size_t)b * a.Hq + g * a.G + min(h0 + k, a.G - 1)) * D + c;
+        qw[k] = BF16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(a.q)[qi])
+                     : reinterpret_cast<const float*>(a.q)[qi];
+      }
+#pragma unroll
+      for (int k = 0; k < QB; ++k)
+        if (h0 + k < a.G) s = __dadd_rn(s, (double)qw[k]);
     }
     qbar[threadIdx.x] = s;
   }
@@ -258,7 +279,7 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(TopkArgs a) {
 #pragma unroll
     for (int k = 0; k < kSelBatch; ++k) kv[k] = k16[min(k * nt + tid, a.max_len - 1)];
   }
-  const int L = a.kv_len[b];
+  const int L = ld_uniform(a.kv_len, b);
 
   if (K >= L) {
     for (int j = tid; j < K; j += nt) out[j] = (j < L) ? j : -1;
@@ -600,10 +621,10 @@ __global__ __launch_bounds__(256) void std_score_kernel(StdArgs s, TopkArgs a, f
   const int tiles = (a.max_len + kScoreKeys - 1) / kScoreKeys;
   const int u = blockIdx.x / tiles, tile = blockIdx.x - (blockIdx.x / tiles) * tiles;
   const int b = u / a.Hkv;
-  const int L = a.kv_len[b];
+  const int L = ld_uniform(a.kv_len, b);
   const int j0 = tile * kScoreKeys;
   if (j0 >= L) return;
-  const int T = s.text_len[b];
+  const int T = ld_uniform(s.text_len, b);
   const int nrb = (T * s.G + 127) / 128;
   for (int i = threadIdx.x; i < kHistBins / 2; i += blockDim.x) hist[i] = 0;
   if (threadIdx.x < kScoreKeys / 32) text_bits[threadIdx.x] = 0;
@@ -680,7 +701,7 @@ __global__ __launch_bounds__(256) void std_list_kernel(StdArgs s, int K, int32_t
   const int u = blockIdx.x / per_u;
   const int item = (blockIdx.x - u * per_u) * 256 + (int)threadIdx.x;
   const int b = u / s.Hkv;
-  const int L = s.kv_len[b], T = s.text_len[b];
+  const int L = ld_uniform(s.kv_len, b), T = ld_uniform(s.text_len, b);
   const int nvis = L - T;
   const int32_t* text = s.text_idx + (size_t)b * s.t_max;
   int32_t* su = sel + (size_t)u * K;

@@ -106,6 +106,21 @@ def test_many_short_units(n, page):
     assert_attention_close(out, lse, ro, rl, c.q_len, W.BF16, f"short units vata n={n}")
 
 
+@pytest.mark.parametrize("page", [0, 16])
+def test_balanced_splits_of_very_uneven_lengths(page):
+    """Balanced splits from the device lengths: one long sequence beside
+    very short ones (and a 1-position one) in a batch of 5, so the long
+    sequence takes most of the splits and the short ones one each;
+    verification and text-anchored attention, paged and contiguous."""
+    L = (30000, 7, 1, 650, 129)
+    c = W.small_attn(91 + page, 5, 28, 4, 128, 6, L, W.BF16, page_size=page,
+                     q_len=[6, 6, 1, 6, 6])
+    out, lse, ro, rl = _verify_pair(c)
+    assert_attention_close(out, lse, ro, rl, c.q_len, W.BF16, "uneven verify")
+    out, lse, ro, rl = _vata_pair(c)
+    assert_attention_close(out, lse, ro, rl, c.q_len, W.BF16, "uneven vata")
+
+
 def test_padded_query_rows_and_bf16_output():
     c = W.small_attn(11, 3, 8, 2, 128, 6, (900, 450, 1200), W.BF16, q_len=[6, 2, 4])
     out, lse, ro, rl = _verify_pair(c, out_dtype=torch.bfloat16)
@@ -239,20 +254,25 @@ def test_paged_equals_contiguous_on_device():
 
 
 @pytest.mark.parametrize("dt", [W.BF16, W.F32])
-@pytest.mark.parametrize("L", [(5000, 3100, 130), (904, 2017, 130), (938, 997, 1300),
-                               (1064, 1131, 2400)])
-def test_rows_past_the_length_are_never_used(dt, L):
+@pytest.mark.parametrize("L,max_len", [((5000, 3100, 130), 5600), ((904, 2017, 130), 5600),
+                                       ((938, 997, 1300), 5600), ((1064, 1131, 2400), 5600),
+                                       ((2017,), 18432), ((5000,), 18432), ((997,), 18432),
+                                       ((1064,), 18432), ((1131,), 18432)])
+def test_rows_past_the_length_are_never_used(dt, L, max_len):
     """Cache capacity beyond kv_len holds NaN keys and infinite values: the
-    output must still match the oracle (which never reads those rows).  With
-    256 CUs these shapes plan 288-key splits whose first four 64-key tiles
-    the dense bf16 kernel requests before the length is known; 904 and 2017
-    end inside a split's tile 0, 938 inside tile 1, 997 and 1300 inside tile
-    2, 1064 inside tile 3, so those tiles are requested again; 1131 ends in
-    tile 4, which is requested only after the length is known."""
-    c = W.small_attn(41, 3, 28, 4, 128, 6, L, dt, max_len=5600)
+    output must still match the oracle (which never reads those rows).
+    Batches of several sequences split the lengths present.  A single
+    sequence is split over the capacity: with 256 CUs, 18,432 positions plan
+    288-key splits whose first four 64-key tiles the dense bf16 kernel
+    requests before the length is known; 2017 ends inside a split's tile 0,
+    5000 inside tile 1, 997 inside tile 2, 1064 inside tile 3, so those
+    tiles are requested again; 1131 ends in tile 4, which is requested only
+    after the length is known."""
+    B = len(L)
+    c = W.small_attn(41, B, 28, 4, 128, 6, L, dt, max_len=max_len)
     kb, vb = c.k.bits.copy(), c.v.bits.copy()
     nan, inf = (0x7FC0, 0x7F80) if dt == W.BF16 else (np.nan, np.inf)   # bf16 bits / fp32 values
-    for b_ in range(3):
+    for b_ in range(B):
         kb[b_, :, L[b_]:] = nan
         vb[b_, :, L[b_]:] = inf
     c.k, c.v = W.Stored(dt, kb), W.Stored(dt, vb)
