@@ -634,11 +634,14 @@ struct PipeCfg {
   static constexpr int TILE_KEYS = 32 * KP;
   static constexpr int SUB_BYTES = 32 * 256;               // one sub-tile of K (or V)
   static constexpr int TILE_BYTES = KP * 2 * SUB_BYTES;
-  // 128 KiB of ring; gathered splits need the other 32 KiB for their slot
-  // tables.  (A five-stage 160 KiB ring for dense splits measured slower:
-  // the deeper first burst delays every split's first tile.)
-  static constexpr int RING_BYTES = 128 * 1024;
-  static constexpr int NS = RING_BYTES / TILE_BYTES;       // 4 or 2 stages
+  // Dense splits of 64-key tiles keep a three-stage ring (two tiles in
+  // flight while one is computed); gathered splits keep four stages, and
+  // their slot tables take the LDS beside the ring.  Deeper dense rings
+  // measured slower at 25k keys over 248 splits (four stages about 1 us
+  // per call more, five about 2 us), also with the first burst held at two
+  // tiles, so the cost is in the steady state, not in the prologue.
+  static constexpr int RING_BYTES = (!GATHER && NB >= 2 ? 96 : 128) * 1024;
+  static constexpr int NS = RING_BYTES / TILE_BYTES;       // 2 to 4 stages
   static constexpr int INSTR = TILE_BYTES / 1024;          // 1 KB DMA instructions per tile
   static constexpr int PER_WAVE = INSTR / WAVES;
   static_assert(NS >= 2, "ring depth");

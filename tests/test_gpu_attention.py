@@ -263,11 +263,11 @@ def test_rows_past_the_length_are_never_used(dt, L, max_len):
     output must still match the oracle (which never reads those rows).
     Batches of several sequences split the lengths present.  A single
     sequence is split over the capacity: with 256 CUs, 18,432 positions plan
-    288-key splits whose first four 64-key tiles the dense bf16 kernel
-    requests before the length is known; 2017 ends inside a split's tile 0,
-    5000 inside tile 1, 997 inside tile 2, 1064 inside tile 3, so those
-    tiles are requested again; 1131 ends in tile 4, which is requested only
-    after the length is known."""
+    288-key splits whose first two 64-key tiles the dense bf16 kernel
+    requests before the length is known; 2017 ends inside a split's tile 0
+    and 5000 inside tile 1, so those tiles are requested again; 997, 1064
+    and 1131 end inside tiles 2, 3 and 4, which are requested only after the
+    length is known."""
     B = len(L)
     c = W.small_attn(41, B, 28, 4, 128, 6, L, dt, max_len=max_len)
     kb, vb = c.k.bits.copy(), c.v.bits.copy()
