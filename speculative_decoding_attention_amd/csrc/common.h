@@ -48,6 +48,20 @@ __device__ __forceinline__ int ld_uniform(const int32_t* p, int i) {
   return ((cptr_t)p)[__builtin_amdgcn_readfirstlane(i)];
 }
 
+// fp64 product and sum, each rounded once to nearest even and never fused
+// with a neighbour into an FMA (fixed-order chains that define a result bit
+// for bit need both roundings; the compiler's default contraction, which
+// also applies to the math header's __dmul_rn / __dadd_rn, would drop the
+// product's).
+__device__ __forceinline__ double mul_rn(double a, double b) {
+#pragma clang fp contract(off)
+  return a * b;
+}
+__device__ __forceinline__ double add_rn(double a, double b) {
+#pragma clang fp contract(off)
+  return a + b;
+}
+
 // 16-byte global load / store helpers.
 __device__ __forceinline__ u32x4_t ld16(const void* p) {
   return *reinterpret_cast<const u32x4_t*>(p);

@@ -7,11 +7,14 @@
 // The evaluation order is fixed so the result is reproducible bit for bit by
 // any implementation.  Keys are ranked by (score desc, index asc).
 //
-// topk_score_kernel: 256 keys per workgroup are staged through LDS with
-//   coalesced 16-byte loads; each thread then runs one key's fp64 chain.  It
-//   writes the score and adds the key to a per-unit 4096-bin histogram of a
-//   coarse monotone key (the top 12 bits of the order-preserving bit pattern
-//   of float(score): sign, exponent, 3 mantissa bits).
+// topk_score_ring_kernel (bf16 keys): one workgroup of 8 waves per range of
+//   a unit's keys; every wave streams its own 64-key tiles through an LDS
+//   slot by DMA and runs one key's fp64 chain per lane while the next tile
+//   is in flight.  It writes the score and adds the key to a per-unit
+//   4096-bin histogram of a coarse monotone key (the top 12 bits of the
+//   order-preserving bit pattern of float(score): sign, exponent, 3 mantissa
+//   bits).  topk_score_kernel does the same for fp32 keys, 256 keys per
+//   workgroup staged with plain loads.
 // topk_select_kernel: one 1024-thread workgroup per unit.  From the
 //   histogram it finds the bin holding the K-th key.  One pass over the
 //   16-bit float keys (also written by the score kernel) sets an LDS
@@ -27,6 +30,8 @@
 //   the scores when the cache is longer than the LDS bit mask.
 #include <math.h>
 #include <string.h>
+
+#include <algorithm>
 
 #include "common.h"
 #include "internal.h"
@@ -48,6 +53,7 @@ struct TopkArgs {
   const int32_t* page_table;
   int32_t max_pages, page_shift;
   int32_t B, Hq, Hkv, G, max_len, top_k;
+  int32_t splits;       // key ranges per unit (streaming score pass)
   double* scores;       // [U, max_len]
   uint16_t* key16;      // [U, max_len] top 16 bits of the ordered float key
   uint32_t* hist;       // [U, kHistBins]
@@ -119,7 +125,7 @@ __global__ __launch_bounds__(256) void topk_score_kernel(TopkArgs a) {
     double s = 0.0;
 #pragma unroll
     for (int k = 0; k < QB; ++k)
-      if (k < a.G) s = __dadd_rn(s, (double)qv[k]);
+      if (k < a.G) s = add_rn(s, (double)qv[k]);
     for (int h0 = QB; h0 < a.G; h0 += QB) {   // groups of more than 8 heads
       float qw[QB];
 #pragma unroll
@@ -130,7 +136,7 @@ __global__ __launch_bounds__(256) void topk_score_kernel(TopkArgs a) {
       }
 #pragma unroll
       for (int k = 0; k < QB; ++k)
-        if (h0 + k < a.G) s = __dadd_rn(s, (double)qw[k]);
+        if (h0 + k < a.G) s = add_rn(s, (double)qw[k]);
     }
     qbar[threadIdx.x] = s;
   }
@@ -173,16 +179,16 @@ __global__ __launch_bounds__(256) void topk_score_kernel(TopkArgs a) {
         const double k1 = (double)__uint_as_float(w.x & 0xFFFF0000u);
         const double k2 = (double)__uint_as_float(w.y << 16);
         const double k3 = (double)__uint_as_float(w.y & 0xFFFF0000u);
-        acc = __dadd_rn(acc, __dmul_rn(qbar[c], k0));
-        acc = __dadd_rn(acc, __dmul_rn(qbar[c + 1], k1));
-        acc = __dadd_rn(acc, __dmul_rn(qbar[c + 2], k2));
-        acc = __dadd_rn(acc, __dmul_rn(qbar[c + 3], k3));
+        acc = add_rn(acc, mul_rn(qbar[c], k0));
+        acc = add_rn(acc, mul_rn(qbar[c + 1], k1));
+        acc = add_rn(acc, mul_rn(qbar[c + 2], k2));
+        acc = add_rn(acc, mul_rn(qbar[c + 3], k3));
       }
     } else {
       for (int c = 0; c < D; c += 2) {
         const float2 w = *reinterpret_cast<const float2*>(row + c * 4);
-        acc = __dadd_rn(acc, __dmul_rn(qbar[c], (double)w.x));
-        acc = __dadd_rn(acc, __dmul_rn(qbar[c + 1], (double)w.y));
+        acc = add_rn(acc, mul_rn(qbar[c], (double)w.x));
+        acc = add_rn(acc, mul_rn(qbar[c + 1], (double)w.y));
       }
     }
     a.scores[(size_t)u * a.max_len + j0 + key] = acc;
@@ -195,6 +201,113 @@ __global__ __launch_bounds__(256) void topk_score_kernel(TopkArgs a) {
   uint32_t* gh = a.hist + (size_t)u * kHistBins;
   for (int i = threadIdx.x; i < kHistBins; i += blockDim.x)
     if (const uint32_t c = (hist[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) atomicAdd(&gh[i], c);
+}
+
+// Streaming score pass for bf16 keys.  The unit's length is cut on the
+// device into a.splits ranges of whole 64-key tiles; range s is workgroup
+// (u, s).  Wave w takes the range's tiles w, w + 8, ... through a private
+// LDS slot.  The DMA stores chunk c of tile row r at chunk position
+// c ^ (r % CH), so the lanes of a quarter-wave, each reading its own key's
+// row, address distinct banks.  A lane copies its row to registers; the
+// slot then takes the next tile's DMA, and the fp64 chain runs while that is
+// in flight.  Only this wave reads and refills its slot, so its own waits
+// order the two: no workgroup barrier inside the loop.
+constexpr int kRingWaves = 8;
+constexpr int kRingTile = 64;   // keys per wave tile (one per lane)
+
+template <int D>
+__global__ __launch_bounds__(kRingWaves * 64, 1) void topk_score_ring_kernel(TopkArgs a) {
+  constexpr int ROW_B = D * 2;               // bytes per key row
+  constexpr int CH = ROW_B / 16;             // 16-byte chunks per row
+  constexpr int RPI = 64 / CH;               // rows per 1 KB DMA instruction
+  constexpr int NI = kRingTile / RPI;        // DMA instructions per tile
+  constexpr int SLOT = kRingTile * ROW_B;
+  __shared__ __align__(16) unsigned char slots[kRingWaves * SLOT];
+  __shared__ __align__(16) double qbar[D];
+  __shared__ uint32_t hist[kHistBins];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int u = blockIdx.x / a.splits, s = blockIdx.x - (blockIdx.x / a.splits) * a.splits;
+  const int b = u / a.Hkv, g = u - b * a.Hkv;
+  const int L = ld_uniform(a.kv_len, b);
+  const int per = ((L + a.splits - 1) / a.splits + kRingTile - 1) / kRingTile * kRingTile;
+  const int t_beg = s * per, t_end = min(L, t_beg + per);
+  const int n_tiles = t_end > t_beg ? (t_end - t_beg + kRingTile - 1) / kRingTile : 0;
+  const int my_tiles = n_tiles > wave ? (n_tiles - wave + kRingWaves - 1) / kRingWaves : 0;
+  lds_u8_t* const slot_l = (lds_u8_t*)(slots + wave * SLOT);
+  const uint32_t slot_lds = (uint32_t)(size_t)slot_l;
+  const unsigned char* kb = reinterpret_cast<const unsigned char*>(a.k);
+  const int rr = lane / CH, cpos = lane % CH;   // DMA lane: row within the instruction, chunk slot
+
+  // DMA of wave tile i: instruction j brings rows RPI*j .. RPI*j + RPI-1
+  // (keys past the range repeat its last key; their scores are not kept).
+  auto issue = [&](int i) {
+    const int k0 = t_beg + (wave + i * kRingWaves) * kRingTile;
+    const size_t mine = topk_row(a, b, g, min(k0 + lane, t_end - 1));
+    const uint32_t lo = (uint32_t)mine, hi = (uint32_t)(mine >> 32);
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int r = RPI * j + rr;
+      const size_t row = (size_t)__shfl(lo, r) | ((size_t)__shfl(hi, r) << 32);
+      dma16(kb + row * ROW_B + 16 * (cpos ^ (r % CH)), slot_lds + (uint32_t)(j * 1024));
+    }
+  };
+  if (my_tiles > 0) issue(0);
+
+  // group query sum, fp64 in head order (the first tile is already in flight)
+  for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) hist[i] = 0;
+  if (threadIdx.x < D) {   // heads requested 8 at a time (clamped), then added in order
+    const uint16_t* qh = reinterpret_cast<const uint16_t*>(a.q) +
+                         ((size_t)b * a.Hq + g * a.G) * D + threadIdx.x;
+    double q = 0.0;
+    for (int h0 = 0; h0 < a.G; h0 += 8) {
+      float qv[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) qv[k] = bf16_bits_to_f32(qh[(size_t)min(h0 + k, a.G - 1) * D]);
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (h0 + k < a.G) q = add_rn(q, (double)qv[k]);
+    }
+    qbar[threadIdx.x] = q;
+  }
+  __syncthreads();
+
+  double* const sc = a.scores + (size_t)u * a.max_len;
+  uint16_t* const k16 = a.key16 + (size_t)u * a.max_len;
+  for (int i = 0; i < my_tiles; ++i) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");      // this wave's tile i is in LDS
+    u32x4_t kr[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+      kr[c] = *reinterpret_cast<const u32x4_t*>(slots + wave * SLOT + lane * ROW_B +
+                                                16 * (c ^ (lane % CH)));
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");    // the slot is free again
+    if (i + 1 < my_tiles) issue(i + 1);
+    double acc = 0.0;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t w = kr[c][e];
+        acc = add_rn(acc, mul_rn(qbar[8 * c + 2 * e], (double)__uint_as_float(w << 16)));
+        acc = add_rn(acc, mul_rn(qbar[8 * c + 2 * e + 1],
+                                       (double)__uint_as_float(w & 0xFFFF0000u)));
+      }
+    }
+    const int key = t_beg + (wave + i * kRingWaves) * kRingTile + lane;
+    if (key < t_end) {
+      sc[key] = acc;
+      const uint32_t k32 = fine_key32(acc);
+      k16[key] = (uint16_t)(k32 >> 16);
+      atomicAdd(&hist[k32 >> 20], 1u);
+    }
+  }
+  __syncthreads();
+  if (n_tiles > 0) {
+    uint32_t* gh = a.hist + (size_t)u * kHistBins;
+    for (int i = threadIdx.x; i < kHistBins; i += blockDim.x)
+      if (const uint32_t c = hist[i]) atomicAdd(&gh[i], c);
+  }
 }
 
 // Block-wide exclusive prefix sum of one value per thread (1024 threads).
@@ -802,6 +915,7 @@ spec_status_t launch_topk_select(const AttnArgs& aa, int d, int dtype, int top_k
                                  int32_t* sel_idx, const TopkPlan& plan, void* ws,
                                  hipStream_t stream) {
   TopkArgs a;
+  memset(&a, 0, sizeof(a));
   a.q = aa.q;
   a.k = aa.k;
   a.kv_len = aa.kv_len;
@@ -828,8 +942,11 @@ spec_status_t launch_topk_select(const AttnArgs& aa, int d, int dtype, int top_k
   }
   const dim3 grid(units * tiles), block(256);
   if (dtype == SPEC_BF16) {
-    if (d == 64) hipLaunchKernelGGL((topk_score_kernel<64, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((topk_score_kernel<128, true>), grid, block, 0, stream, a);
+    // about one streaming workgroup per CU
+    a.splits = std::max(1, device_cu_count() / units);
+    const dim3 rgrid(units * a.splits), rblock(kRingWaves * 64);
+    if (d == 64) hipLaunchKernelGGL((topk_score_ring_kernel<64>), rgrid, rblock, 0, stream, a);
+    else hipLaunchKernelGGL((topk_score_ring_kernel<128>), rgrid, rblock, 0, stream, a);
   } else {
     if (d == 64) hipLaunchKernelGGL((topk_score_kernel<64, false>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((topk_score_kernel<128, false>), grid, block, 0, stream, a);

@@ -151,3 +151,19 @@ def test_topk_longer_than_the_selection_bitmask():
     rs, ro, rl = _ref(c, 512)
     assert np.array_equal(sel, rs)
     assert_attention_close(out, lse, ro, rl, np.ones(1, np.int32), W.BF16, "topk long")
+
+
+@pytest.mark.parametrize("dt", [W.BF16, W.F32])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("j1,j2", [(37, 201), (250, 3)])
+def test_score_products_are_rounded_before_the_sum(dt, d, j1, j2):
+    """Two keys whose order flips if a product is fused into its sum (see
+    the oracle's pin of the same case): top-1 must be j2, top-2 both."""
+    from test_oracle_topk import _rounding_case
+    q, k = _rounding_case(d, 300, j1, j2)
+    c = W.small_attn(31, 1, 2, 1, d, 1, (300,), dt)
+    c.q, c.k = W.Stored.from_f32(q, dt), W.Stored.from_f32(k, dt)
+    for K, want in ((1, [j2]), (2, sorted([j1, j2]))):
+        sel, _, _ = _run(c, K)
+        assert sel[0, 0].tolist() == want
+        assert np.array_equal(sel, _ref(c, K)[0])

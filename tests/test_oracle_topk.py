@@ -98,3 +98,33 @@ def test_topk_attention_only_reads_selected_rows():
     v[0, 0, mask] = 1e9
     _, o2, _ = oracle.topk_attention(c.q.values, c.k.values, v, c.kv_len, 1, 8, c.scale)
     assert np.array_equal(o, o2)
+
+
+def _rounding_case(d: int = 8, L: int = 6, j1: int = 1, j2: int = 4):
+    """Queries whose group sum needs 51 bits and two keys whose ranking
+    depends on each product being rounded before it is added.
+
+    qbar = (1, 1 + 2^-50, 2^-50 + 2^-58, 0, ...).  Key j1 = (-(1 + 2^-7),
+    1 + 2^-7, 0, ...): the product (1 + 2^-50)(1 + 2^-7) = 1 + 2^-7 + 2^-50
+    + 2^-57 rounds to 1 + 2^-7 + 2^-50 (2^-57 is below half an ulp of 1), so
+    the chain gives exactly 2^-50.  Key j2 = (0, 0, 1, 0, ...) scores
+    2^-50 + 2^-58.  A fused multiply-add would keep the 2^-57 and rank j1
+    first.  Every other key is zero (score 0)."""
+    q = np.zeros((1, 1, 2, d), np.float32)
+    q[0, 0, 0, :3] = [1.0, 1.0, 2.0 ** -50]
+    q[0, 0, 1, :3] = [0.0, 2.0 ** -50, 2.0 ** -58]
+    k = np.zeros((1, 1, L, d), np.float32)
+    k[0, 0, j1, :2] = [-(1 + 2.0 ** -7), 1 + 2.0 ** -7]
+    k[0, 0, j2, 2] = 1.0
+    return q, k
+
+
+def test_score_products_are_rounded_before_the_sum():
+    q, k = _rounding_case()
+    sc = oracle.topk_scores(q, k, np.array([6]), 1)[0][0]
+    assert sc[1] == 2.0 ** -50
+    assert sc[4] == 2.0 ** -50 + 2.0 ** -58
+    fused = 2.0 ** -50 + 2.0 ** -57          # the same chain with the j1 product unrounded
+    assert fused > sc[4] > sc[1]
+    assert oracle.topk_select(q, k, np.array([6]), 1, 1)[0, 0].tolist() == [4]
+    assert oracle.topk_select(q, k, np.array([6]), 1, 2)[0, 0].tolist() == [1, 4]
