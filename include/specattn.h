@@ -334,8 +334,9 @@ spec_status_t spec_accept(const void* logits, int32_t dtype, int32_t batch, int3
                           int32_t* target_tok, int32_t* accept_len, int32_t* next_tok,
                           void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Human-readable name of a status code (static string, never NULL). */
-const char* spec_status_str(spec_status_t status);
+/* Human-readable name of a status code (static string, never NULL).  Takes
+ * any int: a value that is no spec_status_t gives "unknown spec_status_t". */
+const char* spec_status_str(int32_t status);
 
 /*
  * spec_commit -- the bookkeeping that follows acceptance, on the device, so a

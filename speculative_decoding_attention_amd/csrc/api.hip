@@ -139,7 +139,7 @@ int32_t spec_abi_version(void) { return SPEC_ABI_VERSION; }
 
 int32_t spec_set_debug(int32_t on) { return set_debug(on); }
 
-const char* spec_status_str(spec_status_t status) {
+const char* spec_status_str(int32_t status) {
   switch (status) {
     case SPEC_OK: return "SPEC_OK";
     case SPEC_ERR_NULL: return "SPEC_ERR_NULL: a required pointer is NULL";

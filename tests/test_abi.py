@@ -14,6 +14,9 @@ HEADER = os.path.join(ROOT, "include", "specattn.h")
 @pytest.fixture(scope="module")
 def L():
     from speculative_decoding_attention_amd import _binding, build
+    other = os.environ.get("SPECATTN_TEST_LIB")   # e.g. the host-sanitizer build
+    if other:
+        return _binding.load_library(other)
     if not os.path.exists(_binding.LIB_PATH):
         build.build_library()
     return _binding.load_library()
