@@ -6,8 +6,8 @@
 // 64-bit key (see below) and stores it to its own slot (no atomics:
 // device-scope atomics on shared words serialise and cost tens of
 // microseconds at batch 64).
-// accept_finish_kernel: one workgroup per sequence takes the maximum over
-// each row's slots, turns it into the target token and counts the matching
+// accept_finish_kernel: one wave per sequence takes the maximum over each
+// row's slots, turns it into the target token and counts the matching
 // prefix.
 #include <algorithm>
 
@@ -124,50 +124,51 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_scan_kernel(AcceptArgs 
   }
 }
 
-// One workgroup per sequence: row r's target token is the maximum over its
-// chunk slots (every slot load in flight at once, reduced in LDS); wave 0
-// then takes rows 64 at a time, one per lane, and finds the first mismatch
-// with a ballot.
-__global__ __launch_bounds__(kAcceptThreads) void accept_finish_kernel(AcceptArgs a) {
-  constexpr int kRows = 64;                 // rows reduced per round
+// One wave per sequence: row r's target token is the maximum over its chunk
+// slots (every slot load in flight at once, reduced in LDS), and a lane per
+// row finds the first mismatch with a ballot, 64 rows per round.  The draft
+// tokens go out with the slot loads and gamma is a scalar load, so the
+// sequence pays one round trip to memory before its stores.
+__global__ __launch_bounds__(64) void accept_finish_kernel(AcceptArgs a) {
+  constexpr int kRows = 64;                 // rows reduced per round (one per lane)
   __shared__ unsigned long long rmax[kRows];
-  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
-  const int gam = a.gamma ? min(max(a.gamma[b], 0), a.n_max - 1) : a.n_max - 1;
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const int gam = a.gamma ? min(max(ld_uniform(a.gamma, b), 0), a.n_max - 1) : a.n_max - 1;
   int n = -1, nxt = 0;
   for (int r0 = 0; r0 < a.n_max; r0 += kRows) {
     const int rows = min(kRows, a.n_max - r0);
-    if (tid < kRows) rmax[tid] = 0ull;
+    const int r = r0 + lane;
+    // draft token of row r (index clamped; only rows below gamma use it)
+    const int dr = (a.n_max > 1) ? a.draft[(size_t)b * (a.n_max - 1) + min(r, a.n_max - 2)] : -1;
+    rmax[lane] = 0ull;
     __syncthreads();
     const int total = rows * a.chunks;
     const unsigned long long* src = a.best + ((size_t)b * a.n_max + r0) * a.chunks;
-    for (int i0 = 0; i0 < total; i0 += kAcceptThreads * 8) {
+    for (int i0 = 0; i0 < total; i0 += kRows * 8) {
       unsigned long long v[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = src[min(i0 + k * kAcceptThreads + tid, total - 1)];
+      for (int k = 0; k < 8; ++k) v[k] = src[min(i0 + k * kRows + lane, total - 1)];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const int i = i0 + k * kAcceptThreads + tid;
+        const int i = i0 + k * kRows + lane;
         if (i < total) atomicMax(&rmax[i / a.chunks], v[k]);   // LDS atomic
       }
     }
     __syncthreads();
-    if (tid < 64) {
-      const int r = r0 + lane;
-      const unsigned long long k = (lane < rows) ? rmax[lane] : 0ull;
-      const int d = (r < gam) ? a.draft[(size_t)b * (a.n_max - 1) + min(r, a.n_max - 2)] : -1;
-      const int t = (r <= gam) ? (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull)) : -1;
-      if (r < a.n_max) a.target_tok[(size_t)b * a.n_max + r] = t;
-      const unsigned long long stop =
-          __builtin_amdgcn_ballot_w64(r < a.n_max && r <= gam && (r == gam || d != t));
-      if (n < 0 && stop) {
-        const int first = __ffsll((long long)stop) - 1;
-        n = r0 + first;
-        nxt = __shfl(t, first);
-      }
+    const unsigned long long k = (lane < rows) ? rmax[lane] : 0ull;
+    const int d = (r < gam) ? dr : -1;
+    const int t = (r <= gam) ? (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull)) : -1;
+    if (r < a.n_max) a.target_tok[(size_t)b * a.n_max + r] = t;
+    const unsigned long long stop =
+        __builtin_amdgcn_ballot_w64(r < a.n_max && r <= gam && (r == gam || d != t));
+    if (n < 0 && stop) {
+      const int first = __ffsll((long long)stop) - 1;
+      n = r0 + first;
+      nxt = __shfl(t, first);
     }
-    __syncthreads();
+    __syncthreads();   // every lane has read rmax before the next round clears it
   }
-  if (tid == 0) {
+  if (lane == 0) {
     a.accept_len[b] = n;
     a.next_tok[b] = nxt;
   }
@@ -277,8 +278,7 @@ spec_status_t launch_accept(const void* logits, int dtype, int batch, int n_max,
   else
     hipLaunchKernelGGL((accept_scan_kernel<false, 2>), grid, block, 0, stream, a);
   if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
-  hipLaunchKernelGGL(accept_finish_kernel, dim3((unsigned)batch), dim3(kAcceptThreads), 0, stream,
-                     a);
+  hipLaunchKernelGGL(accept_finish_kernel, dim3((unsigned)batch), dim3(64), 0, stream, a);
   return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 
