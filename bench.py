@@ -23,7 +23,6 @@ bandwidth; draft steps/s is 1 / (HSR + text-anchored attention time).
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -36,8 +35,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix peak
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_c2_traffic.json")
-KERNEL_SOURCES = ["attention.hip", "common.h", "internal.h", "api.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def _parse():
@@ -50,7 +48,7 @@ def _parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--only", choices=["verify", "vata", "hsr", "topk", "accept", "step", "c5",
-                                       "std", "verify_b16", "c3", "c4", "lvis"],
+                                       "std", "verify_b16", "c3", "c4", "lvis", "ceiling"],
                     default=None, help="time one part only (for counter passes)")
     return ap.parse_args()
 
@@ -142,14 +140,6 @@ def break_even_alpha(gamma, draft_us, verify_us, dense_us):
         else:
             hi = mid
     return round(hi, 4)
-
-
-def _source_hash(names):
-    h = hashlib.sha256()
-    for n in names:
-        with open(os.path.join(ROOT, "speculative_decoding_attention_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
 
 
 def main():
@@ -262,6 +252,47 @@ def main():
         t1.synchronize()
         return t0.elapsed_time(t1) / replays   # ms per replay
 
+    def main_kernel_us(call, count, warm=2):
+        """Mean duration (us) of the main kernel of call(i), i = 0, 1, ...:
+        the library's measurement hook records two events on the call's
+        stream right before and right after that kernel (eager calls)."""
+        pairs = []
+        for i in range(warm + count):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            # a spin ahead of the call keeps the GPU busy while the host
+            # enqueues the events and the call's launches, so the kernel
+            # starts right after `before` instead of waiting for the host
+            torch.cuda._sleep(200_000)
+            S.mark_main_kernel(e0, e1)
+            call(i)
+            pairs.append((e0, e1))
+        torch.cuda.synchronize()
+        return float(np.mean([a_.elapsed_time(b_) for a_, b_ in pairs[warm:]])) * 1e3
+
+    from speculative_decoding_attention_amd.profiling import source_hash
+    src_hash = source_hash()
+    counters = {}
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("source_hash") == src_hash:
+            counters = tr.get("kernels", {})
+
+    def roofline(key, bound, work, us):
+        """Roofline of one main kernel: `work` algorithmic bytes (hbm) or
+        flops (mfma) per launch over its measured duration; `traffic` is the
+        HBM bytes per launch the FETCH_SIZE / WRITE_SIZE counters saw for
+        this kernel with the same sources (None otherwise)."""
+        if bound == "hbm":
+            ach, peak, unit = work / (us * 1e-6) / 1e9, HBM_PEAK_GBS, "GB/s"
+        else:
+            ach, peak, unit = work / (us * 1e-6) / 1e12, MFMA_BF16_PEAK_TFS, "TFLOP/s"
+        c = counters.get(key)
+        return {"bound": bound, "achieved": round(ach, 1), "peak": peak, "unit": unit,
+                "frac": round(ach / peak, 4), "traffic": c["bytes"] if c else None,
+                "kernel": key, "kernel_us": round(us, 3), "work_per_launch": work}
+
     result = {}
     parts = {}
     only = args.only
@@ -329,6 +360,9 @@ def main():
         g = capture(lambda: [S.spec_vata_attn(kv, qc, tic, tlc, scale=scale, out=oc, lse=lc,
                                               workspace=wsp["vata"]) for kv in kvc])
         vata_c5_us = time_graph(g, max(4, args.reps // 4)) * 1e3 / len(kvc)
+        vata_main_us = main_kernel_us(lambda i: S.spec_vata_attn(kvc[i % 2], qc, tic, tlc,
+                                                                 scale=scale, out=oc, lse=lc,
+                                                                 workspace=wsp["vata"]), 6)
         del kvc
         lgc = [torch.randn(Bc, n, V, device=dev).to(torch.bfloat16) for _ in range(3)]
         drc = torch.randint(0, V, (Bc, gamma), dtype=torch.int32, device=dev)
@@ -338,6 +372,11 @@ def main():
         g = capture(lambda: [S.spec_accept(lg, drc, target_tok=tc, accept_len=ac, next_tok=nc,
                                            workspace=wsp["accept"]) for lg in lgc])
         acc_c5_us = time_graph(g, max(4, args.reps // 4)) * 1e3 / len(lgc)
+        acc_main_us = main_kernel_us(lambda i: S.spec_accept(lgc[i % len(lgc)], drc, target_tok=tc,
+                                                             accept_len=ac, next_tok=nc,
+                                                             workspace=wsp["accept"]), 6)
+        hsr_main_us = main_kernel_us(lambda i: S.spec_hsr_fuse(ec, hc, ws[i % R], y=yc,
+                                                               workspace=wsp["hsr"]), 10)
         del lgc
         hsr_c5_flops = 2 * Mc * D * 2 * D
         vata_c5_bytes = 2 * Bc * Hkv * Lt * d * 2 + Bc * Lt * 4 + 2 * Bc * gamma * Hq * d * 2
@@ -349,7 +388,14 @@ def main():
               "vata_us": round(vata_c5_us, 2),
               "vata_gbs": round(vata_c5_bytes / (vata_c5_us * 1e-6) / 1e9, 1),
               "accept_us": round(acc_c5_us, 2),
-              "accept_gbs": round(acc_c5_bytes / (acc_c5_us * 1e-6) / 1e9, 1)}
+              "accept_gbs": round(acc_c5_bytes / (acc_c5_us * 1e-6) / 1e9, 1),
+              # main kernels: the GEMM (no split-K reduce), the split pass of
+              # the text-anchored attention (its K/V/Q reads), the logits scan
+              "roofline": roofline("c5_hsr_gemm", "mfma", hsr_c5_flops, hsr_main_us),
+              "vata_roofline": roofline("c5_vata_split", "hbm",
+                                        2 * Bc * Hkv * Lt * d * 2 + Bc * Lt * 4 +
+                                        Bc * gamma * Hq * d * 2, vata_main_us),
+              "accept_roofline": roofline("c5_accept_scan", "hbm", acc_c5_bytes, acc_main_us)}
 
     # ---- the draft step as the video grows: text-anchored attention (one
     # row, 512 text positions in the same layout) and the draft step (HSR row
@@ -425,6 +471,8 @@ def main():
             call_select()
             torch.cuda.synchronize()
             sel_t = time_graph(capture(call_select), max(4, args.reps // 4)) * 1e3
+            if kk == cs.top_k:
+                pass_us[0] = main_kernel_us(lambda i: call_select(), 4, warm=1)
             keep_tail = keep_s.clone()
             # the kept positions at or past the tail start are the tail's own
             keep_tail[keep_tail >= L - tail] = -1
@@ -447,6 +495,7 @@ def main():
             bytes_ = 2 * kept_ * d * 2 + kept_ * 4 + 2 * Hq * d * 2 + Hq * 4
             return sel_t, sp_t, kept_, bytes_
 
+        pass_us = [None]
         per_k = {kk: select_and_sparse(kk) for kk in (512, 1024, 2048, 4096)}
         select_us, sparse_us, kept, sparse_bytes = per_k[cs.top_k]
         # work of the selection: both passes form every visible score
@@ -502,10 +551,9 @@ def main():
                                           "probability alpha; attention of one layer only",
                             "rows": model},
                "io_model_by_top_k": kl_rows}
-        sel_tfs = sel_flops / (select_us * 1e-6) / 1e12
-        std["roofline"] = {"bound": "mfma", "achieved": round(sel_tfs, 1),
-                           "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-                           "frac": round(sel_tfs / MFMA_BF16_PEAK_TFS, 4), "traffic": None}
+        # main kernel: the first of the two score passes (each forms every
+        # visible score once: 2 d flops per (row, key) pair and head)
+        std["roofline"] = roofline("std_score_pass", "mfma", sel_flops // 2, pass_us[0])
         if not args.no_cpu_baseline and only is None:
             # the oracle on one of the four KV heads (about 2 s), scaled to the layer
             import oracle
@@ -541,10 +589,14 @@ def main():
         g = capture(lambda: [S.spec_verify_attn(kv, qb, scale=scale, out=ob, lse=lb,
                                                 workspace=wsp["verify"]) for kv in kvb])
         vb_us = time_graph(g, max(4, args.reps // 4)) * 1e3 / len(kvb)
+        vb_main_us = main_kernel_us(lambda i: S.spec_verify_attn(kvb[i % 2], qb, scale=scale, out=ob,
+                                                                 lse=lb, workspace=wsp["verify"]), 6)
         vb_bytes = 2 * Bb * Hkv * Lb * d * 2 + 2 * Bb * n * Hq * d * 2 + Bb * n * Hq * 4
         vb_gbs = vb_bytes / (vb_us * 1e-6) / 1e9
         vb16 = {"workload": "verify-16x32768", "us": round(vb_us, 1), "gbs": round(vb_gbs, 1),
-                "frac": round(vb_gbs / HBM_PEAK_GBS, 4)}
+                "frac": round(vb_gbs / HBM_PEAK_GBS, 4),
+                "roofline": roofline("b16_verify_split", "hbm",
+                                     2 * Bb * Hkv * Lb * d * 2 + Bb * n * Hq * d * 2, vb_main_us)}
         del kvb
 
     # ---- ragged paged batch (16 sequences, 16-token pages in a random pool
@@ -589,6 +641,7 @@ def main():
         # a call this short is timed four to a graph, so that the host's graph
         # launch is not on the clock
         t_vat = time_graph(capture(lambda: [c3_vata(kv3) for _ in range(4)]), reps3) * 1e3 / 4
+        ver3_main_us = main_kernel_us(lambda i: c3_verify(kv3), 4)
         del kp, vp, kv3
         mx = int(lay.L.max())
         kc = torch.randn(B3, Hkv, mx, d, device=dev).mul_(0.5).to(torch.bfloat16)
@@ -608,7 +661,12 @@ def main():
               "verify_paged_frac": round(ver3_bytes / (t_ver * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
               "verify_contiguous_us": round(t_verc, 1),
               "verify_contiguous_gbs": gbs(ver3_bytes, t_verc),
-              "vata_paged_us": round(t_vat, 1), "vata_paged_gbs": gbs(vat3_bytes, t_vat)}
+              "vata_paged_us": round(t_vat, 1), "vata_paged_gbs": gbs(vat3_bytes, t_vat),
+              # main kernel: the paged split pass (K/V of every position, the
+              # valid query rows, the page table)
+              "roofline": roofline("c3_verify_paged_split", "hbm",
+                                   2 * int(lay.L.sum()) * Hkv * d * 2 + nq3 * Hq * d * 2 +
+                                   4 * int(((lay.L + ps - 1) // ps).sum()), ver3_main_us)}
 
     # ---- top-K draft and dense verification, 4 sequences of 32,768 keys
     # (28,672 visual + 4,096 text), K = 2048: the per-step top-K (score all
@@ -636,6 +694,11 @@ def main():
         reps4 = max(4, args.reps // 4)
         t4v = time_graph(capture(f_ver), reps4) * 1e3 / len(kv4)
         t4k = time_graph(capture(f_top), reps4) * 1e3 / len(kv4)
+        v4_main_us = main_kernel_us(lambda i: S.spec_verify_attn(kv4[i % 2], q4, scale=scale, out=o4,
+                                                                 lse=l4, workspace=ws4["verify"]), 6)
+        k4_main_us = main_kernel_us(lambda i: S.spec_topk_attn(kv4[i % 2], q4l, K4, scale=scale,
+                                                               sel_idx=s4, out=o4k, lse=l4k,
+                                                               workspace=ws4["topk"]), 6)
         del kv4
         v4_bytes = 2 * B4 * Hkv * L4 * d * 2 + 2 * B4 * n * Hq * d * 2 + B4 * n * Hq * 4
         k4_bytes = B4 * Hkv * L4 * d * 2 + 2 * B4 * Hkv * K4 * d * 2 + B4 * Hkv * K4 * 4 + \
@@ -644,7 +707,42 @@ def main():
               "verify_gbs": round(v4_bytes / (t4v * 1e-6) / 1e9, 1),
               "verify_frac": round(v4_bytes / (t4v * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
               "topk_us": round(t4k, 1), "topk_gbs": round(k4_bytes / (t4k * 1e-6) / 1e9, 1),
-              "topk_to_dense_bytes": round(k4_bytes / v4_bytes, 3)}
+              "topk_to_dense_bytes": round(k4_bytes / v4_bytes, 3),
+              # main kernels: the score pass of the top-K call (every key row
+              # and the query heads) and the split pass of the verification
+              "roofline": roofline("c4_topk_score", "hbm",
+                                   B4 * Hkv * L4 * d * 2 + B4 * Hq * d * 2, k4_main_us),
+              "verify_roofline": roofline("c4_verify_split", "hbm",
+                                          2 * B4 * Hkv * L4 * d * 2 + B4 * n * Hq * d * 2,
+                                          v4_main_us)}
+
+    # ---- plain streaming at the sizes above: the library's read probe (a
+    # bare read: 16-byte loads, eight in flight per thread, 1024 workgroups)
+    # and, for context, the vendor's device copy (reads and writes every
+    # byte), each over enough rotated copies that 520 MB or more stream per
+    # pass.  The probe's time for a 52 MB verification call's bytes bounds
+    # what any kernel can reach at that size.
+    ceiling = None
+    if only in (None, "ceiling"):
+        ceiling = []
+        sink = torch.empty(S.SPEC_READ_PROBE_SINK_WORDS, dtype=torch.int32, device=dev)
+        for nbytes in (52_335_264, 268_435_456, 1_073_741_824):
+            cn = max(2, -(-520_000_000 // nbytes))
+            xs = [torch.ones(nbytes // 2, dtype=torch.bfloat16, device=dev) for _ in range(cn)]
+            ys = [torch.empty_like(xs[0]) for _ in range(cn)]
+            for j in range(cn):
+                S.read_probe(xs[j], sink)
+                ys[j].copy_(xs[j])
+            torch.cuda.synchronize()
+            t_rd = time_graph(capture(lambda: [S.read_probe(x_, sink) for x_ in xs]), 6) * 1e3 / cn
+            t_cpy = time_graph(capture(lambda: [y_.copy_(x_) for x_, y_ in zip(xs, ys)]),
+                               6) * 1e3 / cn
+            ceiling.append({"bytes": nbytes, "copies": cn,
+                            "read_us": round(t_rd, 2),
+                            "read_gbs": round(nbytes / (t_rd * 1e-6) / 1e9, 1),
+                            "copy_us": round(t_cpy, 2),
+                            "copy_moved_gbs": round(2 * nbytes / (t_cpy * 1e-6) / 1e9, 1)})
+            del xs, ys
 
     # ---- algorithmic bytes (per call)
     kv_bytes = 2 * L * Hkv * d * 2
@@ -685,20 +783,15 @@ def main():
     if not args.no_cpu_baseline and only is None:
         cpu = cpu_verify_baseline(oracle, attn, Hkv, scale, verify_bytes, args.cpu_seconds)
 
-    traffic = None
-    src_hash = _source_hash(KERNEL_SOURCES)
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
-            tr = json.load(f)
-        if tr.get("source_hash") == src_hash:
-            traffic = tr.get("bytes_per_launch")
-
     verify_us = parts.get("verify_us")
     value = verify_bytes / (verify_us * 1e-6) / 1e9 if verify_us else None
     roof = None
     if verify_us:
-        roof = {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(value / HBM_PEAK_GBS, 4), "traffic": traffic}
+        # the call's dominant kernel: the split pass (the K/V rows and the
+        # query block it must read; the partials it writes for the merge are
+        # this implementation's traffic, not the method's)
+        split_us = main_kernel_us(lambda i: call_verify(i % R), 4 * R)
+        roof = roofline("c2_verify_split", "hbm", kv_bytes + n * Hq * d * 2, split_us)
     draft_us = parts.get("draft_step_us")
     result = {
         "metric": "verify-attn HBM GB/s (% peak) + draft steps/s at 25k visual tokens, 1 GPU",
@@ -733,6 +826,7 @@ def main():
         "verify_batch16": vb16,
         "ragged_paged": c3,
         "topk_batch4": c4,
+        "read_ceiling": ceiling,
         "verify_max_abs_err_vs_oracle": err,
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -84,7 +84,7 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 3
+#define SPEC_ABI_VERSION 4
 
 /* Bytes at the start of every non-empty workspace that must be zero before
  * its first use (see Workspace above). */
@@ -373,6 +373,29 @@ int32_t spec_abi_version(void);
 /* Debug mode on (non-zero) or off for this process; returns the previous
  * setting.  The initial setting comes from SPEC_DEBUG in the environment. */
 int32_t spec_set_debug(int32_t on);
+
+/* Measurement hook, for timing one kernel without a profiler.  The calling
+ * thread's next call of an entry point records `before` on that call's
+ * stream right before its main kernel is launched and `after` right after
+ * it, then forgets both (they are not recorded again).  Main kernel: the
+ * split attention pass of verify, text-anchored, sparse and the no-allocation
+ * verify; the score pass of spec_topk_attn; the GEMM (or the one-row stream
+ * pass) of spec_hsr_fuse; the vocabulary scan of spec_accept; the first
+ * score pass of spec_std_select.  A call that fails before its launches
+ * leaves both set.  Both NULL clears them; exactly one NULL is
+ * SPEC_ERR_NULL.  The events belong to the caller and must outlive the
+ * call; nothing the call computes depends on them. */
+spec_status_t spec_mark_main_kernel(hipEvent_t before, hipEvent_t after);
+
+/* Measurement aid: a plain streaming read of `bytes` bytes at device
+ * address `p` (16-byte aligned, `bytes` a non-zero multiple of 16), the
+ * reference rate for the library's HBM-bound kernels at a given size.
+ * SPEC_READ_PROBE_SINK_WORDS workgroups each write one 32-bit word to
+ * `sink` (device, that many words): the XOR of the 32-bit words they read,
+ * so the XOR of all sink words is the XOR of the buffer's words.  Errors:
+ * SPEC_ERR_NULL, SPEC_ERR_SHAPE (alignment or size), SPEC_ERR_HIP. */
+#define SPEC_READ_PROBE_SINK_WORDS 1024
+spec_status_t spec_read_probe(const void* p, size_t bytes, uint32_t* sink, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libspecattn.so")
 
 SPEC_F32 = 0
 SPEC_BF16 = 1
-SPEC_ABI_VERSION = 3
+SPEC_ABI_VERSION = 4
 SPEC_WS_SYNC_BYTES = 1 << 20
 SPEC_NOALLOC_SCRATCH_BYTES = 32 << 20
 
@@ -65,6 +65,8 @@ SIGNATURES = {
     "spec_commit": (_I, [_I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _I, _P]),
     "spec_abi_version": (_I, []),
     "spec_set_debug": (_I, [_I]),
+    "spec_mark_main_kernel": (_I, [_P, _P]),
+    "spec_read_probe": (_I, [_P, ctypes.c_size_t, _P, _P]),
 }
 
 
@@ -475,6 +477,39 @@ def spec_status_str(status: int) -> str:
 
 def spec_abi_version() -> int:
     return int(lib().spec_abi_version())
+
+
+def mark_main_kernel(before: "torch.cuda.Event", after: "torch.cuda.Event") -> None:
+    """Measurement hook: the calling thread's next library call records
+    `before` right before its main kernel and `after` right after it, on the
+    call's stream (see spec_mark_main_kernel).  Both events must be timing
+    events of the call's device; each is recorded once here first so that
+    its handle exists."""
+    for e in (before, after):
+        e.record()
+    _check("spec_mark_main_kernel",
+           lib().spec_mark_main_kernel(ctypes.c_void_p(before.cuda_event),
+                                       ctypes.c_void_p(after.cuda_event)))
+
+
+SPEC_READ_PROBE_SINK_WORDS = 1024
+
+
+def read_probe(x: torch.Tensor, sink: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Measurement aid: one plain streaming read of x's bytes (contiguous,
+    16-byte aligned, a multiple of 16 bytes); returns the sink of
+    SPEC_READ_PROBE_SINK_WORDS int32 words whose XOR is the XOR of x's
+    32-bit words."""
+    if not (x.is_cuda and x.is_contiguous()):
+        raise ValueError("x must be a contiguous device tensor")
+    if sink is None:
+        sink = torch.empty(SPEC_READ_PROBE_SINK_WORDS, dtype=torch.int32, device=x.device)
+    _dev(sink, "sink", torch.int32)
+    if sink.numel() < SPEC_READ_PROBE_SINK_WORDS:
+        raise ValueError("sink too small")
+    _check("spec_read_probe", lib().spec_read_probe(x.data_ptr(), x.numel() * x.element_size(),
+                                                    sink.data_ptr(), _stream(x.device)))
+    return sink
 
 
 def spec_set_debug(on: bool) -> bool:

@@ -24,7 +24,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libspecattn.so")
 LIB_HOSTSAN = os.path.join(PKG, "libspecattn_hostsan.so")
-SOURCES = ["api.hip", "attention.hip", "topk.hip", "hsr.hip", "accept.hip", "validate.hip", "std.hip"]
+SOURCES = ["api.hip", "attention.hip", "topk.hip", "hsr.hip", "accept.hip", "validate.hip", "std.hip",
+           "stream.hip"]
 ARCH = os.environ.get("SPEC_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

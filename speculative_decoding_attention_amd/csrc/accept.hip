@@ -269,6 +269,7 @@ spec_status_t launch_accept(const void* logits, int dtype, int batch, int n_max,
   a.chunks = p.chunks;
   a.vec = p.vec;
   const dim3 grid((unsigned)batch * n_max * p.chunks), block(kAcceptThreads);
+  mark_before_main(stream);
   if (bf16 && p.loads == 8)
     hipLaunchKernelGGL((accept_scan_kernel<true, 8>), grid, block, 0, stream, a);
   else if (bf16)
@@ -277,6 +278,7 @@ spec_status_t launch_accept(const void* logits, int dtype, int batch, int n_max,
     hipLaunchKernelGGL((accept_scan_kernel<false, 8>), grid, block, 0, stream, a);
   else
     hipLaunchKernelGGL((accept_scan_kernel<false, 2>), grid, block, 0, stream, a);
+  mark_after_main(stream);
   if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
   hipLaunchKernelGGL(accept_finish_kernel, dim3((unsigned)batch), dim3(64), 0, stream, a);
   return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;

@@ -133,11 +133,45 @@ spec_status_t check_ws(size_t need, const void* ws, size_t ws_bytes) {
 
 }  // namespace
 
+namespace spec {
+namespace {
+// events of the measurement hook, per calling thread (one-shot)
+thread_local hipEvent_t g_mark_before = nullptr;
+thread_local hipEvent_t g_mark_after = nullptr;
+void set_main_marks(hipEvent_t before, hipEvent_t after) {
+  g_mark_before = before;
+  g_mark_after = after;
+}
+}  // namespace
+
+void mark_before_main(hipStream_t s) {
+  if (g_mark_before) hipEventRecord(g_mark_before, s);
+  g_mark_before = nullptr;
+}
+
+void mark_after_main(hipStream_t s) {
+  if (g_mark_after) hipEventRecord(g_mark_after, s);
+  g_mark_after = nullptr;
+}
+}  // namespace spec
+
 extern "C" {
 
 int32_t spec_abi_version(void) { return SPEC_ABI_VERSION; }
 
 int32_t spec_set_debug(int32_t on) { return set_debug(on); }
+
+spec_status_t spec_read_probe(const void* p, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (!p || !sink) return SPEC_ERR_NULL;
+  if (bytes == 0 || bytes % 16 || reinterpret_cast<uintptr_t>(p) % 16) return SPEC_ERR_SHAPE;
+  return launch_read_probe(p, bytes, sink, stream);
+}
+
+spec_status_t spec_mark_main_kernel(hipEvent_t before, hipEvent_t after) {
+  if ((before == nullptr) != (after == nullptr)) return SPEC_ERR_NULL;
+  set_main_marks(before, after);
+  return SPEC_OK;
+}
 
 const char* spec_status_str(int32_t status) {
   switch (status) {

@@ -1536,12 +1536,14 @@ spec_status_t launch_attention(AttnArgs a, int d, int dtype, const AttnPlan& pla
   }
   if (grid == 0) return SPEC_OK;
   hipError_t e;
+  mark_before_main(stream);
   if (plan.gather)
     e = (d == 64) ? launch_d<64, true>(a, dtype, grid, stream)
                   : launch_d<128, true>(a, dtype, grid, stream);
   else
     e = (d == 64) ? launch_d<64, false>(a, dtype, grid, stream)
                   : launch_d<128, false>(a, dtype, grid, stream);
+  mark_after_main(stream);
   if (e != hipSuccess) return SPEC_ERR_HIP;
   if (plan.S > 1) {
     // balanced plans merge few partials per unit when the capacity plan has

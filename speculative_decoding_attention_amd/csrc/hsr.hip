@@ -398,7 +398,9 @@ spec_status_t launch_hsr(const void* e, const void* h, const void* w, int m, int
     constexpr int RW = 1, U = 14, WV = 8;   // one W row per wave (measured best)
     const dim3 grid((d_model + WV * RW - 1) / (WV * RW)), block(WV * 64);
     static_assert(kGemvMaxM == 1, "one X row in LDS");
+    mark_before_main(stream);
     hipLaunchKernelGGL((hsr_gemv_kernel<1, RW, U, WV>), grid, block, (size_t)4 * d_model, stream, a);
+    mark_after_main(stream);
     return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
   }
   const HsrPlan p = plan_hsr(m, d_model);
@@ -418,6 +420,7 @@ spec_status_t launch_hsr(const void* e, const void* h, const void* w, int m, int
   const dim3 grid(p.tiles_m * p.tiles_n * p.S), block(128 * kGemmWN);
   constexpr int N64 = 64 / (16 * kGemmWN), N128 = 128 / (16 * kGemmWN);
   constexpr int N256 = 256 / (16 * kGemmWN);
+  mark_before_main(stream);
   switch (p.MT * 1000 + p.BN) {
     case 4256: hipLaunchKernelGGL((hsr_mfma_kernel<4, N256, kGemmWN>), grid, block, 0, stream, a); break;
     case 2064: hipLaunchKernelGGL((hsr_mfma_kernel<2, N64, kGemmWN>), grid, block, 0, stream, a); break;
@@ -425,6 +428,7 @@ spec_status_t launch_hsr(const void* e, const void* h, const void* w, int m, int
     case 4064: hipLaunchKernelGGL((hsr_mfma_kernel<4, N64, kGemmWN>), grid, block, 0, stream, a); break;
     default: hipLaunchKernelGGL((hsr_mfma_kernel<4, N128, kGemmWN>), grid, block, 0, stream, a); break;
   }
+  mark_after_main(stream);
   if (p.S > 1) {
     if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
     const size_t n4 = (size_t)m * d_model / 4;

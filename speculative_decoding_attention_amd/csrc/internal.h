@@ -202,6 +202,15 @@ struct ValidateArgs {
 };
 bool debug_enabled();
 int set_debug(int on);
+
+// Measurement hook (spec_mark_main_kernel): the events the calling thread
+// set are recorded on the stream right before and right after the main
+// kernel of its next call, then forgotten.  No effect on any result.
+void mark_before_main(hipStream_t s);
+void mark_after_main(hipStream_t s);
+
+// stream.hip: the plain streaming read behind spec_read_probe
+spec_status_t launch_read_probe(const void* p, size_t bytes, uint32_t* sink, hipStream_t stream);
 // Runs the checks on `stream` and waits for them: SPEC_ERR_SHAPE when a
 // value is out of range.
 spec_status_t validate(const ValidateArgs& v, hipStream_t stream);

@@ -941,6 +941,7 @@ spec_status_t launch_topk_select(const AttnArgs& aa, int d, int dtype, int top_k
     if (st != SPEC_OK) return st;
   }
   const dim3 grid(units * tiles), block(256);
+  mark_before_main(stream);
   if (dtype == SPEC_BF16) {
     // about one streaming workgroup per CU
     a.splits = std::max(1, device_cu_count() / units);
@@ -951,6 +952,7 @@ spec_status_t launch_topk_select(const AttnArgs& aa, int d, int dtype, int top_k
     if (d == 64) hipLaunchKernelGGL((topk_score_kernel<64, false>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((topk_score_kernel<128, false>), grid, block, 0, stream, a);
   }
+  mark_after_main(stream);
   if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
   hipLaunchKernelGGL(topk_select_kernel, dim3(units), dim3(1024), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;

@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.spec_abi_version() == 3
+    assert L.spec_abi_version() == 4
     for code in range(7):
         s = L.spec_status_str(code).decode()
         assert s.startswith("SPEC_")
@@ -230,3 +230,17 @@ def test_commit_rejections(L):
                          None) == 2
     assert L.spec_commit(1, 6, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, FAKE, 0, None, None, 0,
                          None) == 2                      # tokens with no capacity
+
+
+def test_mark_main_kernel_takes_both_events_or_neither(L):
+    assert L.spec_mark_main_kernel(None, None) == 0
+    assert L.spec_mark_main_kernel(FAKE, None) == 1      # SPEC_ERR_NULL, nothing kept
+    assert L.spec_mark_main_kernel(None, FAKE) == 1
+    assert L.spec_mark_main_kernel(None, None) == 0
+
+
+def test_read_probe_rejects_bad_arguments(L):
+    assert L.spec_read_probe(None, 16, FAKE, None) == 1          # SPEC_ERR_NULL
+    assert L.spec_read_probe(FAKE, 16, None, None) == 1
+    for p, n in ((FAKE, 0), (FAKE, 15), (FAKE, 24), (FAKE + 8, 16)):
+        assert L.spec_read_probe(p, n, FAKE, None) == 2          # SPEC_ERR_SHAPE
