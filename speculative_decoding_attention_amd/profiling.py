@@ -24,7 +24,8 @@ failure:
 profiles/traffic.md and one kernel-duration table per section.  For every
 configuration the main kernel is the kernel of the given name whose mean
 duration in that section's trace is largest; its counters are then taken
-from the dispatches with the same name and grid.  traffic.json carries the
+from the dispatches with the same name and grid (the slow mode only, when
+two calls of a section share both).  traffic.json carries the
 hash of the kernel sources, and bench.py reports ``traffic`` only while the
 sources still hash the same.
 
@@ -51,8 +52,10 @@ CSRC = os.path.join(ROOT, "speculative_decoding_attention_amd", "csrc")
 KERNEL_SOURCES = ["api.hip", "attention.hip", "topk.hip", "hsr.hip", "accept.hip", "std.hip",
                   "stream.hip", "common.h", "internal.h"]
 
-BENCH_ARGS = ["--no-cpu-baseline", "--steps", "2", "--warmup", "1", "--reps", "4", "--rotate", "2"]
-TRACE_SECTIONS = ["verify", "c3", "c4", "c5", "std", "verify_b16", "ceiling"]
+# the bench's own rotation (enough input copies that every pass streams from
+# HBM, not from the 256 MiB MALL), fewer replays
+BENCH_ARGS = ["--no-cpu-baseline", "--steps", "2", "--warmup", "1", "--reps", "4"]
+TRACE_SECTIONS = ["step", "verify", "c3", "c4", "c5", "std", "verify_b16", "ceiling"]
 BYTE_SECTIONS = ["verify", "c3", "c4", "c5", "std", "verify_b16"]
 MFMA_SECTIONS = ["c5", "std"]
 COPY_CMD = ("import torch; x = torch.ones(128 * 1024 * 1024, dtype=torch.bfloat16, device='cuda'); "
@@ -137,21 +140,59 @@ def _short(name: str) -> str:
 
 
 def _durations(out: str, sec: str):
-    """{(kernel, grid): [duration us]} of one section's trace."""
+    """{(kernel, grid): [duration us, in dispatch order]} of one section's trace."""
     d = defaultdict(list)
-    for r in _rows(os.path.join(out, f"trace_{sec}", "**", "*kernel_trace.csv")):
+    rows = sorted(_rows(os.path.join(out, f"trace_{sec}", "**", "*kernel_trace.csv")),
+                  key=lambda r: int(r["Start_Timestamp"]))
+    for r in rows:
         grid = int(r.get("Grid_Size_X") or r.get("Grid_Size") or 0)
         d[(r["Kernel_Name"], grid)].append((int(r["End_Timestamp"]) -
                                             int(r["Start_Timestamp"])) / 1000.0)
     return d
 
 
+def _mode_labels(durs, gap: float = 2.0):
+    """Mode of each dispatch of one (kernel, grid) group, durations given in
+    dispatch order.  Two calls of a section can launch the same kernel with
+    the same grid (the paged verification and the paged text-anchored
+    attention of the ragged batch, the read probe at three sizes).  The
+    dispatches are cut into runs wherever one takes over `gap` times as long
+    as the one before it, or under 1/gap of it; runs whose medians are
+    within `gap` of each other form one mode.  Returns (labels, modes),
+    label 0 the fastest mode."""
+    runs = []
+    for i, t in enumerate(durs):
+        if runs and max(t, durs[i - 1]) <= gap * min(t, durs[i - 1]):
+            runs[-1].append(i)
+        else:
+            runs.append([i])
+    med = [statistics.median(durs[j] for j in r) for r in runs]
+    order = sorted(range(len(runs)), key=lambda k: med[k])
+    labels, mode = [0] * len(durs), 0
+    for pos, k in enumerate(order):
+        if pos > 0 and med[k] > gap * med[order[pos - 1]]:
+            mode += 1
+        for j in runs[k]:
+            labels[j] = mode
+    return labels, mode + 1
+
+
+def _slowest(durs):
+    """The durations of the slowest mode (all of them when there is one)."""
+    labels, n = _mode_labels(durs)
+    return [t for t, m in zip(durs, labels) if m == n - 1]
+
+
 def _counter(out: str, run: str, name: str, grid: int, counter: str):
-    vals = [float(r["Counter_Value"])
-            for r in _rows(os.path.join(out, run, "**", "*counter_collection.csv"))
-            if r["Kernel_Name"] == name and int(r.get("Grid_Size") or 0) == grid and
-            r["Counter_Name"] == counter]
-    return statistics.mean(vals) if vals else None
+    """Mean of one counter over the slowest mode of a kernel's dispatches."""
+    rows = sorted((r for r in _rows(os.path.join(out, run, "**", "*counter_collection.csv"))
+                   if r["Kernel_Name"] == name and int(r.get("Grid_Size") or 0) == grid and
+                   r["Counter_Name"] == counter), key=lambda r: int(r["Start_Timestamp"]))
+    if not rows:
+        return None
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0 for r in rows]
+    labels, n = _mode_labels(durs)
+    return statistics.mean(float(r["Counter_Value"]) for r, m in zip(rows, labels) if m == n - 1)
 
 
 def summarize(out: str, dest: str = PROFILES) -> dict:
@@ -166,11 +207,11 @@ def summarize(out: str, dest: str = PROFILES) -> dict:
     for key, (sec, test, bound) in MAIN_KERNELS.items():
         if sec not in traces:
             traces[sec] = _durations(out, sec)
-        cands = [(statistics.mean(v), k) for k, v in traces[sec].items() if test(k[0])]
+        cands = [(statistics.mean(_slowest(v)), k) for k, v in traces[sec].items() if test(k[0])]
         if not cands:
             continue
         _, (name, grid) = max(cands)
-        dur = traces[sec][(name, grid)]
+        dur = _slowest(traces[sec][(name, grid)])
         e = {"section": sec, "kernel": _short(name), "grid": grid, "bound": bound,
              "dispatches": len(dur), "mean_us": round(statistics.mean(dur), 3),
              "median_us": round(statistics.median(dur), 3)}
@@ -192,8 +233,10 @@ def summarize(out: str, dest: str = PROFILES) -> dict:
     with open(os.path.join(dest, "traffic.json"), "w") as f:
         json.dump(doc, f, indent=1)
     _write_traffic_md(doc, dest)
-    for sec, d in traces.items():
-        _write_trace_md(sec, d, dest)
+    for sec in TRACE_SECTIONS:
+        d = traces.get(sec) or _durations(out, sec)
+        if d:
+            _write_trace_md(sec, d, dest)
     return doc
 
 
@@ -240,7 +283,8 @@ def _write_traffic_md(doc: dict, dest: str) -> None:
         "",
         "Main kernel of a configuration: the kernel of that name with the largest mean duration in "
         "the section's kernel trace; counters are the mean over its dispatches with the same "
-        "grid.  Durations here are from the kernel trace (profiling adds little to a kernel's "
+        "grid (when one section launches the same kernel and grid for two calls of very "
+        "different length, only the slow call's dispatches count).  Durations here are from the kernel trace (profiling adds little to a kernel's "
         "own duration; bench.py measures the same kernels live with the library's event hook).",
         "",
         "| configuration | kernel (grid) | mean us | fetched bytes | written bytes | traffic "
@@ -264,13 +308,20 @@ def _write_trace_md(sec: str, d: dict, dest: str) -> None:
              f"rocprofv3 --kernel-trace --stats --output-format csv -d OUT/trace_{sec} -o t -- "
              + _bench_cmd(sec), "```", "",
              "Per kernel and grid size (threads); durations in microseconds.  The counts include "
-             "the eager warm-up calls before graph capture.", "",
+             "the eager warm-up calls before graph capture.  A kernel launched with the same "
+             "grid by two calls of very different length is split into duration modes (runs of "
+             "dispatches cut where one takes over twice or under half as long as the one before; "
+             "runs with medians within a factor of two form a mode).", "",
              "| kernel | grid | dispatches | mean | median | min | max |",
              "|---|---|---|---|---|---|---|"]
     rows = sorted(d.items(), key=lambda kv: -sum(kv[1]))
     for (name, grid), v in rows[:24]:
-        lines.append(f"| `{_short(name)}` | {grid} | {len(v)} | {statistics.mean(v):.2f} | "
-                     f"{statistics.median(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+        labels, n = _mode_labels(v)
+        modes = [[t for t, lab in zip(v, labels) if lab == i] for i in range(n)]
+        for i, m in enumerate(modes):
+            tag = f" (mode {i + 1} of {n})" if n > 1 else ""
+            lines.append(f"| `{_short(name)}`{tag} | {grid} | {len(m)} | {statistics.mean(m):.2f} | "
+                         f"{statistics.median(m):.2f} | {min(m):.2f} | {max(m):.2f} |")
     lines.append("")
     with open(os.path.join(dest, f"kernels_{sec}.md"), "w") as f:
         f.write("\n".join(lines))

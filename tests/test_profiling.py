@@ -8,7 +8,8 @@ import os
 from speculative_decoding_attention_amd import profiling as P
 
 TRACE_COLS = ["Kernel_Name", "Grid_Size", "Start_Timestamp", "End_Timestamp"]
-PMC_COLS = ["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
+PMC_COLS = ["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value", "Start_Timestamp",
+            "End_Timestamp"]
 
 
 def _write(path, cols, rows):
@@ -30,14 +31,14 @@ def test_summary_picks_the_slowest_named_kernel_and_scales_counters(tmp_path):
         (small, 4096, 0, 9000), (merge, 172032, 0, 4000)])
     copy = "__amd_rocclr_copyBuffer"
     _write(f"{out}/FETCH_SIZE_copy/x/p_counter_collection.csv", PMC_COLS,
-           [(copy, 131072, "FETCH_SIZE", 131072.0)] * 3)           # half the bytes counted
+           [(copy, 131072, "FETCH_SIZE", 131072.0, 0, 9000)] * 3)   # half the bytes counted
     _write(f"{out}/WRITE_SIZE_copy/x/p_counter_collection.csv", PMC_COLS,
-           [(copy, 131072, "WRITE_SIZE", 262144.0)] * 3)
+           [(copy, 131072, "WRITE_SIZE", 262144.0, 0, 9000)] * 3)
     _write(f"{out}/FETCH_SIZE_verify/x/p_counter_collection.csv", PMC_COLS, [
-        (split, 126976, "FETCH_SIZE", 25000.0), (split, 126976, "FETCH_SIZE", 27000.0),
-        (small, 4096, "FETCH_SIZE", 999.0)])
+        (split, 126976, "FETCH_SIZE", 25000.0, 0, 15000), (split, 126976, "FETCH_SIZE", 27000.0, 0, 16000),
+        (small, 4096, "FETCH_SIZE", 999.0, 0, 9000)])
     _write(f"{out}/WRITE_SIZE_verify/x/p_counter_collection.csv", PMC_COLS, [
-        (split, 126976, "WRITE_SIZE", 5000.0)])
+        (split, 126976, "WRITE_SIZE", 5000.0, 0, 15000)])
     dest = str(tmp_path / "profiles")
     doc = P.summarize(out, dest)
     e = doc["kernels"]["c2_verify_split"]
@@ -50,3 +51,25 @@ def test_summary_picks_the_slowest_named_kernel_and_scales_counters(tmp_path):
     assert on_disk["source_hash"] == P.source_hash()
     assert os.path.exists(os.path.join(dest, "traffic.md"))
     assert os.path.exists(os.path.join(dest, "kernels_verify.md"))
+
+
+def test_a_kernel_shared_by_two_calls_counts_the_slow_one(tmp_path):
+    """The paged verification and the paged text-anchored attention launch
+    the same kernel with the same grid; the main kernel is the slow call."""
+    out = str(tmp_path / "raw")
+    k = "void spec::(anonymous namespace)::attn_bf16_pipe_kernel<4, true>(spec::AttnArgs)"
+    _write(f"{out}/trace_c3/x/t_kernel_trace.csv", TRACE_COLS,
+           [(k, 131072, 0, 130000), (k, 131072, 0, 14000), (k, 131072, 0, 136000),
+            (k, 131072, 0, 13000)])
+    copy = "__amd_rocclr_copyBuffer"
+    for ctr, v in (("FETCH_SIZE", 262144.0), ("WRITE_SIZE", 262144.0)):
+        _write(f"{out}/{ctr}_copy/x/p_counter_collection.csv", PMC_COLS,
+               [(copy, 131072, ctr, v, 0, 1000)])
+    cols = PMC_COLS
+    _write(f"{out}/FETCH_SIZE_c3/x/p_counter_collection.csv", cols,
+           [(k, 131072, "FETCH_SIZE", 550000.0, 0, 140000), (k, 131072, "FETCH_SIZE", 9000.0, 0, 15000)])
+    _write(f"{out}/WRITE_SIZE_c3/x/p_counter_collection.csv", cols,
+           [(k, 131072, "WRITE_SIZE", 12000.0, 0, 140000), (k, 131072, "WRITE_SIZE", 900.0, 0, 15000)])
+    e = P.summarize(out, str(tmp_path / "profiles"))["kernels"]["c3_verify_paged_split"]
+    assert e["dispatches"] == 2 and e["mean_us"] == 133.0
+    assert e["fetch_bytes"] == 550000 * 1024 and e["write_bytes"] == 12000 * 1024
