@@ -383,7 +383,8 @@ int32_t spec_set_debug(int32_t on);
  * pass) of spec_hsr_fuse; the vocabulary scan of spec_accept; the first
  * score pass of spec_std_select.  A call that fails before its launches
  * leaves both set.  Both NULL clears them; exactly one NULL is
- * SPEC_ERR_NULL.  The events belong to the caller and must outlive the
+ * SPEC_ERR_NULL.  Meant for calls made outside stream capture (the records
+ * are plain ones).  The events belong to the caller and must outlive the
  * call; nothing the call computes depends on them. */
 spec_status_t spec_mark_main_kernel(hipEvent_t before, hipEvent_t after);
 

@@ -482,11 +482,12 @@ def spec_abi_version() -> int:
 def mark_main_kernel(before: "torch.cuda.Event", after: "torch.cuda.Event") -> None:
     """Measurement hook: the calling thread's next library call records
     `before` right before its main kernel and `after` right after it, on the
-    call's stream (see spec_mark_main_kernel).  Both events must be timing
-    events of the call's device; each is recorded once here first so that
-    its handle exists."""
+    call's stream (see spec_mark_main_kernel), for calls made outside
+    stream capture.  Both must be timing events of the call's device; an
+    event that has no handle yet is recorded once first to make one."""
     for e in (before, after):
-        e.record()
+        if not e.cuda_event:
+            e.record()
     _check("spec_mark_main_kernel",
            lib().spec_mark_main_kernel(ctypes.c_void_p(before.cuda_event),
                                        ctypes.c_void_p(after.cuda_event)))

@@ -63,3 +63,4 @@ def test_read_probe_reads_every_word_once(words):
     want = np.bitwise_xor.reduce(x.numpy().view(np.uint32))
     got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
     assert got == want
+
