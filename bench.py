@@ -269,7 +269,7 @@ def main():
             # a spin ahead of the call keeps the GPU busy while the host
             # enqueues the events and the call's launches, so the kernel
             # starts right after `before` instead of waiting for the host
-            torch.cuda._sleep(200_000)
+            torch.cuda._sleep(1_000_000)
             S.mark_main_kernel(e0, e1)
             call(i)
             pairs.append((e0, e1))
