@@ -102,6 +102,7 @@ __global__ __launch_bounds__(128 * WN, 1) void hsr_mfma_kernel(HsrArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, q4 = lane >> 4;
   const int wm = wave & 1, wn = wave >> 1;
+  const int kswap = (wave >> 2) & 1;              // waves are dealt to SIMDs round-robin
   // work item = (tile_n, split, tile_m): the tile_m neighbours share the W
   // slab of the same K range and land on the same XCD
   const int item = xcd_remap(blockIdx.x, gridDim.x);
@@ -136,7 +137,11 @@ __global__ __launch_bounds__(128 * WN, 1) void hsr_mfma_kernel(HsrArgs a) {
     gemm_src<MT, NT, WN>(a, m0, n0, refill ? ks0 + t + C::NS - 1 : ks0, wave, lane, src);
     const unsigned char* st = ring + (t % C::NS) * C::STAGE;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {            // two 32-wide k steps of the MFMA
+    for (int kh = 0; kh < 2; ++kh) {            // two 32-wide k steps of the MFMA
+      // the two waves that share a SIMD (w and w + 4) take the halves in
+      // opposite orders, so one's LDS reads overlap the other's MFMAs
+      // instead of both waiting for the same reads after the barrier
+      const int kk = kh ^ kswap;
       const int c = 4 * kk + q4;
       bf16x8_t af[MT], bfr[NT];
 #pragma unroll
@@ -156,7 +161,7 @@ __global__ __launch_bounds__(128 * WN, 1) void hsr_mfma_kernel(HsrArgs a) {
         for (int nt = 0; nt < NT; ++nt)
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bfr[nt], acc[mt][nt], 0, 0, 0);
       if (refill) {
-        if (kk == 0) gemm_dma<MT, NT, WN, 0, C::PER_WAVE / 2>(src, nxt, wave);
+        if (kh == 0) gemm_dma<MT, NT, WN, 0, C::PER_WAVE / 2>(src, nxt, wave);
         else gemm_dma<MT, NT, WN, C::PER_WAVE / 2, C::PER_WAVE>(src, nxt, wave);
       }
     }
