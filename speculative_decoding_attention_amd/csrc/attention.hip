@@ -131,23 +131,26 @@ __device__ __forceinline__ DynSplit dyn_split(const AttnArgs& a, int key, bool b
   int t = (a.mode == 1) ? a.slot_len[bb] : a.kv_len[bb];
   if (a.mode == 2) t = min(t, a.slot_stride);
   const int T = (lane < a.B) ? max(t, 0) : 0;
+  // 32-bit arithmetic in the search (lengths and split lengths stay below
+  // 2^30; only the batch's total needs 64 bits): a 64-bit division is a long
+  // emulated sequence, and every split and merge workgroup runs this search
   long tot = T;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o);
   tot *= a.Hkv;
-  long lo = (tot + a.dyn_groups - 1) / a.dyn_groups;
-  lo = max(((lo + kTK - 1) / kTK) * kTK, (long)(kTK * kNW));
-  long hi = max((long)a.chunk, lo);                  // the capacity plan's length fits
+  int lo = (int)((tot + a.dyn_groups - 1) / a.dyn_groups);
+  lo = max(((lo + kTK - 1) / kTK) * kTK, kTK * kNW);
+  int hi = max(a.chunk, lo);                         // the capacity plan's length fits
   while (lo < hi) {                                  // multiples of kTK: smallest that fits
-    const long mid = ((lo + hi) / 2 / kTK) * kTK;
-    const long c = max(mid, lo);
-    long n = (lane < a.B) ? max(1L, ((long)T + c - 1) / c) : 0;
+    const int mid = ((lo + hi) / 2 / kTK) * kTK;
+    const int c = max(mid, lo);
+    int n = (lane < a.B) ? max(1, (int)(((unsigned)T + (unsigned)c - 1u) / (unsigned)c)) : 0;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) n += __shfl_xor(n, o);
     if (n * a.Hkv <= a.dyn_groups) hi = c;
     else lo = c + kTK;
   }
-  const int ch = (int)hi;
+  const int ch = hi;
   const int Sb = (lane < a.B) ? max(1, (T + ch - 1) / ch) : 0;
   const int cnt = Sb * a.Hkv;
   const int incl = wave_inclusive_scan(cnt, lane);
