@@ -649,9 +649,10 @@ def main():
         reps3 = max(4, args.reps // 4)
         c3_verify(kv3), c3_vata(kv3)
         torch.cuda.synchronize()
-        t_ver = time_graph(capture(lambda: c3_verify(kv3)), reps3) * 1e3
-        # a call this short is timed four to a graph, so that the host's graph
-        # launch is not on the clock
+        # four calls to a graph, so that the graph's own launch is not on the
+        # clock of one call (the 565 MB pool is twice the 256 MiB MALL, so a
+        # call still streams it from HBM)
+        t_ver = time_graph(capture(lambda: [c3_verify(kv3) for _ in range(4)]), reps3) * 1e3 / 4
         t_vat = time_graph(capture(lambda: [c3_vata(kv3) for _ in range(4)]), reps3) * 1e3 / 4
         ver3_main_us = main_kernel_us(lambda i: c3_verify(kv3), 4)
         del kp, vp, kv3
@@ -661,7 +662,7 @@ def main():
         kvc3 = S.KVCache(kc, vc, L3)
         c3_verify(kvc3)
         torch.cuda.synchronize()
-        t_verc = time_graph(capture(lambda: c3_verify(kvc3)), reps3) * 1e3
+        t_verc = time_graph(capture(lambda: [c3_verify(kvc3) for _ in range(4)]), reps3) * 1e3 / 4
         del kc, vc, kvc3
         nq3 = int((lay.gamma + 1).sum())
         ver3_bytes = 2 * int(lay.L.sum()) * Hkv * d * 2 + 2 * nq3 * Hq * d * 2 + nq3 * Hq * 4
