@@ -259,13 +259,13 @@ def main():
         """Mean duration (us) of the main kernel of call(i), i = 0, 1, ...:
         the library's measurement hook records two events on the call's
         stream right before and right after that kernel (eager calls).  The
-        pair also spans the command processor's handling of the two event
-        packets and the kernel's dispatch, about 2-3 us beyond the kernel's
-        own execution as a kernel trace sees it."""
+        events are timing-only HIP events (no system-scope fence when
+        recorded), so the pair spans the kernel's dispatch and the command
+        processor's handling of the two event packets, but no cache
+        write-back or invalidation."""
         pairs = []
         for i in range(warm + count):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
+            e0, e1 = S.TimingEvent(), S.TimingEvent()
             # a spin ahead of the call keeps the GPU busy while the host
             # enqueues the events and the call's launches, so the kernel
             # starts right after `before` instead of waiting for the host
@@ -274,7 +274,7 @@ def main():
             call(i)
             pairs.append((e0, e1))
         torch.cuda.synchronize()
-        return float(np.mean([a_.elapsed_time(b_) for a_, b_ in pairs[warm:]])) * 1e3
+        return float(np.mean([a_.elapsed_ms(b_) for a_, b_ in pairs[warm:]])) * 1e3
 
     from speculative_decoding_attention_amd.profiling import source_hash
     src_hash = source_hash()
@@ -357,6 +357,15 @@ def main():
         g = capture(lambda: [S.spec_hsr_fuse(ec, hc, ws[r], y=yc, workspace=wsp["hsr"])
                              for r in range(R)])
         hsr_c5_us = time_graph(g, max(4, args.reps // 4)) * 1e3 / R
+        # context, not the library's path: the vendor GEMM (hipBLASLt through
+        # torch) at the same shape and weight layout, on the rows already
+        # concatenated, over the same rotated weight copies
+        xcat = torch.cat([ec, hc], 1)
+        torch.nn.functional.linear(xcat, ws[0])      # the library's own set-up, eager
+        torch.cuda.synchronize()
+        g = capture(lambda: [torch.nn.functional.linear(xcat, ws[r]) for r in range(R)])
+        vendor_c5_us = time_graph(g, max(4, args.reps // 4)) * 1e3 / R
+        del xcat, g
         kvc = []
         for _ in range(2):      # two copies: 2 x 268 MB, more than the 256 MiB cache
             kc = torch.randn(Bc, Hkv, Lt, d, device=dev).mul_(0.5).to(torch.bfloat16)
@@ -395,6 +404,7 @@ def main():
               "hsr_tflops": round(hsr_c5_flops / (hsr_c5_us * 1e-6) / 1e12, 1),
               "hsr_mfma_frac": round(hsr_c5_flops / (hsr_c5_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFS,
                                      4),
+              "vendor_gemm_us": round(vendor_c5_us, 2),
               "vata_us": round(vata_c5_us, 2),
               "vata_gbs": round(vata_c5_bytes / (vata_c5_us * 1e-6) / 1e9, 1),
               "accept_us": round(acc_c5_us, 2),

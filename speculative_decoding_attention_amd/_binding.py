@@ -479,18 +479,69 @@ def spec_abi_version() -> int:
     return int(lib().spec_abi_version())
 
 
-def mark_main_kernel(before: "torch.cuda.Event", after: "torch.cuda.Event") -> None:
+class TimingEvent:
+    """A HIP event for timing only, created with hipEventDisableSystemFence:
+    recording it makes no system-scope cache write-back and invalidation, so
+    a pair of them around one kernel measures little beyond the kernel.
+    elapsed_ms() is valid once the stream has passed both records (after a
+    device synchronisation); the event itself orders no memory."""
+
+    _FLAGS = 0x20000000          # hipEventDisableSystemFence
+    _hip: Optional[ctypes.CDLL] = None
+
+    @classmethod
+    def _rt(cls) -> ctypes.CDLL:
+        if cls._hip is None:
+            torch.cuda.init()
+            # the runtime the process already has (torch's, and the library's)
+            h = ctypes.CDLL("libamdhip64.so.7")
+            h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                              ctypes.c_void_p]
+            h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            for f in (h.hipEventCreateWithFlags, h.hipEventElapsedTime, h.hipEventDestroy):
+                f.restype = ctypes.c_int
+            cls._hip = h
+        return cls._hip
+
+    def __init__(self):
+        ev = ctypes.c_void_p()
+        rc = self._rt().hipEventCreateWithFlags(ctypes.byref(ev), self._FLAGS)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        self.handle = ev.value
+
+    def elapsed_ms(self, end: "TimingEvent") -> float:
+        ms = ctypes.c_float()
+        rc = self._rt().hipEventElapsedTime(ctypes.byref(ms), self.handle, end.handle)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def __del__(self):
+        if getattr(self, "handle", None) and TimingEvent._hip is not None:
+            TimingEvent._hip.hipEventDestroy(self.handle)
+            self.handle = None
+
+
+def _event_handle(e) -> int:
+    if isinstance(e, TimingEvent):
+        return e.handle
+    if not e.cuda_event:
+        e.record()
+    return e.cuda_event
+
+
+def mark_main_kernel(before, after) -> None:
     """Measurement hook: the calling thread's next library call records
     `before` right before its main kernel and `after` right after it, on the
     call's stream (see spec_mark_main_kernel), for calls made outside
-    stream capture.  Both must be timing events of the call's device; an
-    event that has no handle yet is recorded once first to make one."""
-    for e in (before, after):
-        if not e.cuda_event:
-            e.record()
+    stream capture.  Both are timing events of the call's device: TimingEvent
+    or torch.cuda.Event (one that has no handle yet is recorded once first to
+    make one)."""
+    hb, ha = _event_handle(before), _event_handle(after)
     _check("spec_mark_main_kernel",
-           lib().spec_mark_main_kernel(ctypes.c_void_p(before.cuda_event),
-                                       ctypes.c_void_p(after.cuda_event)))
+           lib().spec_mark_main_kernel(ctypes.c_void_p(hb), ctypes.c_void_p(ha)))
 
 
 SPEC_READ_PROBE_SINK_WORDS = 1024

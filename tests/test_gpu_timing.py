@@ -53,6 +53,30 @@ def test_every_entry_point_marks_its_main_kernel(which):
     assert e0.elapsed_time(e1) > 0.0
 
 
+def test_timing_events_bracket_the_main_kernel_inside_the_call():
+    """Fence-free timing events work with the hook as torch's events do: the
+    main kernel's span is positive and inside the whole call's span."""
+    import speculative_decoding_attention_amd as S
+    c = W.small_attn(3, 2, 28, 4, 128, 6, (9000, 4100), W.BF16)
+    kv, q = kvcache(c), dev(c.q)
+    ref_o, ref_l = S.spec_verify_attn(kv, q, scale=c.scale, out_dtype=torch.float32)
+    e0, e1, t0, t1 = (S.TimingEvent() for _ in range(4))
+    S.mark_main_kernel(t0, t1)                 # the whole call: two hooks in a row
+    S.mark_main_kernel(e0, e1)                 # the later hook wins
+    o, l = S.spec_verify_attn(kv, q, scale=c.scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
+    assert e0.elapsed_ms(e1) > 0.0
+    # bracket a whole call with a pair recorded through torch's own events
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    S.mark_main_kernel(t0, t1)
+    w0.record()
+    S.spec_verify_attn(kv, q, scale=c.scale, out_dtype=torch.float32)
+    w1.record()
+    torch.cuda.synchronize()
+    assert 0.0 < t0.elapsed_ms(t1) <= w0.elapsed_time(w1)
+
+
 @pytest.mark.parametrize("words", [4, 4 * 12345, 13_107_200])
 def test_read_probe_reads_every_word_once(words):
     import speculative_decoding_attention_amd as S
