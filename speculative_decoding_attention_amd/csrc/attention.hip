@@ -111,13 +111,24 @@ struct DynSplit {
   bool valid;       // false: this workgroup has no split
 };
 
-__device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+// Inclusive prefix sum over the wave's 64 lanes by DPP: Hillis-Steele shifts
+// within each 16-lane row, then the gfx9 row broadcasts of lane 15 (into
+// rows 1 and 3) and lane 31 (into rows 2 and 3).  Each step is one VALU
+// instruction; a shuffle step would be an LDS permute with its round trip.
+// Every lane of the wave must be active.
+__device__ __forceinline__ uint32_t wave_prefix_sum(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return x;
+}
+
+// The wave's sum, uniform (lane 63 of the prefix sum).
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_prefix_sum(x), 63);
 }
 
 // by_unit: `key` is a unit index (the merge's query).  Otherwise `key` is
@@ -132,48 +143,46 @@ __device__ __forceinline__ DynSplit dyn_split(const AttnArgs& a, int key, bool b
   if (a.mode == 2) t = min(t, a.slot_stride);
   const int T = (lane < a.B) ? max(t, 0) : 0;
   // 32-bit arithmetic in the search (lengths and split lengths stay below
-  // 2^30; only the batch's total needs 64 bits): a 64-bit division is a long
-  // emulated sequence, and every split and merge workgroup runs this search
-  long tot = T;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o);
-  tot *= a.Hkv;
+  // 2^30; only the batch's total needs 64 bits, here from two 32-bit sums):
+  // a 64-bit division is a long emulated sequence, and every split and merge
+  // workgroup runs this search.  Its sums over the batch are DPP sums.
+  const long tot = ((long)wave_sum((uint32_t)T >> 6) * 64 + (long)wave_sum((uint32_t)T & 63u)) *
+                   a.Hkv;
   int lo = (int)((tot + a.dyn_groups - 1) / a.dyn_groups);
   lo = max(((lo + kTK - 1) / kTK) * kTK, kTK * kNW);
   int hi = max(a.chunk, lo);                         // the capacity plan's length fits
   while (lo < hi) {                                  // multiples of kTK: smallest that fits
     const int mid = ((lo + hi) / 2 / kTK) * kTK;
     const int c = max(mid, lo);
-    int n = (lane < a.B) ? max(1, (int)(((unsigned)T + (unsigned)c - 1u) / (unsigned)c)) : 0;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) n += __shfl_xor(n, o);
+    const int n = (int)wave_sum(
+        (lane < a.B) ? max(1u, ((unsigned)T + (unsigned)c - 1u) / (unsigned)c) : 0u);
     if (n * a.Hkv <= a.dyn_groups) hi = c;
     else lo = c + kTK;
   }
   const int ch = hi;
   const int Sb = (lane < a.B) ? max(1, (T + ch - 1) / ch) : 0;
   const int cnt = Sb * a.Hkv;
-  const int incl = wave_inclusive_scan(cnt, lane);
+  const int incl = (int)wave_prefix_sum((uint32_t)cnt);
   DynSplit d;
   d.ch = ch;
   if (by_unit) {
-    d.b = key / a.Hkv;
+    d.b = __builtin_amdgcn_readfirstlane(key / a.Hkv);   // a unit of the workgroup
     d.g = key - d.b * a.Hkv;
     d.s = 0;
-    d.S = __shfl(Sb, d.b);
-    d.first = __shfl(incl - cnt, d.b) + d.g * d.S;
+    d.S = __builtin_amdgcn_readlane(Sb, d.b);
+    d.first = __builtin_amdgcn_readlane(incl - cnt, d.b) + d.g * d.S;
     d.w = d.first;
     d.valid = true;
     return d;
   }
-  const int total = __shfl(incl, 63);                // lanes past B add nothing
+  const int total = __builtin_amdgcn_readlane(incl, 63);   // lanes past B add nothing
   d.valid = key < total;
   key = d.valid ? xcd_remap(key, total) : 0;
   d.w = key;
   const uint64_t m = __builtin_amdgcn_ballot_w64(lane < a.B && key < incl);
   d.b = d.valid ? __ffsll((long long)m) - 1 : 0;
-  d.S = max(1, __shfl(Sb, d.b));
-  const int off = key - __shfl(incl - cnt, d.b);
+  d.S = max(1, __builtin_amdgcn_readlane(Sb, d.b));
+  const int off = key - __builtin_amdgcn_readlane(incl - cnt, d.b);
   d.g = off / d.S;
   d.s = off - d.g * d.S;
   d.first = key - d.s;

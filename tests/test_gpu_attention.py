@@ -121,6 +121,25 @@ def test_balanced_splits_of_very_uneven_lengths(page):
     assert_attention_close(out, lse, ro, rl, c.q_len, W.BF16, "uneven vata")
 
 
+@pytest.mark.parametrize("B,Hkv,lmax,page", [(64, 2, 1200, 0), (64, 2, 1200, 16),
+                                              (2, 4, 40000, 0), (47, 4, 3000, 0)])
+def test_balanced_plan_over_batch_sizes(B, Hkv, lmax, page):
+    """Balanced splits for a batch that gives every lane of the plan's
+    wave-wide sums a length (64 sequences, so lanes in all four 16-lane rows
+    count; two KV heads, so the capacity plan has two splits per unit and
+    the balanced plan applies), two very unequal sequences, and an odd
+    batch, each verified against the oracle (one or two query rows)."""
+    rng = np.random.default_rng(700 + B + page)
+    L = [int(x) for x in rng.integers(1, lmax + 1, size=B)]
+    if B == 2:
+        L = [lmax, 3]
+    ql = [min(2, x) for x in L]
+    c = W.small_attn(710 + B + page, B, 4 * Hkv, Hkv, 128, 2, tuple(L), W.BF16,
+                     page_size=page, q_len=ql)
+    out, lse, ro, rl = _verify_pair(c)
+    assert_attention_close(out, lse, ro, rl, c.q_len, W.BF16, f"balanced B={B} page={page}")
+
+
 def test_padded_query_rows_and_bf16_output():
     c = W.small_attn(11, 3, 8, 2, 128, 6, (900, 450, 1200), W.BF16, q_len=[6, 2, 4])
     out, lse, ro, rl = _verify_pair(c, out_dtype=torch.bfloat16)
