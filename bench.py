@@ -244,7 +244,11 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     def time_graph(g, replays):
-        g.replay()
+        # untimed replays first: the first passes over a freshly allocated
+        # pool run slower (the ragged paged batch: 142 against 120 us per
+        # call), a one-time cost that steady-state calls do not pay
+        for _ in range(max(1, replays // 2)):
+            g.replay()
         torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
