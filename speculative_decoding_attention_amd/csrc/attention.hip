@@ -111,26 +111,6 @@ struct DynSplit {
   bool valid;       // false: this workgroup has no split
 };
 
-// Inclusive prefix sum over the wave's 64 lanes by DPP: Hillis-Steele shifts
-// within each 16-lane row, then the gfx9 row broadcasts of lane 15 (into
-// rows 1 and 3) and lane 31 (into rows 2 and 3).  Each step is one VALU
-// instruction; a shuffle step would be an LDS permute with its round trip.
-// Every lane of the wave must be active.
-__device__ __forceinline__ uint32_t wave_prefix_sum(uint32_t x) {
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);   // row_shr:1
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);   // row_shr:2
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);   // row_shr:4
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);   // row_shr:8
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
-  return x;
-}
-
-// The wave's sum, uniform (lane 63 of the prefix sum).
-__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_readlane((int)wave_prefix_sum(x), 63);
-}
-
 // by_unit: `key` is a unit index (the merge's query).  Otherwise `key` is
 // the workgroup index: workgroups below the number of splits take one each,
 // through the XCD-aware order over exactly that many (the hardware deals

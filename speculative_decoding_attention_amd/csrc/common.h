@@ -73,6 +73,26 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) {
 
 // Butterfly reductions across lanes l ^ 16 and l ^ 32 (the four 16-lane
 // rows of a wave that hold the same MFMA output column).
+// Inclusive prefix sum over the wave's 64 lanes by DPP: Hillis-Steele shifts
+// within each 16-lane row, then the gfx9 row broadcasts of lane 15 (into
+// rows 1 and 3) and lane 31 (into rows 2 and 3).  Each step is one VALU
+// instruction; a shuffle step would be an LDS permute with its round trip.
+// Every lane of the wave must be active.
+__device__ __forceinline__ uint32_t wave_prefix_sum(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
+// The wave's sum, uniform (lane 63 of the prefix sum).
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_prefix_sum(x), 63);
+}
+
 __device__ __forceinline__ float max_across_rows(float x) {
   x = fmaxf(x, __shfl_xor(x, 16));
   x = fmaxf(x, __shfl_xor(x, 32));

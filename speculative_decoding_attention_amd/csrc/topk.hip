@@ -310,31 +310,22 @@ __global__ __launch_bounds__(kRingWaves * 64, 1) void topk_score_ring_kernel(Top
   }
 }
 
-// Block-wide exclusive prefix sum of one value per thread (1024 threads).
+// Block-wide exclusive prefix sum of one value per thread (at most 64
+// waves); every thread of the block calls it.
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum,
                                                          uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_prefix_sum(v);             // inclusive, within the wave
   if (lane == 63) wsum[wave] = x;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t run = 0;
-    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
-      const uint32_t t = wsum[w];
-      wsum[w] = run;
-      run += t;
-    }
-    *total = run;
-  }
-  __syncthreads();
-  const uint32_t r = wsum[wave] + x - v;
-  __syncthreads();
-  return r;
+  // every wave scans the waves' sums itself (one LDS read, one DPP scan)
+  const int nw = (int)(blockDim.x >> 6);
+  const uint32_t wp = wave_prefix_sum(lane < nw ? wsum[lane] : 0u);
+  const uint32_t before =
+      wave > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)wp, wave - 1) : 0u;
+  if (threadIdx.x == 0) *total = (uint32_t)__builtin_amdgcn_readlane((int)wp, 63);
+  __syncthreads();   // wsum is read by every wave before the next scan writes it
+  return before + x - v;
 }
 
 __device__ __forceinline__ bool cand_before(uint64_t ka, int ia, uint64_t kb, int ib) {
@@ -442,35 +433,39 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(TopkArgs a) {
 #pragma unroll
         for (int k = 0; k < kSelWords; ++k) kw[k] = w16[min(c0 + k * nt + tid, nw - 1)];
       }
+      // Branch-free unsigned arithmetic on the 16-bit keys (a compare per
+      // key would go through a scalar mask and a select, a VALU -> SALU ->
+      // VALU chain per key): a key's coarse bin (its top 12 bits) lies above
+      // bstar iff the key exceeds gt_key, and equals bstar iff key - eq_key
+      // is below 16; keys at or past L are masked once per word.
+      const uint32_t gt_key = (bstar << 4) | 15u, eq_key = bstar << 4;
       uint32_t cmask[kSelWords];
       uint32_t cnt = 0;
 #pragma unroll
       for (int k = 0; k < kSelWords; ++k) {
         const int c = c0 + k * nt + tid;
         const uint32_t wd[4] = {kw[k][0], kw[k][1], kw[k][2], kw[k][3]};
+        const int rem = L - c * 8;                     // keys of this word below L
+        const uint32_t vmask = rem >= 8 ? 0xFFu : (1u << max(rem, 0)) - 1u;
         uint32_t am = 0, cm = 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int j = c * 8 + e;
-          const uint32_t cb = ((wd[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) >> 4;
-          am |= (uint32_t)(j < L && cb > bstar) << e;
-          cm |= (uint32_t)(j < L && cb == bstar) << e;
+          const uint32_t key = (wd[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+          am |= ((gt_key - key) >> 31) << e;                  // key > gt_key
+          cm |= ((((key - eq_key) >> 4) - 1u) >> 31) << e;    // 0 <= key - eq_key < 16
         }
+        am &= vmask;
+        cm &= vmask;
         if (use_mask && c < nwm) selb[c] = (uint8_t)am;
         cmask[k] = cm;
         cnt += (uint32_t)__popc(cm);
       }
-      uint32_t incl = cnt;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(incl, o);
-        if (lane >= o) incl += y;
-      }
-      const uint32_t wtot = __shfl(incl, 63);
+      const uint32_t incl = wave_prefix_sum(cnt);
+      const uint32_t wtot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
       if (wtot) {
         uint32_t wbase = 0;
         if (lane == 0) wbase = atomicAdd(&s_ncand, wtot);
-        uint32_t pos = __shfl(wbase, 0) + incl - cnt;
+        uint32_t pos = (uint32_t)__builtin_amdgcn_readfirstlane((int)wbase) + incl - cnt;
 #pragma unroll
         for (int k = 0; k < kSelWords; ++k) {
           uint32_t cm = cmask[k];
@@ -511,7 +506,7 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(TopkArgs a) {
     if (wtotal) {
       uint32_t wbase = 0;
       if (lane == 0) wbase = atomicAdd(&s_ncand, wtotal);
-      wbase = __shfl(wbase, 0);
+      wbase = (uint32_t)__builtin_amdgcn_readfirstlane((int)wbase);
       const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
       for (int k = 0; k < kSelBatch; ++k) {
