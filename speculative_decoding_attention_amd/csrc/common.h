@@ -93,15 +93,27 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_readlane((int)wave_prefix_sum(x), 63);
 }
 
+// Across the four 16-lane rows of the wave (lanes l, l^16, l^32, l^48).  The
+// gfx950 row swaps exchange rows in the VALU (a shuffle would be an LDS
+// permute): after v_permlane16_swap of a value with itself, a lane's two
+// results are its own value and its partner row's, in some order; the same
+// holds for v_permlane32_swap one level up.  Combining the two is
+// commutative, so every lane gets what the xor-16-then-32 order gives.
 __device__ __forceinline__ float max_across_rows(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float sum_across_rows(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // ---------------------------------------------------------- LDS DMA ----
