@@ -117,10 +117,11 @@ def test_c1_accept_planted():
     assert n[0] == 2 and np.array_equal(t, rt) and nxt[0] == rnx[0]
 
 
+@pytest.mark.parametrize("B", [9, 16, 8])
 @pytest.mark.parametrize("V,dt", [(1000, W.F32), (1003, W.BF16), (7, W.F32), (50001, W.BF16)])
-def test_accept_ragged_gamma_and_ties(V, dt):
-    rng = np.random.default_rng(V)
-    B, n_max = 9, 6
+def test_accept_ragged_gamma_and_ties(V, dt, B):
+    rng = np.random.default_rng(V + B)
+    n_max = 6
     logits = rng.integers(-3, 4, size=(B, n_max, V)).astype(np.float32)   # heavy ties
     logits[0, 1, :] = 0.0
     logits[0, 1, 5 % V] = -0.0
@@ -129,11 +130,28 @@ def test_accept_ragged_gamma_and_ties(V, dt):
     for b in range(B):
         m = b % n_max
         draft[b, :m] = t_ref[b, :m]
-    gamma = np.array([5, 0, 1, 2, 3, 4, 5, 5, 3], np.int32)
+    gamma = np.resize(np.array([5, 0, 1, 2, 3, 4, 5, 5, 3], np.int32), B)
     case = W.AcceptCase("ragged", W.Stored.from_f32(logits, dt), draft, gamma)
     t, n, nxt = _accept(case)
     rt, rn, rnx = oracle.accept(case.logits.values, case.draft, case.gamma)
     assert np.array_equal(t, rt) and np.array_equal(n, rn) and np.array_equal(nxt, rnx)
+
+
+def test_accept_batches_in_turn():
+    """Calls of several batch sizes in a row on one workspace, vectorised and
+    scalar vocabularies, ragged gamma."""
+    rng = np.random.default_rng(11)
+    for B in (64, 8, 9, 24, 64):
+        V = 32000 + B
+        logits = rng.standard_normal((B, 4, V)).astype(np.float32)
+        t_ref = logits.argmax(-1)
+        draft = t_ref[:, :3].astype(np.int32).copy()
+        draft[::3, 1] = (draft[::3, 1] + 1) % V
+        gamma = rng.integers(0, 4, size=B).astype(np.int32)
+        case = W.AcceptCase("turns", W.Stored.from_f32(logits, W.BF16), draft, gamma)
+        t, n, nxt = _accept(case)
+        rt, rn, rnx = oracle.accept(case.logits.values, case.draft, case.gamma)
+        assert np.array_equal(t, rt) and np.array_equal(n, rn) and np.array_equal(nxt, rnx), B
 
 
 def test_accept_single_row_no_draft():
