@@ -1512,10 +1512,13 @@ spec_status_t launch_attention(AttnArgs a, int d, int dtype, const AttnPlan& pla
     a.dyn = 1;
   } else if (plan.S > 1 && dtype == SPEC_BF16 && d == 128) {
     // the pipelined kernel's waves write their own partials when that keeps
-    // the merge small (phases per split as in PipeCfg)
+    // the merge small (phases per split as in PipeCfg) and the rows are few.
+    // With 33-64 rows, twice the partial bytes cost the merge more than the
+    // phase merge in LDS costs the split (the ragged paged text-anchored
+    // batch, 56 rows: 19.7 us with one partial per split, 21.1 with two).
     const int nb = min(4, (a.R + 15) / 16);
     const int kp = (nb >= 3) ? 2 : 4 / nb;
-    if (plan.S * kp <= plan.sp_max) a.SP = plan.S * kp;
+    if (nb <= 2 && plan.S * kp <= plan.sp_max) a.SP = plan.S * kp;
   }
   a.chunk = plan.chunk;
   if (plan.S > 1) {
