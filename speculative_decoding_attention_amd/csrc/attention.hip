@@ -1328,19 +1328,24 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
         live ? (Mx + log2f(Ls)) * 0.69314718055994531f : -INFINITY;
 }
 
-// Few partials per unit (a batch of short or ragged units): one thread per
-// (row, column), 256 / D rows per workgroup, the row's partials requested
-// kMergeSmall at a time (one round for the capacity plan's few partials;
-// the balanced plan's units may have more, merged round by round against a
+// Few partials per unit (a batch of short or ragged units): one wave per
+// row, each thread D / 64 adjacent columns (one 8-byte load per partial at
+// D = 128, against two 4-byte loads with one column per thread: the ragged
+// paged batch's verification 118.3 -> 115.9 us, its text-anchored call
+// 19.7 -> 18.0 us), 4 rows per workgroup.  The row's partials are requested
+// kMergeSmall at a time (one round for the capacity plan's few partials; the
+// balanced plan's units may have more, merged round by round against a
 // running maximum).  The grouped kernel above would spend a 512-thread
 // workgroup on each (row, 64 columns) with most groups idle.
 constexpr int kMergeSmall = 8;
+constexpr int kMergeSmallRows = 4;     // rows (waves) per workgroup
 
 template <int D>
-__global__ __launch_bounds__(256) void attn_merge_small_kernel(AttnArgs a) {
-  constexpr int RPW = 256 / D;
+__global__ __launch_bounds__(64 * kMergeSmallRows) void attn_merge_small_kernel(AttnArgs a) {
+  constexpr int CPT = D / 64;          // columns per thread
+  typedef float vec_t __attribute__((ext_vector_type(CPT)));
   const int R = a.R;
-  const int blocks_per_unit = (R + RPW - 1) / RPW;
+  const int blocks_per_unit = (R + kMergeSmallRows - 1) / kMergeSmallRows;
   const int u = blockIdx.x / blocks_per_unit, rb = blockIdx.x - u * blocks_per_unit;
   int S = a.SP;
   size_t first = (size_t)u * a.SP;
@@ -1350,21 +1355,23 @@ __global__ __launch_bounds__(256) void attn_merge_small_kernel(AttnArgs a) {
     S = ds.S;
     first = (size_t)ds.first;
   }
-  // the row is uniform over a wave (D is a multiple of 64): scalar statistics
-  const int r = __builtin_amdgcn_readfirstlane(rb * RPW + (int)threadIdx.x / D);
+  // the row is the wave's: scalar statistics
+  const int r = __builtin_amdgcn_readfirstlane(rb * kMergeSmallRows + (int)threadIdx.x / 64);
   if (r >= R) return;
-  const int d = threadIdx.x % D;
+  const int d = CPT * ((int)threadIdx.x % 64);
   const int b = u / a.Hkv, g = u - b * a.Hkv;
   const int i = r / a.G, hh = r - i * a.G;
   const float* pm = a.part_ml + first * 3 * R + r;
   const float* pa = a.part_acc + first * R * D + (size_t)r * D + d;
-  float M = -INFINITY, o = 0.f, Ls = 0.f, Lr = 0.f;
+  float M = -INFINITY, Ls = 0.f, Lr = 0.f;
+  vec_t o = {};
   for (int base = 0; base < S; base += kMergeSmall) {
-    float v[kMergeSmall], mv[kMergeSmall], lv[kMergeSmall], rv[kMergeSmall];
+    vec_t v[kMergeSmall];
+    float mv[kMergeSmall], lv[kMergeSmall], rv[kMergeSmall];
 #pragma unroll
     for (int j = 0; j < kMergeSmall; ++j) {          // clamped, masked after
       const int sp = min(base + j, S - 1);
-      v[j] = pa[(size_t)sp * R * D];
+      v[j] = *reinterpret_cast<const vec_t*>(pa + (size_t)sp * R * D);
       mv[j] = pm[(size_t)sp * 3 * R];
       lv[j] = pm[(size_t)sp * 3 * R + R];
       rv[j] = pm[(size_t)sp * 3 * R + 2 * R];
@@ -1377,13 +1384,15 @@ __global__ __launch_bounds__(256) void attn_merge_small_kernel(AttnArgs a) {
     }
     const float Mu = (mr == -INFINITY) ? 0.f : mr;
     const float sc = __builtin_amdgcn_exp2f(M - Mu);   // M = -inf: nothing merged yet -> 0
-    o *= sc;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) o[c] *= sc;
     Ls *= sc;
     Lr *= sc;
 #pragma unroll
     for (int j = 0; j < kMergeSmall; ++j) {
       const float w = __builtin_amdgcn_exp2f(mv[j] - Mu);
-      o = __builtin_fmaf(v[j], w, o);
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) o[c] = __builtin_fmaf(v[j][c], w, o[c]);
       Ls = __builtin_fmaf(lv[j], w, Ls);
       Lr = __builtin_fmaf(rv[j], w, Lr);
     }
@@ -1391,12 +1400,23 @@ __global__ __launch_bounds__(256) void attn_merge_small_kernel(AttnArgs a) {
   }
   const int nq = a.q_len ? ld_uniform(a.q_len, b) : a.n_max;
   const bool live = (i < nq) && (Ls > 0.f);
-  o = live ? o / Lr : 0.f;
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) o[c] = live ? o[c] / Lr : 0.f;
   const size_t oi = (((size_t)b * a.n_max + i) * a.Hq + g * a.G + hh) * D + d;
-  if (a.out_bf16)
-    reinterpret_cast<uint16_t*>(a.out)[oi] = (uint16_t)f32_to_bf16_bits(o);
-  else
-    reinterpret_cast<float*>(a.out)[oi] = o;
+  if constexpr (CPT == 2) {                      // one 4- or 8-byte store
+    if (a.out_bf16)
+      reinterpret_cast<uint32_t*>(a.out)[oi / 2] = pack_bf16x2(o[0], o[1]);
+    else
+      *reinterpret_cast<vec_t*>(reinterpret_cast<float*>(a.out) + oi) = o;
+  } else {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      if (a.out_bf16)
+        reinterpret_cast<uint16_t*>(a.out)[oi + c] = (uint16_t)f32_to_bf16_bits(o[c]);
+      else
+        reinterpret_cast<float*>(a.out)[oi + c] = o[c];
+    }
+  }
   if (a.lse && d == 0)
     a.lse[((size_t)b * a.n_max + i) * a.Hq + g * a.G + hh] =
         live ? (M + log2f(Ls)) * 0.69314718055994531f : -INFINITY;
@@ -1543,12 +1563,12 @@ spec_status_t launch_attention(AttnArgs a, int d, int dtype, const AttnPlan& pla
     // balanced plans merge few partials per unit when the capacity plan has
     // few splits (a unit's balanced split count is about its share of them)
     if (a.dyn ? plan.S <= 2 * kMergeSmall : a.SP <= kMergeSmall) {
-      const int rpw = 256 / d;
-      const int blocks = units * ((a.R + rpw - 1) / rpw);
+      const int blocks = units * ((a.R + kMergeSmallRows - 1) / kMergeSmallRows);
+      const dim3 block(64 * kMergeSmallRows);
       if (d == 64)
-        hipLaunchKernelGGL(attn_merge_small_kernel<64>, dim3(blocks), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(attn_merge_small_kernel<64>, dim3(blocks), block, 0, stream, a);
       else
-        hipLaunchKernelGGL(attn_merge_small_kernel<128>, dim3(blocks), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(attn_merge_small_kernel<128>, dim3(blocks), block, 0, stream, a);
     } else {
       const int blocks = units * a.R * (d > kMergeSlice ? d / kMergeSlice : 1);
       if (d == 64)
