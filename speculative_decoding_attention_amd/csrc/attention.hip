@@ -1215,36 +1215,42 @@ __global__ __launch_bounds__(256, 1) void attn_f32_kernel(AttnArgs a) {
 }
 
 // --------------------------------------------------------------- merge ----
-// One workgroup per (unit, row, slice of kMergeSlice output columns): combine
-// the S partials with the log-sum-exp rule.  Threads form
-// kMergeThreads/kMergeSlice groups over the splits (group k takes splits
-// k, k + NG, ...).  Each thread requests its partials and their splits'
-// (m, l, l_rnd) in one round of loads, merges them against its group's own
-// running maximum, and the groups are then combined in a fixed order against
-// the overall maximum.  One load round trip and one barrier on the critical
-// path; no thread waits for another's weights.
+// One workgroup per (unit, row, slice of 64 * CPT output columns): combine
+// the S partials with the log-sum-exp rule.  Threads form kMergeThreads / 64
+// groups over the splits (group k takes splits k, k + NG, ...), and each
+// thread of a group takes CPT adjacent columns.  Each thread requests its
+// partials and their splits' (m, l, l_rnd) in one round of loads, merges
+// them against its group's own running maximum, and the groups are then
+// combined in a fixed order against the overall maximum.  One load round
+// trip and one barrier on the critical path; no thread waits for another's
+// weights.  Two columns per thread (one workgroup per row at d = 128) when
+// the rows are many: half the workgroups and 8-byte loads (C2's
+// verification, 168 rows: 20.0 -> 19.7 us); one column per thread when they
+// are few, so that more workgroups share the load round trip (7 rows: 9.8
+// against 10.2 us for the text-anchored call).
 constexpr int kMaxSplits = 4096;
 // Up to this many partials per unit, the pipelined kernel's waves write one
 // each (no LDS merge at the end of a split).
 constexpr int kWavePartials = 64;
 constexpr int kMergeThreads = 512;   // 8 groups of 64 threads over the splits
-constexpr int kMergeSlice = 64;       // output columns per workgroup: one wave per split
+constexpr int kMergeWideRows = 128;   // rows (units x R) from which a thread takes two columns
 constexpr int kMergeLoads = 4096;     // partial values one workgroup requests per round
 
-template <int D>
+template <int D, int CPT>
 __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
-  constexpr int DS = kMergeSlice < D ? kMergeSlice : D;
-  constexpr int NG = kMergeThreads / DS;
+  constexpr int DS = 64 * CPT;                      // output columns per workgroup
+  constexpr int NG = kMergeThreads / 64;            // groups of 64 threads over the splits
   constexpr int PB = kMergeLoads / kMergeThreads;   // splits per thread per load round
-  static_assert(DS % 64 == 0 && PB >= 1, "merge shape");
-  __shared__ float part[NG][DS];
+  static_assert(D % DS == 0 && PB >= 1, "merge shape");
+  typedef float vec_t __attribute__((ext_vector_type(CPT)));
+  __shared__ vec_t part[NG][64];
   __shared__ float gstat[3][NG];
   const int R = a.R;
   const int row = blockIdx.x / (D / DS), slice = blockIdx.x - row * (D / DS);
   const int u = row / R, r = row - u * R;
   const int b = u / a.Hkv, g = u - b * a.Hkv;
   const int i = r / a.G, hh = r - i * a.G;
-  const int tid = threadIdx.x, dl = tid % DS, d = slice * DS + dl;
+  const int tid = threadIdx.x, dl = tid % 64, d = slice * DS + CPT * dl;
   // the unit's partials: S per unit in the capacity plan, or the balanced
   // plan's (a unit with one split wrote its output itself)
   int S = a.SP;
@@ -1255,21 +1261,23 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
     S = ds.S;
     first = (size_t)ds.first;
   }
-  // the group index is uniform over a wave (DS is a multiple of 64), so the
-  // per-split statistics below are scalar loads
-  const int grp = __builtin_amdgcn_readfirstlane(tid / DS);
+  // the group index is uniform over a wave, so the per-split statistics
+  // below are scalar loads
+  const int grp = __builtin_amdgcn_readfirstlane(tid / 64);
   const float* pm = a.part_ml + first * 3 * R + r;
   const float* pa = a.part_acc + first * R * D + (size_t)r * D + d;
 
-  float M = -INFINITY, o = 0.f, ls = 0.f, lr = 0.f;
+  float M = -INFINITY, ls = 0.f, lr = 0.f;
+  vec_t o = {};
   for (int base = grp; base < S; base += NG * PB) {
     // clamped indices, loaded unconditionally and masked afterwards: a guarded
     // load would wait for itself before the next one is issued
-    float v[PB], mv[PB], lv[PB], rv[PB];
+    vec_t v[PB];
+    float mv[PB], lv[PB], rv[PB];
 #pragma unroll
     for (int j = 0; j < PB; ++j) {
       const int sp = min(base + NG * j, S - 1);
-      v[j] = pa[(size_t)sp * R * D];
+      v[j] = *reinterpret_cast<const vec_t*>(pa + (size_t)sp * R * D);
       mv[j] = pm[(size_t)sp * 3 * R];
       lv[j] = pm[(size_t)sp * 3 * R + R];
       rv[j] = pm[(size_t)sp * 3 * R + 2 * R];
@@ -1282,13 +1290,15 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
     }
     const float Mu = (mr == -INFINITY) ? 0.f : mr;
     const float sc = __builtin_amdgcn_exp2f(M - Mu);   // M = -inf: nothing merged yet -> 0
-    o *= sc;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) o[c] *= sc;
     ls *= sc;
     lr *= sc;
 #pragma unroll
     for (int j = 0; j < PB; ++j) {
       const float w = __builtin_amdgcn_exp2f(mv[j] - Mu);
-      o = __builtin_fmaf(v[j], w, o);
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) o[c] = __builtin_fmaf(v[j][c], w, o[c]);
       ls = __builtin_fmaf(lv[j], w, ls);
       lr = __builtin_fmaf(rv[j], w, lr);
     }
@@ -1307,22 +1317,35 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
   for (int k = 0; k < NG; ++k) Mx = fmaxf(Mx, gstat[0][k]);
   const float Mu = (Mx == -INFINITY) ? 0.f : Mx;
   float Ls = 0.f, Lr = 0.f;
-  o = 0.f;
+  o = vec_t{};
 #pragma unroll
   for (int k = 0; k < NG; ++k) {
     const float f = __builtin_amdgcn_exp2f(gstat[0][k] - Mu);
-    o = __builtin_fmaf(part[k][dl], f, o);
+    const vec_t pk = part[k][dl];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) o[c] = __builtin_fmaf(pk[c], f, o[c]);
     Ls = __builtin_fmaf(gstat[1][k], f, Ls);
     Lr = __builtin_fmaf(gstat[2][k], f, Lr);
   }
   const int nq = a.q_len ? ld_uniform(a.q_len, b) : a.n_max;
   const bool live = (i < nq) && (Ls > 0.f);
-  o = live ? o / Lr : 0.f;
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) o[c] = live ? o[c] / Lr : 0.f;
   const size_t oi = (((size_t)b * a.n_max + i) * a.Hq + g * a.G + hh) * D + d;
-  if (a.out_bf16)
-    reinterpret_cast<uint16_t*>(a.out)[oi] = (uint16_t)f32_to_bf16_bits(o);
-  else
-    reinterpret_cast<float*>(a.out)[oi] = o;
+  if constexpr (CPT == 2) {                      // one 4- or 8-byte store
+    if (a.out_bf16)
+      reinterpret_cast<uint32_t*>(a.out)[oi / 2] = pack_bf16x2(o[0], o[1]);
+    else
+      *reinterpret_cast<vec_t*>(reinterpret_cast<float*>(a.out) + oi) = o;
+  } else {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      if (a.out_bf16)
+        reinterpret_cast<uint16_t*>(a.out)[oi + c] = (uint16_t)f32_to_bf16_bits(o[c]);
+      else
+        reinterpret_cast<float*>(a.out)[oi + c] = o[c];
+    }
+  }
   if (a.lse && d == 0)
     a.lse[((size_t)b * a.n_max + i) * a.Hq + g * a.G + hh] =
         live ? (Mx + log2f(Ls)) * 0.69314718055994531f : -INFINITY;
@@ -1570,11 +1593,13 @@ spec_status_t launch_attention(AttnArgs a, int d, int dtype, const AttnPlan& pla
       else
         hipLaunchKernelGGL(attn_merge_small_kernel<128>, dim3(blocks), block, 0, stream, a);
     } else {
-      const int blocks = units * a.R * (d > kMergeSlice ? d / kMergeSlice : 1);
+      const dim3 block(kMergeThreads);
       if (d == 64)
-        hipLaunchKernelGGL(attn_merge_kernel<64>, dim3(blocks), dim3(kMergeThreads), 0, stream, a);
+        hipLaunchKernelGGL((attn_merge_kernel<64, 1>), dim3(units * a.R), block, 0, stream, a);
+      else if ((long)units * a.R >= kMergeWideRows)
+        hipLaunchKernelGGL((attn_merge_kernel<128, 2>), dim3(units * a.R), block, 0, stream, a);
       else
-        hipLaunchKernelGGL(attn_merge_kernel<128>, dim3(blocks), dim3(kMergeThreads), 0, stream, a);
+        hipLaunchKernelGGL((attn_merge_kernel<128, 1>), dim3(units * a.R * 2), block, 0, stream, a);
     }
     if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
   }
