@@ -92,6 +92,19 @@ def test_small_vata(cfg):
     assert_attention_close(out, lse, ro, rl, c.q_len, dt, f"small vata {seed}")
 
 
+# One sequence, many splits: the grouped merge takes one output column per
+# thread below 128 merged rows (3 KV heads x 42 rows = 126) and two columns
+# per thread, one workgroup per row, from 128 on (4 x 42 = 168).
+@pytest.mark.parametrize("Hq,Hkv", [(21, 3), (28, 4)])
+@pytest.mark.parametrize("page", [0, 16])
+def test_grouped_merge_both_widths(Hq, Hkv, page):
+    c = W.small_attn(91 + Hkv, 1, Hq, Hkv, 128, 6, 6000, W.BF16, page_size=page)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        out, lse, ro, rl = _verify_pair(c, out_dtype)
+        assert_attention_close(out.float(), lse, ro, rl, c.q_len, W.BF16,
+                               f"grouped merge {Hq}/{Hkv} page {page} {out_dtype}")
+
+
 @pytest.mark.parametrize("n,page", [(1, 0), (3, 16), (6, 0)])
 def test_many_short_units(n, page):
     """A batch of 32 short ragged sequences: 128 units of one or two splits,
