@@ -174,21 +174,23 @@ __global__ __launch_bounds__(64) void accept_finish_kernel(AcceptArgs a) {
   }
 }
 
+// 16-byte loads per thread and chunk: two (32 bytes in flight per thread,
+// 4,096 bf16 logits per 256-thread chunk).  More per thread measured slower
+// at batch 64 (117 MB of logits): 8 loads gave 27.3 us per call (22.9 us
+// scan), 6 loads 25.9 and 2 loads 26.0 (21.3-21.7 us scan); small,
+// register-light workgroups keep more of them resident per CU.
+constexpr int kAcceptLoads = 2;
+
 struct AcceptPlan {
-  int loads, chunk, chunks, vec;
+  int chunk, chunks, vec;
   size_t ws_bytes;
 };
 
-// Chunks of 256 threads x `loads` 16-byte loads: 8 loads (128 bytes in
-// flight per thread) when that still gives every CU two workgroups, else 2,
-// so that a few rows (one sequence) spread over the chip.
+// Chunks of 256 threads x kAcceptLoads 16-byte loads.
 AcceptPlan plan_accept(int batch, int n_max, int vocab, bool bf16) {
   AcceptPlan p;
   const int vw = bf16 ? 8 : 4;
-  const long rows = (long)batch * n_max;
-  const int big = kAcceptThreads * 8 * vw;
-  p.loads = (rows * ((vocab + big - 1) / big) >= 2L * device_cu_count()) ? 8 : 2;
-  p.chunk = kAcceptThreads * p.loads * vw;
+  p.chunk = kAcceptThreads * kAcceptLoads * vw;
   p.vec = (vocab % vw == 0) ? 1 : 0;
   if (p.chunk > vocab) p.chunk = ((vocab + vw - 1) / vw) * vw;
   p.chunks = (vocab + p.chunk - 1) / p.chunk;
@@ -237,10 +239,10 @@ spec_status_t launch_commit(const CommitArgs& a, hipStream_t stream) {
 }
 
 size_t accept_workspace(int batch, int n_max, int vocab) {
-  // the largest of the plans any dtype and CU count can choose
+  // the larger of the two dtypes' plans
   size_t need = 0;
   for (int vw : {4, 8}) {
-    const int chunk = std::min(kAcceptThreads * 2 * vw, ((vocab + vw - 1) / vw) * vw);
+    const int chunk = std::min(kAcceptThreads * kAcceptLoads * vw, ((vocab + vw - 1) / vw) * vw);
     const size_t chunks = (size_t)((vocab + chunk - 1) / chunk);
     need = std::max(need, kSyncBytes + align_up((size_t)batch * n_max * chunks *
                                                     sizeof(unsigned long long), 256));
@@ -270,14 +272,10 @@ spec_status_t launch_accept(const void* logits, int dtype, int batch, int n_max,
   a.vec = p.vec;
   const dim3 grid((unsigned)batch * n_max * p.chunks), block(kAcceptThreads);
   mark_before_main(stream);
-  if (bf16 && p.loads == 8)
-    hipLaunchKernelGGL((accept_scan_kernel<true, 8>), grid, block, 0, stream, a);
-  else if (bf16)
-    hipLaunchKernelGGL((accept_scan_kernel<true, 2>), grid, block, 0, stream, a);
-  else if (p.loads == 8)
-    hipLaunchKernelGGL((accept_scan_kernel<false, 8>), grid, block, 0, stream, a);
+  if (bf16)
+    hipLaunchKernelGGL((accept_scan_kernel<true, kAcceptLoads>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((accept_scan_kernel<false, 2>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((accept_scan_kernel<false, kAcceptLoads>), grid, block, 0, stream, a);
   mark_after_main(stream);
   if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
   hipLaunchKernelGGL(accept_finish_kernel, dim3((unsigned)batch), dim3(64), 0, stream, a);
