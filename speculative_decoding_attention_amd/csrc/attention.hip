@@ -690,7 +690,8 @@ __device__ __forceinline__ void pipe_finish(const AttnArgs& a, float* smem, int 
       const size_t sp = (size_t)u * a.SP + (size_t)s * KP + p;
       float* pa = a.part_acc + sp * R * D + (size_t)n * D;
 #pragma unroll
-      for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4_t*>(pa + db * 16 + 4 * q4) = acc[db];
+      for (int db = 0; db < 8; ++db)
+        __builtin_nontemporal_store(acc[db], reinterpret_cast<f32x4_t*>(pa + db * 16 + 4 * q4));
       if (q4 == 0) {
         float* pm = a.part_ml + sp * 3 * R;
         pm[n] = m_run;
@@ -777,10 +778,13 @@ __device__ __forceinline__ void pipe_finish(const AttnArgs& a, float* smem, int 
         a.lse[((size_t)b * a.n_max + i) * a.Hq + g * a.G + hh] =
             live ? (mrow[n] + log2f(Ls)) * 0.69314718055994531f : -INFINITY;
     } else {
+      // Partials are read once, by the merge launch: non-temporal stores
+      // (the ragged paged text-anchored call 18.1 -> 17.1 us; no change at
+      // C2).  The HSR split-K partials measured slower that way (31 -> 34 us).
       float* pa = a.part_acc + pidx * R * D + (size_t)n * D;
 #pragma unroll
       for (int db = 0; db < 8; ++db)
-        *reinterpret_cast<f32x4_t*>(pa + db * 16 + 4 * q4) = o[db];
+        __builtin_nontemporal_store(o[db], reinterpret_cast<f32x4_t*>(pa + db * 16 + 4 * q4));
     }
   }
   if (S_unit > 1) {
