@@ -626,13 +626,15 @@ struct PipeCfg {
   static constexpr int TILE_KEYS = 32 * KP;
   static constexpr int SUB_BYTES = 32 * 256;               // one sub-tile of K (or V)
   static constexpr int TILE_BYTES = KP * 2 * SUB_BYTES;
-  // Dense splits of 64-key tiles keep a three-stage ring (two tiles in
-  // flight while one is computed); gathered splits keep four stages, and
-  // their slot tables take the LDS beside the ring.  Deeper dense rings
-  // measured slower at 25k keys over 248 splits (four stages about 1 us
-  // per call more, five about 2 us), also with the first burst held at two
-  // tiles, so the cost is in the steady state, not in the prologue.
-  static constexpr int RING_BYTES = (!GATHER && NB >= 2 ? 96 : 128) * 1024;
+  // Splits of 64-key tiles keep a three-stage ring (two tiles in flight
+  // while one is computed); a gathered split's slot tables take the LDS
+  // beside it.  Deeper rings measured slower: dense at 25k keys over 248
+  // splits, four stages about 1 us per call more, five about 2 us (also with
+  // the first burst held at two tiles, so the cost is in the steady state,
+  // not in the prologue); gathered, four stages against three, C5's
+  // text-anchored batch 57.3 against 56.4 us and the ragged paged
+  // verification 116.3 against 114.8 us.  128-key tiles (NB = 1) keep two.
+  static constexpr int RING_BYTES = (NB >= 2 ? 96 : 128) * 1024;
   static constexpr int NS = RING_BYTES / TILE_BYTES;       // 2 to 4 stages
   static constexpr int INSTR = TILE_BYTES / 1024;          // 1 KB DMA instructions per tile
   static constexpr int PER_WAVE = INSTR / WAVES;
