@@ -96,9 +96,10 @@ def test_small_vata(cfg):
 # thread below 128 merged rows (3 KV heads x 42 rows = 126) and two columns
 # per thread, one workgroup per row, from 128 on (4 x 42 = 168).
 @pytest.mark.parametrize("Hq,Hkv", [(21, 3), (28, 4)])
-@pytest.mark.parametrize("page", [0, 16])
-def test_grouped_merge_both_widths(Hq, Hkv, page):
-    c = W.small_attn(91 + Hkv, 1, Hq, Hkv, 128, 6, 6000, W.BF16, page_size=page)
+@pytest.mark.parametrize("page,q_len", [(0, None), (16, None), (0, [4])])
+def test_grouped_merge_both_widths(Hq, Hkv, page, q_len):
+    # q_len [4] of 6: the merged rows of the two padded query positions are 0, LSE -inf
+    c = W.small_attn(91 + Hkv, 1, Hq, Hkv, 128, 6, 6000, W.BF16, page_size=page, q_len=q_len)
     for out_dtype in (torch.float32, torch.bfloat16):
         out, lse, ro, rl = _verify_pair(c, out_dtype)
         assert_attention_close(out.float(), lse, ro, rl, c.q_len, W.BF16,
