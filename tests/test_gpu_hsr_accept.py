@@ -137,6 +137,26 @@ def test_accept_ragged_gamma_and_ties(V, dt, B):
     assert np.array_equal(t, rt) and np.array_equal(n, rn) and np.array_equal(nxt, rnx)
 
 
+# vocabularies at and just past one chunk (4,096 bf16 or 2,048 fp32 logits per
+# 256-thread chunk): one full chunk, a one-element tail chunk, and a
+# vectorised tail chunk of one 16-byte word
+@pytest.mark.parametrize("V,dt", [(4096, W.BF16), (4097, W.BF16), (4104, W.BF16),
+                                  (2048, W.F32), (2049, W.F32), (2052, W.F32)])
+def test_accept_chunk_boundaries(V, dt):
+    rng = np.random.default_rng(V)
+    B, n_max = 3, 4
+    logits = rng.standard_normal((B, n_max, V)).astype(np.float32)
+    logits[:, :, V - 1] = 9.0                      # the maximum in the last element
+    logits[1, 2, V - 1] = 0.0
+    logits[1, 2, 0] = 9.0                          # the maximum in the first element
+    draft = np.full((B, n_max - 1), V - 1, np.int32)
+    draft[2, 1] = 0
+    case = W.AcceptCase("chunk", W.Stored.from_f32(logits, dt), draft, np.full(B, n_max - 1, np.int32))
+    t, n, nxt = _accept(case)
+    rt, rn, rnx = oracle.accept(case.logits.values, case.draft, case.gamma)
+    assert np.array_equal(t, rt) and np.array_equal(n, rn) and np.array_equal(nxt, rnx)
+
+
 def test_accept_batches_in_turn():
     """Calls of several batch sizes in a row on one workspace, vectorised and
     scalar vocabularies, ragged gamma."""
