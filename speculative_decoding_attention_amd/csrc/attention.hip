@@ -1240,9 +1240,10 @@ constexpr int kMaxSplits = 4096;
 constexpr int kWavePartials = 64;
 constexpr int kMergeThreads = 512;   // 8 groups of 64 threads over the splits
 constexpr int kMergeWideRows = 128;   // rows (units x R) from which a thread takes two columns
+constexpr int kMergeVecStats = 32;    // partials per unit from which statistics are vector loads
 constexpr int kMergeLoads = 4096;     // partial values one workgroup requests per round
 
-template <int D, int CPT>
+template <int D, int CPT, bool VSTAT>
 __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
   constexpr int DS = 64 * CPT;                      // output columns per workgroup
   constexpr int NG = kMergeThreads / 64;            // groups of 64 threads over the splits
@@ -1284,6 +1285,18 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
     for (int j = 0; j < PB; ++j) {
       const int sp = min(base + NG * j, S - 1);
       v[j] = *reinterpret_cast<const vec_t*>(pa + (size_t)sp * R * D);
+    }
+    // VSTAT: the statistics are requested after the partials, and as vector
+    // loads (the compiler otherwise issues them first, as scalar loads, with
+    // waits at the scalar unit's limit of outstanding loads before any
+    // partial is requested): one round trip for all, faster when most of
+    // the PB splits per thread are real (C2 verification 19.6 -> 19.4 us,
+    // top-K 32.0 -> 31.8), slower when most are clamped repeats (the 7-row
+    // text-anchored call, 16 partials: 9.8 -> 10.0)
+    if constexpr (VSTAT) asm volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < PB; ++j) {
+      const int sp = min(base + NG * j, S - 1);
       mv[j] = pm[(size_t)sp * 3 * R];
       lv[j] = pm[(size_t)sp * 3 * R + R];
       rv[j] = pm[(size_t)sp * 3 * R + 2 * R];
@@ -1600,12 +1613,20 @@ spec_status_t launch_attention(AttnArgs a, int d, int dtype, const AttnPlan& pla
         hipLaunchKernelGGL(attn_merge_small_kernel<128>, dim3(blocks), block, 0, stream, a);
     } else {
       const dim3 block(kMergeThreads);
+      const bool vstat = !a.dyn && a.SP >= kMergeVecStats;
+      const bool wide = (long)units * a.R >= kMergeWideRows;
       if (d == 64)
-        hipLaunchKernelGGL((attn_merge_kernel<64, 1>), dim3(units * a.R), block, 0, stream, a);
-      else if ((long)units * a.R >= kMergeWideRows)
-        hipLaunchKernelGGL((attn_merge_kernel<128, 2>), dim3(units * a.R), block, 0, stream, a);
+        hipLaunchKernelGGL((attn_merge_kernel<64, 1, false>), dim3(units * a.R), block, 0, stream, a);
+      else if (wide && vstat)
+        hipLaunchKernelGGL((attn_merge_kernel<128, 2, true>), dim3(units * a.R), block, 0, stream, a);
+      else if (wide)
+        hipLaunchKernelGGL((attn_merge_kernel<128, 2, false>), dim3(units * a.R), block, 0, stream, a);
+      else if (vstat)
+        hipLaunchKernelGGL((attn_merge_kernel<128, 1, true>), dim3(units * a.R * 2), block, 0, stream,
+                           a);
       else
-        hipLaunchKernelGGL((attn_merge_kernel<128, 1>), dim3(units * a.R * 2), block, 0, stream, a);
+        hipLaunchKernelGGL((attn_merge_kernel<128, 1, false>), dim3(units * a.R * 2), block, 0, stream,
+                           a);
     }
     if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
   }
