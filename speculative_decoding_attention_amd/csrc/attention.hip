@@ -1382,7 +1382,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
 constexpr int kMergeSmall = 8;
 constexpr int kMergeSmallRows = 4;     // rows (waves) per workgroup
 
-template <int D>
+template <int D, bool VSTAT>
 __global__ __launch_bounds__(64 * kMergeSmallRows) void attn_merge_small_kernel(AttnArgs a) {
   constexpr int CPT = D / 64;          // columns per thread
   typedef float vec_t __attribute__((ext_vector_type(CPT)));
@@ -1414,6 +1414,15 @@ __global__ __launch_bounds__(64 * kMergeSmallRows) void attn_merge_small_kernel(
     for (int j = 0; j < kMergeSmall; ++j) {          // clamped, masked after
       const int sp = min(base + j, S - 1);
       v[j] = *reinterpret_cast<const vec_t*>(pa + (size_t)sp * R * D);
+    }
+    // VSTAT (balanced plans, whose rounds hold mostly real splits): the
+    // statistics as vector loads after the partials, as in the grouped merge
+    // (4 x 32,768 verification 59.1 -> 58.5 us); with the capacity plan's
+    // few partials per unit the scalar order stays faster
+    if constexpr (VSTAT) asm volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < kMergeSmall; ++j) {
+      const int sp = min(base + j, S - 1);
       mv[j] = pm[(size_t)sp * 3 * R];
       lv[j] = pm[(size_t)sp * 3 * R + R];
       rv[j] = pm[(size_t)sp * 3 * R + 2 * R];
@@ -1608,9 +1617,11 @@ spec_status_t launch_attention(AttnArgs a, int d, int dtype, const AttnPlan& pla
       const int blocks = units * ((a.R + kMergeSmallRows - 1) / kMergeSmallRows);
       const dim3 block(64 * kMergeSmallRows);
       if (d == 64)
-        hipLaunchKernelGGL(attn_merge_small_kernel<64>, dim3(blocks), block, 0, stream, a);
+        hipLaunchKernelGGL((attn_merge_small_kernel<64, false>), dim3(blocks), block, 0, stream, a);
+      else if (a.dyn)
+        hipLaunchKernelGGL((attn_merge_small_kernel<128, true>), dim3(blocks), block, 0, stream, a);
       else
-        hipLaunchKernelGGL(attn_merge_small_kernel<128>, dim3(blocks), block, 0, stream, a);
+        hipLaunchKernelGGL((attn_merge_small_kernel<128, false>), dim3(blocks), block, 0, stream, a);
     } else {
       const dim3 block(kMergeThreads);
       const bool vstat = !a.dyn && a.SP >= kMergeVecStats;
