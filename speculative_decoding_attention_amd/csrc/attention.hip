@@ -1258,6 +1258,9 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
   const int b = u / a.Hkv, g = u - b * a.Hkv;
   const int i = r / a.G, hh = r - i * a.G;
   const int tid = threadIdx.x, dl = tid % 64, d = slice * DS + CPT * dl;
+  // requested first: only the epilogue needs it, and a load there would add
+  // a round trip after the merge
+  const int nq = a.q_len ? ld_uniform(a.q_len, b) : a.n_max;
   // the unit's partials: S per unit in the capacity plan, or the balanced
   // plan's (a unit with one split wrote its output itself)
   int S = a.SP;
@@ -1346,7 +1349,6 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
     Ls = __builtin_fmaf(gstat[1][k], f, Ls);
     Lr = __builtin_fmaf(gstat[2][k], f, Lr);
   }
-  const int nq = a.q_len ? ld_uniform(a.q_len, b) : a.n_max;
   const bool live = (i < nq) && (Ls > 0.f);
 #pragma unroll
   for (int c = 0; c < CPT; ++c) o[c] = live ? o[c] / Lr : 0.f;
@@ -1403,6 +1405,7 @@ __global__ __launch_bounds__(64 * kMergeSmallRows) void attn_merge_small_kernel(
   const int d = CPT * ((int)threadIdx.x % 64);
   const int b = u / a.Hkv, g = u - b * a.Hkv;
   const int i = r / a.G, hh = r - i * a.G;
+  const int nq = a.q_len ? ld_uniform(a.q_len, b) : a.n_max;   // requested first
   const float* pm = a.part_ml + first * 3 * R + r;
   const float* pa = a.part_acc + first * R * D + (size_t)r * D + d;
   float M = -INFINITY, Ls = 0.f, Lr = 0.f;
@@ -1449,7 +1452,6 @@ __global__ __launch_bounds__(64 * kMergeSmallRows) void attn_merge_small_kernel(
     }
     M = mr;
   }
-  const int nq = a.q_len ? ld_uniform(a.q_len, b) : a.n_max;
   const bool live = (i < nq) && (Ls > 0.f);
 #pragma unroll
   for (int c = 0; c < CPT; ++c) o[c] = live ? o[c] / Lr : 0.f;
