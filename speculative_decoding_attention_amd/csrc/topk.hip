@@ -245,12 +245,27 @@ __global__ __launch_bounds__(kRingWaves * 64, 1) void topk_score_ring_kernel(Top
     const int k0 = t_beg + (wave + i * kRingWaves) * kRingTile;
     const size_t mine = topk_row(a, b, g, min(k0 + lane, t_end - 1));
     const uint32_t lo = (uint32_t)mine, hi = (uint32_t)(mine >> 32);
+    // Every row address first: each DMA statement is a compiler memory
+    // barrier.  A contiguous cache's rows are arithmetic; a paged cache's
+    // come from the lanes that looked them up, by shuffles.
+    const unsigned char* src[NI];
+    if (a.page_shift < 0) {
+      const size_t base = ((size_t)b * a.Hkv + g) * (size_t)a.max_len;
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int r = RPI * j + rr;
-      const size_t row = (size_t)__shfl(lo, r) | ((size_t)__shfl(hi, r) << 32);
-      dma16(kb + row * ROW_B + 16 * (cpos ^ (r % CH)), slot_lds + (uint32_t)(j * 1024));
+      for (int j = 0; j < NI; ++j) {
+        const int r = RPI * j + rr;
+        src[j] = kb + (base + (size_t)min(k0 + r, t_end - 1)) * ROW_B + 16 * (cpos ^ (r % CH));
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const int r = RPI * j + rr;
+        const size_t row = (size_t)__shfl(lo, r) | ((size_t)__shfl(hi, r) << 32);
+        src[j] = kb + row * ROW_B + 16 * (cpos ^ (r % CH));
+      }
     }
+#pragma unroll
+    for (int j = 0; j < NI; ++j) dma16(src[j], slot_lds + (uint32_t)(j * 1024));
   };
   if (my_tiles > 0) issue(0);
 
