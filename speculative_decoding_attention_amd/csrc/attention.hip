@@ -1272,7 +1272,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
     first = (size_t)ds.first;
   }
   // the group index is uniform over a wave, so the per-split statistics
-  // below are scalar loads
+  // below can be scalar loads (see VSTAT)
   const int grp = __builtin_amdgcn_readfirstlane(tid / 64);
   const float* pm = a.part_ml + first * 3 * R + r;
   const float* pa = a.part_acc + first * R * D + (size_t)r * D + d;
@@ -1293,8 +1293,8 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
     // loads (the compiler otherwise issues them first, as scalar loads, with
     // waits at the scalar unit's limit of outstanding loads before any
     // partial is requested): one round trip for all, faster when most of
-    // the PB splits per thread are real (C2 verification 19.6 -> 19.4 us,
-    // top-K 32.0 -> 31.8), slower when most are clamped repeats (the 7-row
+    // the PB splits per thread are real (C2 verification 19.7 -> 19.5 us,
+    // top-K 32.1 -> 31.7), slower when most are clamped repeats (the 7-row
     // text-anchored call, 16 partials: 9.8 -> 10.0)
     if constexpr (VSTAT) asm volatile("" ::: "memory");
 #pragma unroll
