@@ -52,3 +52,16 @@ def test_break_even_alpha_limits():
     assert bench.break_even_alpha(2, 10.0, 10.0, 5.0) is None    # 30 us > 3 tokens x 5 us
     # cheaper drafts (a smaller kept fraction) break even at a lower rate
     assert bench.break_even_alpha(5, 2.0, 20.0, 19.0) < bench.break_even_alpha(5, 6.0, 20.0, 19.0)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The library has no multi-GPU path: the bench exits with a message
+    (status 2) before it touches a device."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
