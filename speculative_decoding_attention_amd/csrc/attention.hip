@@ -1541,6 +1541,15 @@ AttnPlan plan_attention(int units, int t_max, int rows, int d, bool gather, size
   long chunk = (total + target - 1) / target;
   if (chunk < (T + kMaxSplits - 1) / kMaxSplits) chunk = (T + kMaxSplits - 1) / kMaxSplits;
   chunk = ((chunk + kTK - 1) / kTK) * kTK;
+  // Dense splits of whole tiles of the pipelined kernel (128 keys up to 16
+  // rows, else 64): a split that ends inside a tile still spends a whole
+  // tile's requests and compute on it, and fewer, fuller splits leave fewer
+  // partials.  At 25,512 keys: 6 rows 19.1 -> 18.9 us, 9 rows 20.6 -> 19.8,
+  // 1 row 18.5 -> 18.1.
+  if (!gather) {
+    const long tile = rows <= 16 ? 128 : 64;
+    chunk = ((chunk + tile - 1) / tile) * tile;
+  }
   if (chunk < kTK * kNW) chunk = kTK * kNW;        // every wave gets a tile
   if (gather) {
     // LDS holds kMaxChunk staged entries: slots, or pages when the split
