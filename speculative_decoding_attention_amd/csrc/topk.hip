@@ -204,8 +204,8 @@ __global__ __launch_bounds__(256) void topk_score_kernel(TopkArgs a) {
 }
 
 // Streaming score pass for bf16 keys.  The unit's length is cut on the
-// device into a.splits ranges of whole rounds of 8 64-key tiles (at most a.splits ranges); range s is workgroup
-// (u, s).  Wave w takes the range's tiles w, w + 8, ... through a private
+// device into at most a.splits ranges of whole rounds of 8 64-key tiles;
+// range s is workgroup (u, s).  Wave w takes the range's tiles w, w + 8, ... through a private
 // LDS slot.  The DMA stores chunk c of tile row r at chunk position
 // c ^ (r % CH), so the lanes of a quarter-wave, each reading its own key's
 // row, address distinct banks.  A lane copies its row to registers; the
