@@ -512,9 +512,12 @@ StdPlan plan_std(int units, int max_len, int t_max, int G, int top_k) {
   StdPlan p;
   p.RB = (t_max * G + kBR - 1) / kBR;
   p.RBP = p.RB * kBR;
-  // enough workgroups for several per CU (two fit at once), splits of at
-  // least 256 keys, every split a whole number of 64-key iterations
-  const long target = 8L * device_cu_count();
+  // about four workgroups per CU (two fit at once), splits of at least 256
+  // keys, every split a whole number of 64-key iterations.  Longer splits
+  // amortise each workgroup's query-row set-up: at 25k keys x 512 text rows,
+  // 10 splits per row block take 278 us against 295 us for 19 (eight per
+  // CU); 7 splits (two or three per CU) take the same 278, 37 take 396
+  const long target = 4L * device_cu_count();
   const long blocks = (long)units * p.RB;
   long S = (target + blocks - 1) / blocks;
   const long smax = (max_len + 255) / 256;
